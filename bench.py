@@ -1,0 +1,258 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+One step = one decode step of one attention layer for the whole batch:
+  1. append each sequence's newest K/V token into its slot (quantize-on-write
+     for INT4/FP8 pools),
+  2. split-K decode over all cached tokens (gathered through block tables),
+  3. log-sum-exp combine of the splits.
+Inputs are seeded synthetic data already resident in HBM when timing starts.
+
+`value` is KV GB/s: the algorithmic K/V bytes one decode step must read
+(sum over sequences of L * Hkv * 2 * D * bytes/element, or the packed
+INT4/FP8 bytes plus their fp16 scales) divided by the measured step time.
+`roofline` prices the dominant kernel (the split kernel) against 8 TB/s with
+its own launch durations, measured with HIP events on the launch stream.
+`cpu_baseline` times the CPU oracle (logical rebuild through the tables +
+float64 attention) on a bounded sample of the same batch.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config llama3-8b]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    "llama3-8b": "Llama-3-8B-shaped decode layer: batch 64, lengths U[512,4096], 32 q / 8 kv heads, "
+                 "head_dim 128, bf16, block 16, shuffled tables, pool +10%",
+    "long-context": "long-context decode: 4 sequences x 65,536 tokens, 32 q / 8 kv heads, head_dim 128, "
+                    "bf16, block 16, shuffled tables",
+    "mixed-int4": "mixed precision: 1 x 65,536 (+64 appended) tokens, FP16 sink block, INT4 g128 body, "
+                  "32 q / 8 kv heads, head_dim 128, 1% outlier channels x10",
+    "mixed-fp8": "mixed precision: 1 x 65,536 (+64 appended) tokens, FP16 sink block, FP8 E4M3 body, "
+                 "32 q / 8 kv heads, head_dim 128, 1% outlier channels x10",
+    "shared-prefix": "shared prefix: 32 forks of a 2,000-token prompt + U[0,512] suffixes, 64 q / 8 kv "
+                     "heads, head_dim 128, bf16",
+    "shared-prefix-partial": "shared prefix (1,992-token prompt, one CoW clone per writing fork), 64 q / "
+                             "8 kv heads, head_dim 128, bf16",
+}
+
+
+def kv_bytes_per_token(wl):
+    D, H = wl.head_dim, wl.n_kv_heads
+    if wl.kv_dtype == "int4":
+        per = D // 2 + 4 * (D // wl.group_size)   # codes + fp16 scale and zero per group
+    elif wl.kv_dtype == "fp8":
+        per = D + 2
+    else:
+        per = D * {"f32": 4, "f16": 2, "bf16": 2}[wl.kv_dtype]
+    return 2 * H * per
+
+
+def algorithmic_bytes(wl, lens):
+    """K/V bytes the decode must read: quantized body tokens at their packed
+    size, sink tokens at fp16."""
+    per = kv_bytes_per_token(wl)
+    if wl.sink_blocks_per_seq:
+        sink = 16 * wl.sink_blocks_per_seq
+        raw = 2 * wl.n_kv_heads * wl.head_dim * 2
+        return int(sum(min(L, sink) * raw + max(0, L - sink) * per for L in lens))
+    return int(sum(lens) * per)
+
+
+def cpu_baseline(kv, wl, t, l, budget_s):
+    """Time the oracle's decode on the first sequences of the batch: rebuild the
+    logical K/V through the table from the copied-back pool bytes, then float64
+    attention.  Stops after ~budget_s seconds."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle import attention as AT
+    from paged_kv_cache_18_amd.binding import DTYPES
+
+    pool_bytes = kv.pool_host_bytes()
+    desc = dict(kv_dtype=DTYPES[wl.kv_dtype], n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+                group_size=wl.group_size or wl.head_dim, num_blocks=wl.num_blocks,
+                num_sink_blocks=wl.num_sink_blocks)
+    view = AT.PoolView(pool_bytes, desc)
+    import torch
+    q = torch.from_numpy(wl.q()).to({"f32": torch.float32, "f16": torch.float16,
+                                     "bf16": torch.bfloat16}[wl.q_dtype]).double().numpy()
+    done, secs = 0, 0.0
+    while done < wl.batch and secs < budget_s:
+        t0 = time.perf_counter()
+        K, V = view.logical_kv(t[done], int(l[done]))
+        AT.attention_one(q[done], K, V, wl.scale)
+        secs += time.perf_counter() - t0
+        done += 1
+    byts = algorithmic_bytes(wl, [int(x) for x in l[:done]])
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    return {"value": round(byts / secs / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {wl.batch} sequences ({int(sum(l[:done]))} tokens): logical "
+                      f"rebuild from the pool bytes + float64 attention, {secs:.1f} s",
+            "queries_per_s": round(done / secs, 3),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama3-8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time the split kernel with a 512 MiB cache flush between steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_18_amd import binding as B
+    from paged_kv_cache_18_amd import workloads as W
+    from paged_kv_cache_18_amd.session import PagedKV, torch_dtype
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    wl = W.by_name(args.config)
+    print(f"[bench] {args.config}: prefill ...", file=sys.stderr, flush=True)
+    kv = PagedKV(wl, dev)
+    kv.replay()
+    tdev, ldev, t, l = kv.device_tables()
+    lens = [int(x) for x in l]
+    max_len = max(lens)
+    q = torch.from_numpy(wl.q()).to(torch_dtype(wl.q_dtype)).to(dev)
+    out = torch.empty_like(q)
+    ws_bytes = B.pa_decode_workspace_bytes(kv.pool, wl.batch, wl.n_q_heads, max_len)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    # the step's append: every sequence's newest token, rewritten in its slot
+    k_new, v_new = [], []
+    for s, L in zip(wl.decode_seqs, lens):
+        K, V = wl.seq_tokens(s)
+        k_new.append(K[L - 1])
+        v_new.append(V[L - 1])
+        del K, V
+    k_new, v_new = np.stack(k_new), np.stack(v_new)
+    in_dt = torch_dtype(wl.in_dtype)
+    k_new = torch.from_numpy(k_new).to(in_dt).to(dev)
+    v_new = torch.from_numpy(v_new).to(in_dt).to(dev)
+    slots = np.array([t[b, (L - 1) // 16] * 16 + (L - 1) % 16 for b, L in enumerate(lens)],
+                     dtype=np.int32)
+    slots_dev = torch.from_numpy(slots).to(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    dargs = (q, kv.pool, tdev, ldev, wl.batch, wl.n_q_heads, wl.q_dtype, tdev.shape[1], max_len,
+             wl.scale, out, ws, ws.numel(), sh)
+
+    split_ev = []
+
+    def step(record):
+        B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, wl.batch, sh)
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        B.pa_decode_split(*dargs)
+        if record:
+            e1.record(stream)
+            split_ev.append((e0, e1))
+        B.pa_decode_combine(*dargs)
+
+    print(f"[bench] warmup {args.warmup} ...", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps ...", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    split_ms = [a.elapsed_time(b) for a, b in split_ev]
+    split_avg = float(np.mean(split_ms))
+
+    byts = algorithmic_bytes(wl, lens)
+    kv_gbs = byts / (ms_step * 1e-3) / 1e9
+    achieved = byts / (split_avg * 1e-3) / 1e9
+
+    extra = {}
+    if args.cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(max(10, args.steps // 2)):
+            flush.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            B.pa_decode_split(*dargs)
+            e1.record(stream)
+            B.pa_decode_combine(*dargs)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        extra["cold_split_ms_median"] = round(float(np.median(cold)), 4)
+        extra["cold_split_gbs"] = round(byts / (np.median(cold) * 1e-3) / 1e9, 1)
+        del flush
+    if args.copy_calibration:
+        a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = 1 << 30
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(kv, wl, t, l, args.cpu_budget)
+
+    split_blocks = B.pa_decode_split_blocks(kv.pool, wl.batch, wl.n_q_heads, max_len)
+    res = {
+        "metric": "paged decode attention KV GB/s (% of HBM peak) and queries/s, 1 MI355X",
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"int4": "int4+f16", "fp8": "fp8e4m3+f16"}.get(wl.kv_dtype, wl.kv_dtype),
+        "data": "synthetic (seeded N(0,1))",
+        "config": {"workload": WORKLOADS[args.config], "batch": wl.batch,
+                   "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": 16, "kv_dtype": wl.kv_dtype,
+                   "total_tokens": int(sum(lens)), "max_seq_len": max_len,
+                   "split_blocks": split_blocks},
+        "queries_per_s": round(wl.batch / (ms_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
+        "kv_bytes_per_step": byts,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_split", "avg_launch_ms": round(split_avg, 5)},
+        "cpu_baseline": cpu,
+    }
+    res.update(extra)
+    print(json.dumps(res), flush=True)
+    kv.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,263 @@
+/*
+ * pa.h -- C ABI of libpa: PagedAttention decode on AMD Instinct MI355X (gfx950).
+ *
+ * One new query token per sequence attends over a KV cache stored in 16-token
+ * physical blocks of one flat pool, reached through a per-sequence block
+ * table.  An optional mixed-precision pool keeps each sequence's first block
+ * (the attention sink) in FP16 and the rest in asymmetric INT4 or FP8 E4M3.
+ *
+ * Sources, cited by page title and section:
+ *  [8GB]  "The 8GB VRAM Breakthrough: How PagedAttention and Dynamic KV-Cache
+ *         Quantization Unlock 64k Context on Consumer GPUs"
+ *  [PR8]  "Capitulo 8 -- Gerenciamento de KV Cache de Proxima Geracao"
+ *         (LLM Primer VI)
+ *  [60Y]  "A Ideia de 60 Anos Que Domou a Memoria da GPU"
+ *  [3MIN] "PagedAttention aplica memoria virtual ao cache KV de LLMs"
+ *
+ * Conventions for every call
+ *  - Every call returns a pa_status; PA_OK is 0.  On any other status the
+ *    library state is unchanged (calls are all-or-nothing) and
+ *    pa_last_error() returns a thread-local message.  No C++ exception
+ *    crosses this boundary.
+ *  - The library never allocates device memory.  Every device buffer (pool
+ *    memory, q/k/v/out, tables, lengths, slots, workspace) is owned by the
+ *    caller and must outlive the calls that use it.  Host arrays passed in are
+ *    copied during the call.
+ *  - "stream" is a hipStream_t passed as void* (NULL = the default stream).
+ *    Device work is asynchronous on that stream; no call synchronizes.
+ *  - A pool is not thread-safe: one thread at a time per pool.
+ *
+ * Pool memory layout (one caller buffer, byte offsets from pa_pool_layout)
+ *  Arrays are placed in the order listed, each starting at a multiple of 256
+ *  bytes.  Each array is [blocks][n_kv_heads][slab], one slab per (block,
+ *  head) for the 16 tokens of the block (the outer order of [8GB] section 7:
+ *  block, head, then tokens).  Body arrays have num_blocks slabs per head,
+ *  sink arrays num_sink_blocks.
+ *    raw body (F32/F16/BF16): K, V             slab = 16*D elements
+ *    INT4 body:  KC, VC (codes)                slab = 16*D/2 bytes
+ *                KS, KZ, VS, VZ (fp16)         slab = 16*(D/group) values
+ *    FP8 body:   KC, VC (codes)                slab = 16*D bytes
+ *                KS, VS (fp16)                 slab = 16 values
+ *    sink arena (if any): SK, SV (fp16 raw)    slab = 16*D elements
+ *  Inside a slab, with t the token (0..15) and d the dimension (0..D-1):
+ *    raw K       element ((d/8)*16 + t)*8 + d%8
+ *    raw V       NT = D/16, r = d/NT, T = d%NT, g = t/4, i = t%4,
+ *                element ((T/2*64 + g*16 + r)*2 + T%2)*4 + i
+ *    INT4 K      k = d/2: byte ((k%16/4*16 + t)*(D/32) + k/16)*4 + k%4
+ *    INT4 V      byte ((g*16 + r)*(NT/2) + T/2)*4 + i
+ *                (INT4: even d in the low nibble, odd d in the high nibble,
+ *                 as in the unpack of [8GB] section 7)
+ *    FP8 K       byte (((d/64)*4 + d%32/8)*16 + t)*16 + (d/32)%2*8 + d%8
+ *    FP8 V       byte ((T/4*64 + g*16 + r)*4 + T%4)*4 + i
+ *    KS/KZ/VS/VZ element t*(D/group) + d/group;  FP8 KS/VS element t
+ *  Each rule makes one 16-byte load of lane l = 16*a + b of a 64-lane
+ *  wavefront (a = l/16, b = l%16) read l*16 + 1024*unit within the slab, and
+ *  deliver exactly one matrix-core operand fragment: K rows are tokens
+ *  (b = t) with 8 consecutive dimensions per lane group, V rows are
+ *  dimensions (b = r) with 4 consecutive tokens per lane group.
+ *  Unwritten slots hold whatever the buffer held; the kernels mask them.
+ *
+ * Block ids and slots
+ *  Body ids are 0..num_blocks-1, sink ids num_blocks..num_blocks+num_sink-1.
+ *  The id range is the block's precision metadata ([8GB] section 4: every
+ *  physical block carries precision metadata).  A slot is id*16 + offset.
+ *
+ * Numerics
+ *  Decode accumulates in fp32 and writes out in q's dtype (rounded once).
+ *  INT4 quantize-on-write, per group of `group` dims of one (token, head),
+ *  from fp16 values, each step one IEEE fp32 op rounded to nearest even:
+ *    s = fp16((max - min) / 15), 1 if that is 0;  z = fp16(-min / s)
+ *    (clamped to +-65504);  q = clamp(rint(x / s + z), 0, 15);
+ *    dequant x = (q - z) * s  ([8GB] section 4, INT4 mode).
+ *  FP8 per (token, head): s = fp16(amax / 448), 1 if 0; code = nearest
+ *  E4M3 (OCP "fn") value to clamp(x / s, -448, 448), ties to even, sign of
+ *  zero kept ([8GB] section 4, FP8 mode: per-head dynamic scale).
+ *  Inputs of another float dtype are first rounded to fp16 (RNE).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+#define PA_OK 0
+#define PA_ERR_INVALID_ARG 1   /* bad argument, shape or descriptor           */
+#define PA_ERR_OUT_OF_BLOCKS 2 /* an arena has too few free blocks            */
+#define PA_ERR_REFCOUNT 3      /* reference to or release of a free block     */
+#define PA_ERR_BAD_ID 4        /* block or sequence id out of range / unknown */
+#define PA_ERR_UNSUPPORTED 5   /* valid request this build does not implement */
+#define PA_ERR_HIP 6           /* a HIP launch or runtime call failed         */
+
+/* element / storage types */
+#define PA_F32 0
+#define PA_F16 1
+#define PA_BF16 2
+#define PA_INT4_ASYM 3
+#define PA_FP8_E4M3 4
+
+#define PA_ARENA_BODY 0
+#define PA_ARENA_SINK 1
+
+/* array slots of pa_layout */
+#define PA_ARR_K 0   /* raw K, or INT4/FP8 K codes */
+#define PA_ARR_V 1   /* raw V, or INT4/FP8 V codes */
+#define PA_ARR_KS 2
+#define PA_ARR_KZ 3
+#define PA_ARR_VS 4
+#define PA_ARR_VZ 5
+#define PA_ARR_SK 6
+#define PA_ARR_SV 7
+#define PA_NUM_ARR 8
+
+typedef struct pa_pool pa_pool;
+
+/* Pool descriptor.  [8GB] section 3: a flat pool of fixed-size blocks,
+ * 16 tokens each; section 4: FP16 sink blocks beside an INT4/FP8 body. */
+typedef struct {
+  int32_t block_size;          /* tokens per block; must be 16                    */
+  int32_t n_kv_heads;          /* >= 1                                            */
+  int32_t head_dim;            /* D: multiple of 32 (of 64 for FP8), 32..256      */
+  int32_t kv_dtype;            /* body storage: PA_F32/F16/BF16/INT4_ASYM/FP8_E4M3 */
+  int32_t group_size;          /* INT4: dims per (scale, zero); multiple of 32
+                                  dividing D.  Ignored otherwise.                 */
+  int32_t num_blocks;          /* body arena blocks, >= 0                         */
+  int32_t num_sink_blocks;     /* FP16 sink arena blocks; 0 = no sink arena;
+                                  only with an INT4 or FP8 body                   */
+  int32_t sink_blocks_per_seq; /* logical blocks 0..k-1 of every sequence come
+                                  from the sink arena; > 0 iff num_sink_blocks > 0 */
+} pa_pool_desc;
+
+typedef struct {
+  size_t total_bytes;              /* bytes the pool memory must hold          */
+  size_t offset[PA_NUM_ARR];       /* byte offset of each array, SIZE_MAX if absent */
+  size_t slab_bytes[PA_NUM_ARR];   /* bytes of one (block, head) slab          */
+} pa_layout;
+
+/* ---- pool ------------------------------------------------------------------ */
+
+/* Bytes of pool memory a descriptor needs (layout above). */
+pa_status pa_pool_bytes(const pa_pool_desc* desc, size_t* bytes);
+
+/* Create a pool over caller memory `dev_mem` (device pointer, at least
+ * pa_pool_bytes bytes, 256-byte aligned).  dev_mem == NULL with dev_bytes == 0
+ * makes a metadata-only pool: allocation, sequences and tables work, device
+ * calls return PA_ERR_INVALID_ARG and clones enqueue no copy.
+ * body_free_order / sink_free_order: host permutations of 0..num_blocks-1 /
+ * 0..num_sink_blocks-1 giving the initial free stack, first element popped
+ * first; NULL = identity.  The free list is a stack ([60Y] "o codigo": rent =
+ * pop, return = push when the refcount reaches 0).  *out owns host metadata
+ * only; destroy it with pa_pool_destroy. */
+pa_status pa_pool_create(const pa_pool_desc* desc, void* dev_mem, size_t dev_bytes,
+                         const int32_t* body_free_order, const int32_t* sink_free_order,
+                         pa_pool** out);
+pa_status pa_pool_destroy(pa_pool* pool);
+pa_status pa_pool_layout(const pa_pool* pool, pa_layout* out);
+
+/* ---- blocks ([60Y] "o codigo": Alugar / Referenciar / Devolver) ------------- */
+
+/* Pop a free block of `arena` (PA_ARENA_*); its refcount becomes 1. */
+pa_status pa_alloc_block(pa_pool* pool, int32_t arena, int32_t* out_id);
+/* Add a reference to a live block (PA_ERR_REFCOUNT if it is free). */
+pa_status pa_incref(pa_pool* pool, int32_t id);
+/* Drop a reference; at zero the block is pushed on its arena's free stack. */
+pa_status pa_free_block(pa_pool* pool, int32_t id);
+/* Copy-on-write clone ([8GB] section 3, "Copy-on-Write (CoW) Prefix
+ * Sharing"): pop a block from src's arena, enqueue a device copy of all of
+ * src's arrays (every head) on `stream`, drop one reference of src. */
+pa_status pa_cow_clone(pa_pool* pool, int32_t src, int32_t* out_dst, void* stream);
+pa_status pa_refcount(const pa_pool* pool, int32_t id, int32_t* out);
+pa_status pa_num_free(const pa_pool* pool, int32_t arena, int32_t* out);
+/* Copy up to `cap` free ids of `arena`, next-to-be-popped first; *n = count. */
+pa_status pa_free_list(const pa_pool* pool, int32_t arena, int32_t* out, int32_t cap, int32_t* n);
+/* Number of copy-on-write clones performed so far. */
+pa_status pa_num_clones(const pa_pool* pool, int64_t* out);
+
+/* ---- sequences (host block tables) -------------------------------------------- */
+
+/* New empty sequence; ids are 0, 1, 2, ... and are not reused. */
+pa_status pa_seq_create(pa_pool* pool, int32_t* out_seq);
+/* Child sharing all of parent's blocks (each gains one reference). */
+pa_status pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* out_child);
+/* Append n_tokens slots to `seq`: a new block only when the tail is full
+ * ([60Y] "a ideia roubada"); logical blocks < sink_blocks_per_seq come from
+ * the sink arena.  If the tail is partially filled and shared, it is cloned
+ * first (pa_cow_clone on `stream`).  slots_out (host, n_tokens entries)
+ * receives id*16 + offset per new token.  All-or-nothing. */
+pa_status pa_seq_reserve(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* slots_out,
+                         void* stream);
+/* Shorten to new_len tokens; blocks no longer used are released last-first. */
+pa_status pa_seq_truncate(pa_pool* pool, int32_t seq, int32_t new_len);
+/* Release all blocks (last-first) and forget the sequence. */
+pa_status pa_seq_release(pa_pool* pool, int32_t seq);
+pa_status pa_seq_info(const pa_pool* pool, int32_t seq, int32_t* len, int32_t* n_blocks);
+/* Export tables of `n` sequences into host tables_out [n][max_blocks] (int32,
+ * padded with -1) and host lens_out [n]; the caller uploads them. */
+pa_status pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n,
+                          int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
+
+/* ---- device work ------------------------------------------------------------------ */
+
+/* Write n_tokens tokens into their slots, quantizing on write for an INT4 or
+ * FP8 body ([8GB] section 5: fused quantizer on the write path).
+ * k, v: device [n_tokens][n_kv_heads][head_dim] of in_dtype (F32/F16/BF16).
+ * slots_dev: device int32 [n_tokens] (from pa_seq_reserve).  Slots whose
+ * block id is out of range are skipped.  Two tokens may not share a slot. */
+pa_status pa_append_kv(pa_pool* pool, const void* k, const void* v, int32_t in_dtype,
+                       const int32_t* slots_dev, int32_t n_tokens, void* stream);
+
+/* Workspace bytes pa_decode_attention needs for these shapes. */
+pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
+                                    int32_t max_seq_len, size_t* bytes);
+
+/* Decode attention ([8GB] section 3: the kernel reads the block table on the
+ * fly and gathers K for Q K^T and V for the softmax-weighted sum; [PR8] 8.1:
+ * the table is an extra kernel input; [3MIN]: paging changes no result).
+ *  q:   device [batch][n_q_heads][head_dim] of q_dtype.  Raw pools need
+ *       q_dtype == kv_dtype; INT4/FP8 pools need PA_F16.
+ *  block_tables_dev: device int32 [batch][max_blocks_per_seq]; entry j of row
+ *       b is the id of logical block j (tokens 16j..16j+15) of sequence b.
+ *  seq_lens_dev: device int32 [batch], each in [0, max_seq_len]; entries past
+ *       ceil(len/16) are not read.  Out-of-range ids are skipped.
+ *  n_q_heads: multiple of n_kv_heads; query head h reads KV head
+ *       h / (n_q_heads / n_kv_heads).
+ *  scale: softmax scale (1/sqrt(head_dim) in the usual case).
+ *  out: device [batch][n_q_heads][head_dim] of q_dtype; rows of empty
+ *       sequences are zero.
+ *  workspace: device, >= pa_decode_workspace_bytes bytes, any contents.
+ * Equivalent to pa_decode_split followed by pa_decode_combine. */
+pa_status pa_decode_attention(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
+                              const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
+                              int32_t q_dtype, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                              float scale, void* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+/* Phase 1: per (sequence, kv head, split of the logical blocks), partial
+ * softmax statistics and weighted sums into the workspace; sequences with a
+ * single split are written to `out` directly. */
+pa_status pa_decode_split(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
+                          const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
+                          int32_t q_dtype, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                          float scale, void* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+/* Phase 2: log-sum-exp merge of the splits of multi-split sequences into out. */
+pa_status pa_decode_combine(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
+                            const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
+                            int32_t q_dtype, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                            float scale, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Blocks per split the decode uses for these shapes (informational). */
+pa_status pa_decode_split_blocks(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
+                                 int32_t max_seq_len, int32_t* out);
+
+/* Text of the last non-OK status on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H_ */

@@ -1,0 +1,45 @@
+// Interface between the C ABI (pa_capi.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../pa_host.hpp"
+
+namespace pa {
+
+// Device view of a pool: base pointer plus the arrays of include/pa.h.
+struct PoolDev {
+  uint8_t* base;
+  int32_t n_kv_heads, head_dim, kv_dtype, group_size, num_blocks, num_sink_blocks;
+  size_t off[kNumArr];
+  size_t slab[kNumArr];
+};
+
+hipError_t launch_append(const PoolDev& p, const void* k, const void* v, int32_t in_dtype,
+                         const int32_t* slots, int32_t n_tokens, hipStream_t s);
+
+hipError_t launch_block_copy(const PoolDev& p, int32_t src, int32_t dst, hipStream_t s);
+
+enum DecodeKernel : int32_t { kKernGeneric = 0, kKernMfma16 = 1 };
+
+struct DecodeArgs {
+  PoolDev pool;
+  const void* q;
+  const int32_t* tables;
+  const int32_t* lens;
+  int32_t batch, n_q_heads, q_dtype, max_blocks_per_seq, max_seq_len;
+  float scale_log2;      // softmax scale * log2(e): scores live in the log2 domain
+  void* out;
+  float* ws_o;           // [batch][n_q_heads][max_splits][head_dim] partial sums
+  float* ws_ml;          // [batch][n_q_heads][max_splits][2] (max, sum), log2 domain
+  int32_t split_blocks;  // logical blocks per split
+  int32_t max_splits;
+  int32_t kernel;        // DecodeKernel
+};
+
+hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace pa

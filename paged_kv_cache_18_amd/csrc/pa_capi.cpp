@@ -1,0 +1,455 @@
+// C ABI of libpa (declarations and contract: include/pa.h).
+//
+// Every entry point validates its arguments before touching any state, turns
+// internal errors into a pa_status, and records a thread-local message.  Device
+// work goes to the kernels behind kernels/launch.hpp on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <string>
+
+#include "../../include/pa.h"
+#include "kernels/launch.hpp"
+#include "pa_host.hpp"
+
+struct pa_pool {
+  pa::PoolCore core;
+  pa::Layout layout;
+  uint8_t* dev;
+  size_t dev_bytes;
+  pa_pool(const pa::Desc& d, const int32_t* bo, const int32_t* so)
+      : core(d, bo, so), layout(pa::compute_layout(d)), dev(nullptr), dev_bytes(0) {}
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+[[noreturn]] void fail(pa::Status s, const std::string& m) { throw pa::Error{s, m}; }
+
+template <class F>
+pa_status guard(F&& f) {
+  try {
+    f();
+    return PA_OK;
+  } catch (const pa::Error& e) {
+    g_err = e.msg;
+    return e.code;
+  } catch (const std::bad_alloc&) {
+    g_err = "host out of memory";
+    return PA_ERR_INVALID_ARG;
+  } catch (...) {
+    g_err = "internal error";
+    return PA_ERR_INVALID_ARG;
+  }
+}
+
+void need(const void* p, const char* what) {
+  if (!p) fail(pa::kInvalidArg, std::string(what) + " is NULL");
+}
+
+pa::Desc to_desc(const pa_pool_desc* d) {
+  need(d, "desc");
+  return pa::Desc{d->block_size,      d->n_kv_heads,      d->head_dim,           d->kv_dtype,
+                  d->group_size,      d->num_blocks,      d->num_sink_blocks,    d->sink_blocks_per_seq};
+}
+
+void check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) fail(pa::kHip, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+pa::PoolDev dev_view(const pa_pool* p) {
+  pa::PoolDev v{};
+  const pa::Desc& d = p->core.desc();
+  v.base = p->dev;
+  v.n_kv_heads = d.n_kv_heads;
+  v.head_dim = d.head_dim;
+  v.kv_dtype = d.kv_dtype;
+  v.group_size = d.kv_dtype == pa::kInt4 ? d.group_size : d.head_dim;
+  v.num_blocks = d.num_blocks;
+  v.num_sink_blocks = d.num_sink_blocks;
+  for (int i = 0; i < pa::kNumArr; ++i) {
+    v.off[i] = p->layout.offset[i];
+    v.slab[i] = p->layout.slab[i];
+  }
+  return v;
+}
+
+void need_device(const pa_pool* p) {
+  need(p, "pool");
+  if (!p->dev) fail(pa::kInvalidArg, "metadata-only pool has no device memory");
+}
+
+void enqueue_copy(pa_pool* p, int32_t src, int32_t dst, void* stream) {
+  if (!p->dev) return;
+  check_hip(pa::launch_block_copy(dev_view(p), src, dst, static_cast<hipStream_t>(stream)),
+            "block copy launch");
+}
+
+// ---- decode planning ---------------------------------------------------------------
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+int32_t plan_split_blocks(int32_t batch, int32_t hkv, int32_t max_seq_len) {
+  const int forced = env_int("PA_SPLIT_BLOCKS", 0);  // tuning knob
+  if (forced > 0) return forced;
+  const int64_t nb = (int64_t(max_seq_len) + 15) / 16;
+  const int64_t pairs = int64_t(batch) * hkv;
+  int32_t s = 16;
+  // enough splits to fill 256 compute units several times over, no more
+  while (s < (1 << 20) && pairs * ((nb + s - 1) / s) > 4096) s *= 2;
+  return s;
+}
+
+struct Plan {
+  int32_t split_blocks, max_splits, kernel;
+  size_t ws_bytes;
+};
+
+Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+               int32_t q_dtype) {
+  const pa::Desc& d = p->core.desc();
+  Plan pl{};
+  pl.split_blocks = plan_split_blocks(batch, d.n_kv_heads, max_seq_len);
+  const int64_t nb = (int64_t(max_seq_len) + 15) / 16;
+  pl.max_splits = int32_t(std::max<int64_t>(1, (nb + pl.split_blocks - 1) / pl.split_blocks));
+  const bool mfma_ok = (d.kv_dtype == pa::kBF16 || d.kv_dtype == pa::kF16) &&
+                       q_dtype == d.kv_dtype && d.head_dim == 128 &&
+                       n_q_heads / d.n_kv_heads <= 16 && d.num_sink_blocks == 0;
+  const char* force = std::getenv("PA_DECODE_KERNEL");  // "generic" forces the VALU kernel
+  pl.kernel = (mfma_ok && !(force && std::strcmp(force, "generic") == 0)) ? pa::kKernMfma16
+                                                                          : pa::kKernGeneric;
+  pl.ws_bytes = pl.max_splits > 1 ? size_t(batch) * size_t(n_q_heads) * size_t(pl.max_splits) *
+                                        (size_t(d.head_dim) + 2) * sizeof(float)
+                                  : 0;
+  return pl;
+}
+
+void check_shapes(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_seq_len) {
+  need(p, "pool");
+  const pa::Desc& d = p->core.desc();
+  if (batch < 0 || batch > 65535) fail(pa::kInvalidArg, "batch must be in [0, 65535]");
+  if (n_q_heads < 1 || n_q_heads % d.n_kv_heads) fail(pa::kInvalidArg, "n_q_heads must be a multiple of n_kv_heads");
+  if (n_q_heads > 65535) fail(pa::kInvalidArg, "n_q_heads too large");
+  if (max_seq_len < 0) fail(pa::kInvalidArg, "negative max_seq_len");
+}
+
+enum Phase { kBoth = 3, kSplit = 1, kCombine = 2 };
+
+pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* tables,
+                 const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t q_dtype,
+                 int32_t max_blocks, int32_t max_seq_len, float scale, void* out, void* ws,
+                 size_t ws_bytes, void* stream) {
+  return guard([&] {
+    need_device(pool);
+    check_shapes(pool, batch, n_q_heads, max_seq_len);
+    const pa::Desc& d = pool->core.desc();
+    if (pa::is_raw(d.kv_dtype)) {
+      if (q_dtype != d.kv_dtype) fail(pa::kInvalidArg, "q_dtype must equal the pool's kv_dtype");
+    } else if (q_dtype != pa::kF16) {
+      fail(pa::kInvalidArg, "INT4/FP8 pools take fp16 queries");
+    }
+    if (max_blocks < 1) fail(pa::kInvalidArg, "max_blocks_per_seq must be >= 1");
+    if (int64_t(max_seq_len) > int64_t(max_blocks) * 16)
+      fail(pa::kInvalidArg, "max_seq_len exceeds 16 * max_blocks_per_seq");
+    if (!std::isfinite(scale)) fail(pa::kInvalidArg, "scale must be finite");
+    if (batch == 0) return;
+    need(q, "q");
+    need(tables, "block_tables_dev");
+    need(lens, "seq_lens_dev");
+    need(out, "out");
+    const Plan pl = make_plan(pool, batch, n_q_heads, max_seq_len, q_dtype);
+    if (pl.ws_bytes > 0) {
+      need(ws, "workspace");
+      if (ws_bytes < pl.ws_bytes)
+        fail(pa::kInvalidArg, "workspace too small: need " + std::to_string(pl.ws_bytes) + " bytes");
+      if (reinterpret_cast<uintptr_t>(ws) % 16) fail(pa::kInvalidArg, "workspace must be 16-byte aligned");
+    }
+    pa::DecodeArgs a{};
+    a.pool = dev_view(pool);
+    a.q = q;
+    a.tables = tables;
+    a.lens = lens;
+    a.batch = batch;
+    a.n_q_heads = n_q_heads;
+    a.q_dtype = q_dtype;
+    a.max_blocks_per_seq = max_blocks;
+    a.max_seq_len = max_seq_len;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out = out;
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_ml = pl.ws_bytes ? a.ws_o + size_t(batch) * n_q_heads * pl.max_splits * d.head_dim
+                          : nullptr;
+    a.split_blocks = pl.split_blocks;
+    a.max_splits = pl.max_splits;
+    a.kernel = pl.kernel;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (phase & kSplit) check_hip(pa::launch_decode_split(a, s), "decode split launch");
+    if (phase & kCombine) check_hip(pa::launch_decode_combine(a, s), "decode combine launch");
+  });
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_pool_bytes(const pa_pool_desc* desc, size_t* bytes) {
+  return guard([&] {
+    need(bytes, "bytes");
+    *bytes = pa::compute_layout(to_desc(desc)).total;
+  });
+}
+
+pa_status pa_pool_create(const pa_pool_desc* desc, void* dev_mem, size_t dev_bytes,
+                         const int32_t* body_free_order, const int32_t* sink_free_order,
+                         pa_pool** out) {
+  return guard([&] {
+    need(out, "out");
+    pa::Desc d = to_desc(desc);
+    pa::Layout L = pa::compute_layout(d);
+    if (dev_mem) {
+      if (dev_bytes < L.total)
+        fail(pa::kInvalidArg, "pool memory too small: need " + std::to_string(L.total) + " bytes");
+      if (reinterpret_cast<uintptr_t>(dev_mem) % 256) fail(pa::kInvalidArg, "pool memory must be 256-byte aligned");
+    } else if (dev_bytes != 0) {
+      fail(pa::kInvalidArg, "dev_bytes must be 0 for a metadata-only pool");
+    }
+    pa_pool* p = new pa_pool(d, body_free_order, sink_free_order);
+    p->dev = static_cast<uint8_t*>(dev_mem);
+    p->dev_bytes = dev_bytes;
+    *out = p;
+  });
+}
+
+pa_status pa_pool_destroy(pa_pool* pool) {
+  return guard([&] {
+    need(pool, "pool");
+    delete pool;
+  });
+}
+
+pa_status pa_pool_layout(const pa_pool* pool, pa_layout* out) {
+  return guard([&] {
+    need(pool, "pool");
+    need(out, "out");
+    out->total_bytes = pool->layout.total;
+    for (int i = 0; i < PA_NUM_ARR; ++i) {
+      out->offset[i] = pool->layout.offset[i];
+      out->slab_bytes[i] = pool->layout.slab[i];
+    }
+  });
+}
+
+pa_status pa_alloc_block(pa_pool* pool, int32_t arena, int32_t* out_id) {
+  return guard([&] {
+    need(pool, "pool");
+    need(out_id, "out_id");
+    *out_id = pool->core.alloc(arena);
+  });
+}
+
+pa_status pa_incref(pa_pool* pool, int32_t id) {
+  return guard([&] {
+    need(pool, "pool");
+    pool->core.incref(id);
+  });
+}
+
+pa_status pa_free_block(pa_pool* pool, int32_t id) {
+  return guard([&] {
+    need(pool, "pool");
+    pool->core.free_block(id);
+  });
+}
+
+pa_status pa_cow_clone(pa_pool* pool, int32_t src, int32_t* out_dst, void* stream) {
+  return guard([&] {
+    need(pool, "pool");
+    need(out_dst, "out_dst");
+    int32_t dst = pool->core.cow_clone(src);
+    *out_dst = dst;
+    enqueue_copy(pool, src, dst, stream);
+  });
+}
+
+pa_status pa_refcount(const pa_pool* pool, int32_t id, int32_t* out) {
+  return guard([&] {
+    need(pool, "pool");
+    need(out, "out");
+    *out = pool->core.refcount(id);
+  });
+}
+
+pa_status pa_num_free(const pa_pool* pool, int32_t arena, int32_t* out) {
+  return guard([&] {
+    need(pool, "pool");
+    need(out, "out");
+    *out = pool->core.num_free(arena);
+  });
+}
+
+pa_status pa_free_list(const pa_pool* pool, int32_t arena, int32_t* out, int32_t cap, int32_t* n) {
+  return guard([&] {
+    need(pool, "pool");
+    need(n, "n");
+    if (cap < 0) fail(pa::kInvalidArg, "negative cap");
+    std::vector<int32_t> f = pool->core.free_list(arena);
+    const int32_t m = std::min<int32_t>(cap, int32_t(f.size()));
+    if (m > 0) need(out, "out");
+    for (int32_t i = 0; i < m; ++i) out[i] = f[size_t(i)];
+    *n = m;
+  });
+}
+
+pa_status pa_num_clones(const pa_pool* pool, int64_t* out) {
+  return guard([&] {
+    need(pool, "pool");
+    need(out, "out");
+    *out = pool->core.num_clones();
+  });
+}
+
+pa_status pa_seq_create(pa_pool* pool, int32_t* out_seq) {
+  return guard([&] {
+    need(pool, "pool");
+    need(out_seq, "out_seq");
+    *out_seq = pool->core.seq_create();
+  });
+}
+
+pa_status pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* out_child) {
+  return guard([&] {
+    need(pool, "pool");
+    need(out_child, "out_child");
+    *out_child = pool->core.seq_fork(parent);
+  });
+}
+
+pa_status pa_seq_reserve(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* slots_out,
+                         void* stream) {
+  return guard([&] {
+    need(pool, "pool");
+    if (n_tokens > 0) need(slots_out, "slots_out");
+    std::vector<std::pair<int32_t, int32_t>> clones;
+    std::vector<int32_t> slots = pool->core.seq_reserve(seq, n_tokens, &clones);
+    if (!slots.empty()) std::memcpy(slots_out, slots.data(), slots.size() * sizeof(int32_t));
+    for (const auto& c : clones) enqueue_copy(pool, c.first, c.second, stream);
+  });
+}
+
+pa_status pa_seq_truncate(pa_pool* pool, int32_t seq, int32_t new_len) {
+  return guard([&] {
+    need(pool, "pool");
+    pool->core.seq_truncate(seq, new_len);
+  });
+}
+
+pa_status pa_seq_release(pa_pool* pool, int32_t seq) {
+  return guard([&] {
+    need(pool, "pool");
+    pool->core.seq_release(seq);
+  });
+}
+
+pa_status pa_seq_info(const pa_pool* pool, int32_t seq, int32_t* len, int32_t* n_blocks) {
+  return guard([&] {
+    need(pool, "pool");
+    const pa::Seq& s = pool->core.seq(seq);
+    if (len) *len = s.length;
+    if (n_blocks) *n_blocks = int32_t(s.table.size());
+  });
+}
+
+pa_status pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n, int32_t max_blocks,
+                          int32_t* tables_out, int32_t* lens_out) {
+  return guard([&] {
+    need(pool, "pool");
+    if (n < 0 || max_blocks < 0) fail(pa::kInvalidArg, "negative size");
+    if (n == 0) return;
+    need(seqs, "seqs");
+    need(tables_out, "tables_out");
+    for (int32_t i = 0; i < n; ++i) {
+      const pa::Seq& s = pool->core.seq(seqs[i]);
+      if (int64_t(s.table.size()) > max_blocks)
+        fail(pa::kInvalidArg, "sequence " + std::to_string(seqs[i]) + " has more blocks than max_blocks");
+    }
+    for (int32_t i = 0; i < n; ++i) {
+      const pa::Seq& s = pool->core.seq(seqs[i]);
+      int32_t* row = tables_out + size_t(i) * size_t(max_blocks);
+      for (int32_t j = 0; j < max_blocks; ++j)
+        row[j] = size_t(j) < s.table.size() ? s.table[size_t(j)] : -1;
+      if (lens_out) lens_out[i] = s.length;
+    }
+  });
+}
+
+pa_status pa_append_kv(pa_pool* pool, const void* k, const void* v, int32_t in_dtype,
+                       const int32_t* slots_dev, int32_t n_tokens, void* stream) {
+  return guard([&] {
+    need_device(pool);
+    if (!pa::is_raw(in_dtype)) fail(pa::kInvalidArg, "in_dtype must be F32, F16 or BF16");
+    if (n_tokens < 0) fail(pa::kInvalidArg, "negative n_tokens");
+    if (n_tokens == 0) return;
+    need(k, "k");
+    need(v, "v");
+    need(slots_dev, "slots_dev");
+    check_hip(pa::launch_append(dev_view(pool), k, v, in_dtype, slots_dev, n_tokens,
+                                static_cast<hipStream_t>(stream)),
+              "append launch");
+  });
+}
+
+pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
+                                    int32_t max_seq_len, size_t* bytes) {
+  return guard([&] {
+    check_shapes(pool, batch, n_q_heads, max_seq_len);
+    need(bytes, "bytes");
+    const pa::Desc& d = pool->core.desc();
+    const int32_t qdt = pa::is_raw(d.kv_dtype) ? d.kv_dtype : int32_t(pa::kF16);
+    *bytes = make_plan(pool, batch, n_q_heads, max_seq_len, qdt).ws_bytes;
+  });
+}
+
+pa_status pa_decode_split_blocks(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
+                                 int32_t max_seq_len, int32_t* out) {
+  return guard([&] {
+    check_shapes(pool, batch, n_q_heads, max_seq_len);
+    need(out, "out");
+    *out = plan_split_blocks(batch, pool->core.desc().n_kv_heads, max_seq_len);
+  });
+}
+
+pa_status pa_decode_attention(const void* q, const pa_pool* pool, const int32_t* tables,
+                              const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t q_dtype,
+                              int32_t max_blocks, int32_t max_seq_len, float scale, void* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return decode(kBoth, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
+                scale, out, ws, ws_bytes, stream);
+}
+
+pa_status pa_decode_split(const void* q, const pa_pool* pool, const int32_t* tables,
+                          const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t q_dtype,
+                          int32_t max_blocks, int32_t max_seq_len, float scale, void* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return decode(kSplit, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
+                scale, out, ws, ws_bytes, stream);
+}
+
+pa_status pa_decode_combine(const void* q, const pa_pool* pool, const int32_t* tables,
+                            const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t q_dtype,
+                            int32_t max_blocks, int32_t max_seq_len, float scale, void* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return decode(kCombine, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks,
+                max_seq_len, scale, out, ws, ws_bytes, stream);
+}
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Host core of libpa: pool descriptor checks, pool memory layout, the LIFO
+// block allocator with refcounts, and per-sequence block tables.  Pure C++17,
+// no HIP: it builds with g++ as well as hipcc.
+//
+// Sources: "The 8GB VRAM Breakthrough ..." section 3 (flat pool of 16-token
+// blocks, block tables, copy-on-write of a partially filled shared block) and
+// section 4 (FP16 sink blocks beside a compressed body); "A Ideia de 60 Anos
+// Que Domou a Memoria da GPU", "o codigo" (pool = stack of free ids + one
+// refcount per block: rent pops, return pushes when the count reaches zero)
+// and "a ideia roubada" (a new block only when the previous one is full).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <utility>
+#include <vector>
+
+namespace pa {
+
+enum Status : int32_t {
+  kOk = 0,
+  kInvalidArg = 1,
+  kOutOfBlocks = 2,
+  kRefcount = 3,
+  kBadId = 4,
+  kUnsupported = 5,
+  kHip = 6,
+};
+
+enum Dtype : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2, kInt4 = 3, kFp8 = 4 };
+enum Arena : int32_t { kBody = 0, kSink = 1 };
+enum ArrayId : int32_t { kArrK = 0, kArrV, kArrKS, kArrKZ, kArrVS, kArrVZ, kArrSK, kArrSV, kNumArr };
+
+constexpr int32_t kBlock = 16;
+
+// Thrown inside the library, turned into a status at the C boundary.
+struct Error {
+  Status code;
+  std::string msg;
+};
+
+struct Desc {
+  int32_t block_size, n_kv_heads, head_dim, kv_dtype, group_size, num_blocks, num_sink_blocks,
+      sink_blocks_per_seq;
+};
+
+struct Layout {
+  size_t total = 0;
+  size_t offset[kNumArr];
+  size_t slab[kNumArr];
+  int32_t nblocks[kNumArr];  // slabs per head in the array (arena size)
+};
+
+bool is_raw(int32_t dt);
+int32_t elem_bytes(int32_t dt);  // raw dtypes only
+void validate_desc(const Desc& d);
+Layout compute_layout(const Desc& d);
+
+struct Seq {
+  std::vector<int32_t> table;
+  int32_t length = 0;
+  bool live = false;
+};
+
+class PoolCore {
+ public:
+  PoolCore(const Desc& d, const int32_t* body_order, const int32_t* sink_order);
+
+  const Desc& desc() const { return d_; }
+  int32_t total_blocks() const { return d_.num_blocks + d_.num_sink_blocks; }
+  int32_t arena_of(int32_t id) const;
+
+  int32_t alloc(int32_t arena);
+  void incref(int32_t id);
+  void free_block(int32_t id);
+  // Pops a block of src's arena, drops one ref of src; the caller copies data.
+  int32_t cow_clone(int32_t src);
+  int32_t refcount(int32_t id) const;
+  int32_t num_free(int32_t arena) const;
+  std::vector<int32_t> free_list(int32_t arena) const;  // next pop first
+  int64_t num_clones() const { return clones_; }
+
+  int32_t seq_create();
+  int32_t seq_fork(int32_t parent);
+  // Appends n slots; clones (src, dst) performed are appended to *clones.
+  std::vector<int32_t> seq_reserve(int32_t seq, int32_t n,
+                                   std::vector<std::pair<int32_t, int32_t>>* clones);
+  void seq_truncate(int32_t seq, int32_t new_len);
+  void seq_release(int32_t seq);
+  const Seq& seq(int32_t id) const;
+
+ private:
+  Seq& seq_mut(int32_t id);
+  void check_id(int32_t id) const;
+  void check_drop(const std::vector<int32_t>& blocks, size_t from) const;
+  int32_t arena_for_logical(int32_t j) const;
+
+  Desc d_;
+  std::vector<int32_t> ref_;
+  std::vector<int32_t> stack_[2];  // back() is the top
+  std::vector<Seq> seqs_;
+  int64_t clones_ = 0;
+};
+
+}  // namespace pa

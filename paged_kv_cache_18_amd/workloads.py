@@ -189,6 +189,30 @@ def shared_prefix(seed=5, prefix=2000, n_children=32, max_suffix=512):
                            "suffix": suffix})
 
 
+def from_lengths(lengths, n_q_heads=32, n_kv_heads=8, head_dim=128, kv_dtype="bf16", seed=11,
+                 name="custom", group=0, sink=False, outliers=False):
+    """Sequences of the given lengths (prefilled sequence-major), pool of the
+    blocks needed + 10 % in a seeded random order.  For a quantized body,
+    ``sink=True`` puts logical block 0 in a FP16 sink arena."""
+    lengths = [int(L) for L in lengths]
+    qdt = kv_dtype if kv_dtype in ("f32", "f16", "bf16") else "f16"
+    n_sink = len(lengths) if sink else 0
+    body = sum(max(0, -(-L // BLOCK) - (1 if sink else 0)) for L in lengths)
+    n = max(1, _pool_size(body))
+    perm = rng(seed, 0).permutation(n)
+    outl = None
+    if outliers:
+        n_out = max(1, int(round(0.01 * n_kv_heads * head_dim)))
+        outl = np.sort(rng(seed, 4).choice(n_kv_heads * head_dim, size=n_out, replace=False))
+    return Workload(name, seed, n_q_heads, n_kv_heads, head_dim, kv_dtype, qdt, qdt, n, perm,
+                    _prefill_ops(lengths), list(range(len(lengths))),
+                    {b: [(1, b, L)] for b, L in enumerate(lengths)},
+                    group_size=group, num_sink_blocks=n_sink,
+                    sink_blocks_per_seq=1 if sink else 0,
+                    sink_free_order=rng(seed, 5).permutation(n_sink) if sink else None,
+                    outlier_channels=outl, extra={"lengths": lengths})
+
+
 def by_name(name, **kw):
     table = {
         "tiny": tiny,

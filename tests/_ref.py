@@ -1,0 +1,96 @@
+"""Test-side glue between workloads and the oracle (CPU).
+
+Builds, from a workload's seeded inputs and the oracle only, the values the
+library must store and the outputs it must produce.  Nothing here calls the
+library.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import attention as AT
+from oracle import quant as QT
+
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def cast64(x, dt):
+    """fp32 numpy -> stored dtype (torch's RNE cast) -> float64."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to(TORCH_DT[dt]).to(torch.float64).numpy()
+
+
+def stored_values(wl, sid):
+    """Float64 [L][Hkv][D] K and V the pool must hold for sequence sid, plus
+    (for quantized bodies) the oracle's codes/scales/zeros of the body tokens."""
+    K, V = wl.seq_tokens(sid)
+    if wl.kv_dtype in TORCH_DT:
+        return cast64(K, wl.kv_dtype), cast64(V, wl.kv_dtype), None
+    Kh = cast64(K, "f16").astype(np.float16)
+    Vh = cast64(V, "f16").astype(np.float16)
+    sink = 16 * wl.sink_blocks_per_seq
+    Kq, Vq = Kh.astype(np.float64), Vh.astype(np.float64)
+    codes = {}
+    if Kh.shape[0] <= sink:
+        return Kq, Vq, {}
+    if wl.kv_dtype == "int4":
+        for name, X, out in (("K", Kh, Kq), ("V", Vh, Vq)):
+            q, s, z = QT.int4_quantize(X[sink:], wl.group_size)
+            out[sink:] = QT.int4_dequant(q, s, z, wl.group_size)
+            codes[name], codes[name + "S"], codes[name + "Z"] = q, s, z
+    else:
+        for name, X, out in (("K", Kh, Kq), ("V", Vh, Vq)):
+            c, s = QT.fp8_quantize(X[sink:])
+            out[sink:] = QT.fp8_dequant(c, s)
+            codes[name], codes[name + "S"] = c, s
+    return Kq, Vq, codes
+
+
+def q_values(wl):
+    return cast64(wl.q(), wl.q_dtype)
+
+
+def expected(wl, seqs=None, pairs=None):
+    """Oracle outputs [B][Hq][D] (float64); with ``pairs`` = list of (b, hq)
+    only those rows are computed (others NaN)."""
+    seqs = wl.decode_seqs if seqs is None else seqs
+    q = q_values(wl)
+    out = np.full((len(seqs), wl.n_q_heads, wl.head_dim), np.nan)
+    want = None if pairs is None else {}
+    if pairs is not None:
+        for b, h in pairs:
+            want.setdefault(b, []).append(h)
+    for b, sid in enumerate(seqs):
+        if want is not None and b not in want:
+            continue
+        K, V, _ = stored_values(wl, sid)
+        full = AT.attention_one(q[b], K, V, wl.scale)
+        if want is None:
+            out[b] = full
+        else:
+            for h in want[b]:
+                out[b, h] = full[h]
+    return out
+
+
+def tolerance(ref, out_dtype):
+    """1e-5 for fp32 outputs; 2e-3 for 16-bit/quantized outputs, plus half an
+    ulp of the output dtype (the single final rounding the output stores)."""
+    ref = np.abs(np.asarray(ref, np.float64))
+    if out_dtype == "f32":
+        return 1e-5 + 0.0 * ref
+    mant = 7 if out_dtype == "bf16" else 10
+    e = np.floor(np.log2(np.maximum(ref, 1e-30)))
+    return 2e-3 + np.where(ref > 0, 2.0 ** (e - mant - 1), 0.0)
+
+
+def assert_close(got, ref, out_dtype, what=""):
+    got = np.asarray(got, np.float64)
+    mask = ~np.isnan(ref)
+    err = np.abs(got[mask] - ref[mask])
+    tol = tolerance(ref[mask], out_dtype)
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; "
+                           f"max err {err.max():.3g}")
+    return float(err.max()) if err.size else 0.0

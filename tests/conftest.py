@@ -23,3 +23,13 @@ def golden():
         with open(os.path.join(GOLDEN, name)) as f:
             return json.load(f)
     return load
+
+
+@pytest.fixture(scope="session")
+def libpa():
+    """The built library; built once if it is missing."""
+    from paged_kv_cache_18_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from paged_kv_cache_18_amd import build
+        build.build()
+    return binding.lib()
