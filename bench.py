@@ -160,31 +160,36 @@ def main():
     dargs = (q, kv.pool, tdev, ldev, wl.batch, wl.n_q_heads, wl.q_dtype, tdev.shape[1], max_len,
              wl.scale, out, ws, ws.numel(), sh)
 
-    split_ev = []
-
-    def step(record):
+    def step():
         B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, wl.batch, sh)
-        if record:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
         B.pa_decode_split(*dargs)
-        if record:
-            e1.record(stream)
-            split_ev.append((e0, e1))
         B.pa_decode_combine(*dargs)
 
     print(f"[bench] warmup {args.warmup} ...", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps ...", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
+
+    # the dominant kernel's launch durations: the same steps again, with HIP
+    # events on the launch stream around every split launch
+    split_ev = []
+    for _ in range(args.steps):
+        B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, wl.batch, sh)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        B.pa_decode_split(*dargs)
+        e1.record(stream)
+        split_ev.append((e0, e1))
+        B.pa_decode_combine(*dargs)
+    torch.cuda.synchronize()
     split_ms = [a.elapsed_time(b) for a, b in split_ev]
     split_avg = float(np.mean(split_ms))
 
@@ -194,10 +199,13 @@ def main():
 
     extra = {}
     if args.cold:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        # evict the caches by *reading* 512 MiB (more than the 256 MB
+        # Infinity Cache plus the L2s); a write would leave dirty lines whose
+        # write-back would compete with the timed kernel
+        flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         cold = []
         for _ in range(max(10, args.steps // 2)):
-            flush.fill_(1)
+            flush.sum()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -209,6 +217,19 @@ def main():
         extra["cold_split_ms_median"] = round(float(np.median(cold)), 4)
         extra["cold_split_gbs"] = round(byts / (np.median(cold) * 1e-3) / 1e9, 1)
         del flush
+    # streaming-read ceiling: a plain reduction over the same number of bytes
+    ceil_buf = torch.ones(byts // 4, dtype=torch.float32, device=dev)
+    ceil_buf.sum()
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        ceil_buf.sum()
+    c1.record(stream)
+    torch.cuda.synchronize()
+    extra["stream_read_ceiling_gbs"] = round(byts / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9, 1)
+    del ceil_buf
     if args.copy_calibration:
         a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)

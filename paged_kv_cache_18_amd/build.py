@@ -26,6 +26,9 @@ COMMON = [
     # the packed fp32 instructions stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    # matrix-core accumulators in ordinary VGPRs: the softmax rescale touches
+    # them with vector ALU ops, which AGPRs would force to copy back and forth
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

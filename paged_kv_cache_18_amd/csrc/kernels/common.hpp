@@ -105,6 +105,11 @@ __device__ inline float wave_min(float x) {
   for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o, 64));
   return x;
 }
+__device__ inline int wave_sum_int(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
 __device__ inline float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);

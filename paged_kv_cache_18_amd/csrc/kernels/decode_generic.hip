@@ -134,8 +134,14 @@ __global__ __launch_bounds__(64) void decode_split_generic(DecodeArgs a) {
 }
 
 // Merge the splits of one (sequence, query head): m = max m_i,
-// l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.
+// l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.  The statistics of all
+// splits are read in parallel (one split per lane), the normalized weights go
+// through LDS, and each lane sums its dimensions over the splits with
+// independent loads.
+constexpr int kCombineChunk = 256;
+
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+  __shared__ float wsh[kCombineChunk];
   const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int D = a.pool.head_dim, Hq = a.n_q_heads, S = a.split_blocks;
   const int L = min(max(a.lens[b], 0), a.max_seq_len);
@@ -143,35 +149,66 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   if (nsplit <= 1) return;
   const size_t row = (size_t(b) * Hq + hq) * a.max_splits;
   const float* ml = a.ws_ml + row * 2;
-  float M = -__builtin_inff();
-  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
+  const float ninf = -__builtin_inff();
+  float M = ninf;
+  for (int i = lane; i < nsplit; i += 64) M = fmaxf(M, ml[2 * i]);
+  M = wave_max(M);
   // a split whose blocks were all skipped has max -inf and weight 0
   float lsum = 0.f;
-  for (int i = 0; i < nsplit; ++i)
-    if (ml[2 * i] != -__builtin_inff()) lsum += ml[2 * i + 1] * exp2f(ml[2 * i] - M);
+  for (int i = lane; i < nsplit; i += 64)
+    if (ml[2 * i] != ninf) lsum += ml[2 * i + 1] * exp2f(ml[2 * i] - M);
+  lsum = wave_sum(lsum);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  for (int d = lane; d < D; d += 64) {
-    float o = 0.f;
-    for (int i = 0; i < nsplit; ++i)
-      if (ml[2 * i] != -__builtin_inff()) o += a.ws_o[(row + i) * D + d] * exp2f(ml[2 * i] - M);
-    store_out(a.out, (size_t(b) * Hq + hq) * D + d, o * inv, a.q_dtype);
+  float acc[kMaxDimPerLane] = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nsplit; c0 += kCombineChunk) {
+    const int cn = min(kCombineChunk, nsplit - c0);
+    __syncthreads();
+    for (int i = lane; i < cn; i += 64) {
+      const float m = ml[2 * (c0 + i)];
+      wsh[i] = m != ninf ? exp2f(m - M) * inv : 0.f;
+    }
+    __syncthreads();
+    const float* base = a.ws_o + (row + c0) * D;
+#pragma unroll
+    for (int k = 0; k < kMaxDimPerLane; ++k) {
+      const int d = lane + 64 * k;
+      if (d >= D) break;
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      int i = 0;
+      for (; i + 4 <= cn; i += 4) {
+        s0 += base[size_t(i + 0) * D + d] * wsh[i + 0];
+        s1 += base[size_t(i + 1) * D + d] * wsh[i + 1];
+        s2 += base[size_t(i + 2) * D + d] * wsh[i + 2];
+        s3 += base[size_t(i + 3) * D + d] * wsh[i + 3];
+      }
+      for (; i < cn; ++i) s0 += base[size_t(i) * D + d] * wsh[i];
+      acc[k] += (s0 + s1) + (s2 + s3);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxDimPerLane; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) store_out(a.out, (size_t(b) * Hq + hq) * D + d, acc[k], a.q_dtype);
   }
 }
 
 }  // namespace
 
 hipError_t launch_decode_split_mfma16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_combine_mfma16(const DecodeArgs& a, hipStream_t s);
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
-  if (a.kernel == kKernMfma16) return launch_decode_split_mfma16(a, s);
+  if (a.kernel == kKernMfma16) return a.max_splits > 0 ? launch_decode_split_mfma16(a, s) : hipSuccess;
   dim3 grid(unsigned(a.max_splits), unsigned(a.n_q_heads), unsigned(a.batch));
   hipLaunchKernelGGL(decode_split_generic, grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s) {
-  if (a.batch <= 0 || a.max_splits <= 1) return hipSuccess;
+  if (a.batch <= 0) return hipSuccess;
+  if (a.kernel == kKernMfma16) return launch_decode_combine_mfma16(a, s);
+  if (a.max_splits <= 1) return hipSuccess;
   dim3 grid(unsigned(a.n_q_heads), unsigned(a.batch));
   hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(64), 0, s, a);
   return hipGetLastError();

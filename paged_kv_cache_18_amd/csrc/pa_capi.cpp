@@ -108,27 +108,68 @@ int32_t plan_split_blocks(int32_t batch, int32_t hkv, int32_t max_seq_len) {
   return s;
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 struct Plan {
   int32_t split_blocks, max_splits, kernel;
-  size_t ws_bytes;
+  size_t ws_bytes, ws_ml_offset;  // bytes; ws_ml_offset = float index of the (max, sum) area
 };
+
+// Upper bound of the flattened work list (blocks of all (sequence, kv head)
+// segments) from the shapes alone.
+int64_t flat_upper(int32_t batch, int32_t hkv, int32_t max_seq_len) {
+  return int64_t(batch) * hkv * ((int64_t(max_seq_len) + 15) / 16);
+}
 
 Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
                int32_t q_dtype) {
   const pa::Desc& d = p->core.desc();
   Plan pl{};
-  pl.split_blocks = plan_split_blocks(batch, d.n_kv_heads, max_seq_len);
-  const int64_t nb = (int64_t(max_seq_len) + 15) / 16;
-  pl.max_splits = int32_t(std::max<int64_t>(1, (nb + pl.split_blocks - 1) / pl.split_blocks));
   const bool mfma_ok = (d.kv_dtype == pa::kBF16 || d.kv_dtype == pa::kF16) &&
                        q_dtype == d.kv_dtype && d.head_dim == 128 &&
                        n_q_heads / d.n_kv_heads <= 16 && d.num_sink_blocks == 0;
   const char* force = std::getenv("PA_DECODE_KERNEL");  // "generic" forces the VALU kernel
   pl.kernel = (mfma_ok && !(force && std::strcmp(force, "generic") == 0)) ? pa::kKernMfma16
                                                                           : pa::kKernGeneric;
-  pl.ws_bytes = pl.max_splits > 1 ? size_t(batch) * size_t(n_q_heads) * size_t(pl.max_splits) *
-                                        (size_t(d.head_dim) + 2) * sizeof(float)
-                                  : 0;
+  const int64_t nb = (int64_t(max_seq_len) + 15) / 16;
+  if (pl.kernel == pa::kKernMfma16) {
+    // Fixed chunks of the flattened list; two partial slots per workgroup.
+    const int64_t w = flat_upper(batch, d.n_kv_heads, max_seq_len);
+    if (w >= (int64_t(1) << 31) - 4096) fail(pa::kInvalidArg, "batch * n_kv_heads * blocks too large");
+    const int32_t c = env_int("PA_SPLIT_BLOCKS", 0);  // fixed chunk size (tuning/tests)
+    if (c > 0) {
+      pl.split_blocks = c;
+      pl.max_splits = int32_t((w + c - 1) / c);
+    } else {
+      // persistent grid: one 4-wave workgroup per resident slot; the chunk
+      // size is derived on the device from the actual lengths
+      pl.split_blocks = 0;
+      const int per_cu = std::max(1, env_int("PA_WG_PER_CU", 3));
+      pl.max_splits = int32_t(std::max<int64_t>(1, std::min<int64_t>(w, int64_t(cu_count()) * per_cu)));
+    }
+    const size_t g = size_t(n_q_heads / d.n_kv_heads);
+    const size_t rows = size_t(pl.max_splits) * 2 * g;
+    pl.ws_ml_offset = rows * size_t(d.head_dim);
+    pl.ws_bytes = rows * (size_t(d.head_dim) + 2) * sizeof(float);
+    return pl;
+  }
+  pl.split_blocks = plan_split_blocks(batch, d.n_kv_heads, max_seq_len);
+  pl.max_splits = int32_t(std::max<int64_t>(1, (nb + pl.split_blocks - 1) / pl.split_blocks));
+  const size_t rows = size_t(batch) * size_t(n_q_heads) * size_t(pl.max_splits);
+  pl.ws_ml_offset = rows * size_t(d.head_dim);
+  pl.ws_bytes = pl.max_splits > 1 ? rows * (size_t(d.head_dim) + 2) * sizeof(float) : 0;
   return pl;
 }
 
@@ -185,8 +226,7 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out = out;
     a.ws_o = static_cast<float*>(ws);
-    a.ws_ml = pl.ws_bytes ? a.ws_o + size_t(batch) * n_q_heads * pl.max_splits * d.head_dim
-                          : nullptr;
+    a.ws_ml = pl.ws_bytes ? a.ws_o + pl.ws_ml_offset : nullptr;
     a.split_blocks = pl.split_blocks;
     a.max_splits = pl.max_splits;
     a.kernel = pl.kernel;
@@ -422,7 +462,10 @@ pa_status pa_decode_split_blocks(const pa_pool* pool, int32_t batch, int32_t n_q
   return guard([&] {
     check_shapes(pool, batch, n_q_heads, max_seq_len);
     need(out, "out");
-    *out = plan_split_blocks(batch, pool->core.desc().n_kv_heads, max_seq_len);
+    const pa::Desc& d = pool->core.desc();
+    const int32_t qdt = pa::is_raw(d.kv_dtype) ? d.kv_dtype : int32_t(pa::kF16);
+    const Plan pl = make_plan(pool, batch, n_q_heads, max_seq_len, qdt);
+    *out = pl.split_blocks > 0 ? pl.split_blocks : -pl.max_splits;
   });
 }
 
