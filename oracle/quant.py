@@ -59,7 +59,8 @@ def to_bf16_bits(x):
 
 
 def bf16_bits_to_f64(bits):
-    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # unwritten pool slots may hold NaN patterns
+        return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 # ---- asymmetric INT4 -------------------------------------------------------------

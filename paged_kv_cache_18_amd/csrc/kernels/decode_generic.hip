@@ -195,11 +195,22 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_split_mfma16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_split_quant(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_combine_mfma16(const DecodeArgs& a, hipStream_t s);
+
+int occupancy_mfma16(int32_t kv_dtype);
+int occupancy_quant(int32_t kv_dtype);
+
+int decode_split_occupancy(int32_t kernel, int32_t kv_dtype) {
+  if (kernel == kKernMfma16) return occupancy_mfma16(kv_dtype);
+  if (kernel == kKernQuant) return occupancy_quant(kv_dtype);
+  return 1;
+}
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
   if (a.kernel == kKernMfma16) return a.max_splits > 0 ? launch_decode_split_mfma16(a, s) : hipSuccess;
+  if (a.kernel == kKernQuant) return a.max_splits > 0 ? launch_decode_split_quant(a, s) : hipSuccess;
   dim3 grid(unsigned(a.max_splits), unsigned(a.n_q_heads), unsigned(a.batch));
   hipLaunchKernelGGL(decode_split_generic, grid, dim3(64), 0, s, a);
   return hipGetLastError();
@@ -207,7 +218,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
-  if (a.kernel == kKernMfma16) return launch_decode_combine_mfma16(a, s);
+  if (a.kernel == kKernMfma16 || a.kernel == kKernQuant) return launch_decode_combine_mfma16(a, s);
   if (a.max_splits <= 1) return hipSuccess;
   dim3 grid(unsigned(a.n_q_heads), unsigned(a.batch));
   hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(64), 0, s, a);

@@ -43,118 +43,27 @@
 // The loads of a wave's next block are issued before its current block is
 // consumed (two register buffers).  After each piece the 4 waves merge
 // (max, sum, acc) through LDS.
-#include "common.hpp"
+#include "decode_common.hpp"
 
 namespace pa {
 
 namespace {
 
-constexpr int kD = 128;        // head_dim handled here
-constexpr int kNT = kD / 16;   // 16-dim output tiles
-constexpr int kWaves = 4;
-
-typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
-
-template <typename T>
-struct Mfma;
-
-template <>
-struct Mfma<__bf16> {
-  typedef __bf16 v8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-  typedef __bf16 v4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
-  static __device__ inline f32x4 qk(v8 a, v8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-  static __device__ inline f32x4 pv(v4 a, v4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Mfma<_Float16> {
-  typedef _Float16 v8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
-  typedef _Float16 v4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
-  static __device__ inline f32x4 qk(v8 a, v8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-  static __device__ inline f32x4 pv(v4 a, v4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-  }
-};
-
-__device__ inline int seq_blocks(const DecodeArgs& a, int b) {
-  const int L = min(max(a.lens[b], 0), a.max_seq_len);
-  return (L + 15) >> 4;
-}
-
-// Start of sequence b's segments in the flattened list: Hkv * sum_{b'<b} nb_b'.
-__device__ inline int seq_start(const DecodeArgs& a, int b, int lane) {
-  int acc = 0;
-  for (int base = 0; base < b; base += 64) {
-    const int bb = base + lane;
-    acc += bb < b ? seq_blocks(a, bb) : 0;
-  }
-  return wave_sum_int(acc) * a.pool.n_kv_heads;
-}
+using namespace dec;
 
 template <typename T>
 __global__ __launch_bounds__(kWaves * 64) void decode_split_mfma16(DecodeArgs a) {
   typedef typename Mfma<T>::v8 v8;
   typedef typename Mfma<T>::v4 v4;
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
-  __shared__ float sm_o[kWaves][16][kD + 1];
-  __shared__ int sh_b, sh_fb, sh_c;
+  __shared__ Shared sh;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4, c = lane & 15;
   const PoolDev& p = a.pool;
-  const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H, B = a.batch;
-  T* out = static_cast<T*>(a.out);
-  // ---- locate the chunk: wave 0 scans the per-sequence sizes ---------------------
-  // With a.split_blocks == 0 the chunk size is derived from the total work W
-  // so that the grid (one workgroup per resident slot) shares it evenly.
-  if (w == 0) {
-    int C = a.split_blocks;
-    if (C <= 0) {
-      int tot = 0;
-      for (int base = 0; base < B; base += 64)
-        tot += base + lane < B ? seq_blocks(a, base + lane) * H : 0;
-      tot = wave_sum_int(tot);
-      C = max(1, (tot + int(gridDim.x) - 1) / int(gridDim.x));
-    }
-    const int pos0 = int(blockIdx.x) * C;
-    int run = 0, fb = 0, fbi = -1;
-    for (int base = 0; base < B; base += 64) {
-      const int bb = base + lane;
-      const int sz = bb < B ? seq_blocks(a, bb) * H : 0;
-      int incl = sz;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-      }
-      const unsigned long long hit = __ballot(run + incl > pos0);
-      if (hit) {
-        const int fl = __builtin_ctzll(hit);
-        fbi = base + fl;
-        fb = run + __shfl(incl - sz, fl, 64);
-        break;
-      }
-      run += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) {
-      sh_b = fbi;
-      sh_fb = fb;
-      sh_c = C;
-    }
-  }
-  __syncthreads();
-  int b = sh_b, fb = sh_fb;
-  const int C = sh_c;
-  const int pos0 = int(blockIdx.x) * C, pos1 = pos0 + C;
-  if (b < 0) return;  // chunk past the end of the work
+  const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H;
+  int b, fb, pos0, pos1;
+  if (!locate_chunk(a, sh, w, lane, b, fb, pos0, pos1)) return;  // past the work
 
   const T* kbase = reinterpret_cast<const T*>(p.base + p.off[kArrK]);
   const T* vbase = reinterpret_cast<const T*>(p.base + p.off[kArrV]);
@@ -256,17 +165,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_mfma16(DecodeArgs a)
 
   int pos = pos0;
   bool first = true;
-  while (pos < pos1 && b < B) {
-    const int nb = seq_blocks(a, b);
-    if (pos >= fb + nb * H) {  // past sequence b (also skips empty ones)
-      fb += nb * H;
-      ++b;
-      continue;
-    }
-    h = (pos - fb) / nb;
-    const int jbeg = (pos - fb) % nb;
-    const int jend = min(nb, jbeg + (pos1 - pos));
-    L = min(max(a.lens[b], 0), a.max_seq_len);
+  int jbeg = 0, jend = 0, nb = 0;
+  while (next_piece(a, pos, pos1, b, fb, h, jbeg, jend, nb)) {
+    L = seq_len(a, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
     {
       // Q^T fragment: lane (g, c) holds Q[h*G + c][32kk + 8g .. +7], zero for c >= G.
@@ -305,45 +206,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_mfma16(DecodeArgs a)
       if (k < n) consume(valid_of(k, ida), ka, va);
     }
 
-    // ---- merge the 4 waves of this piece -------------------------------------
+    // ---- merge the 4 waves of this piece, write it -----------------------------
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
-    if (g == 0) {
-      sm_m[w][c] = m_ref;
-      sm_l[w][c] = l_run;
-    }
-#pragma unroll
-    for (int T_ = 0; T_ < kNT; ++T_)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[w][c][kNT * (4 * g + i) + T_] = o[T_][i];
-    __syncthreads();
-    const bool complete = jbeg == 0 && jend == nb;
-    const int slot = first ? 0 : 1;
-    for (int idx = threadIdx.x; idx < G * kD; idx += kWaves * 64) {
-      const int hc = idx / kD, d = idx % kD;
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm_m[v][hc]);
-      float lsum = 0.f, osum = 0.f;
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) {
-        if (sm_m[v][hc] == -__builtin_inff()) continue;  // wave saw no block
-        const float wt = exp2f(sm_m[v][hc] - M);
-        lsum += sm_l[v][hc] * wt;
-        osum += sm_o[v][hc][d] * wt;
-      }
-      if (complete) {
-        out[(size_t(b) * Hq + h * G + hc) * kD + d] = T(lsum > 0.f ? osum / lsum : 0.f);
-      } else {
-        const size_t row = (size_t(blockIdx.x) * 2 + slot) * G + hc;
-        a.ws_o[row * kD + d] = osum;
-        if (d == 0) {
-          a.ws_ml[row * 2] = M;
-          a.ws_ml[row * 2 + 1] = lsum;
-        }
-      }
-    }
-    __syncthreads();  // LDS is reused by the next piece
+    merge_piece<T>(a, sh, w, g, c, o, m_ref, l_run, jbeg == 0 && jend == nb, first ? 0 : 1, b, h);
     pos += jend - jbeg;
     first = false;
   }
@@ -367,14 +233,7 @@ __global__ __launch_bounds__(64) void decode_combine_mfma16(DecodeArgs a) {
     for (int d = lane; d < kD; d += 64) out[d] = T(0.f);
     return;
   }
-  int C = a.split_blocks;
-  if (C <= 0) {  // the split kernel's derived chunk size
-    int tot = 0;
-    for (int base = 0; base < a.batch; base += 64)
-      tot += base + lane < a.batch ? seq_blocks(a, base + lane) * H : 0;
-    tot = wave_sum_int(tot);
-    C = max(1, (tot + a.max_splits - 1) / a.max_splits);
-  }
+  const int C = chunk_size(a, lane, a.max_splits);  // the split kernel's chunk size
   const int S = seq_start(a, b, lane) + h * nb, E = S + nb;
   const int c0 = S / C, c1 = (E - 1) / C;
   if (c0 == c1) return;  // finished inside one chunk
@@ -434,6 +293,19 @@ hipError_t launch_decode_split_mfma16(const DecodeArgs& a, hipStream_t s) {
   else
     hipLaunchKernelGGL(decode_split_mfma16<_Float16>, grid, dim3(kWaves * 64), 0, s, a);
   return hipGetLastError();
+}
+
+int occupancy_mfma16(int32_t kv_dtype) {
+  static int cache[2] = {0, 0};
+  const int i = kv_dtype == kBF16 ? 0 : 1;
+  if (cache[i] == 0) {
+    int n = 0;
+    const hipError_t e =
+        i == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<__bf16>, kWaves * 64, 0)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<_Float16>, kWaves * 64, 0);
+    cache[i] = (e == hipSuccess && n > 0) ? n : 2;
+  }
+  return cache[i];
 }
 
 hipError_t launch_decode_combine_mfma16(const DecodeArgs& a, hipStream_t s) {

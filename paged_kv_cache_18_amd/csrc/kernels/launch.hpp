@@ -13,6 +13,7 @@ namespace pa {
 struct PoolDev {
   uint8_t* base;
   int32_t n_kv_heads, head_dim, kv_dtype, group_size, num_blocks, num_sink_blocks;
+  int32_t sink_per_seq;  // logical blocks 0..sink_per_seq-1 live in the sink arena
   size_t off[kNumArr];
   size_t slab[kNumArr];
 };
@@ -22,7 +23,7 @@ hipError_t launch_append(const PoolDev& p, const void* k, const void* v, int32_t
 
 hipError_t launch_block_copy(const PoolDev& p, int32_t src, int32_t dst, hipStream_t s);
 
-enum DecodeKernel : int32_t { kKernGeneric = 0, kKernMfma16 = 1 };
+enum DecodeKernel : int32_t { kKernGeneric = 0, kKernMfma16 = 1, kKernQuant = 2 };
 
 struct DecodeArgs {
   PoolDev pool;
@@ -40,6 +41,9 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
+// Resident workgroups per compute unit of the split kernel `kernel` for a pool
+// of kv_dtype (from the runtime's occupancy calculator; cached).
+int decode_split_occupancy(int32_t kernel, int32_t kv_dtype);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace pa

@@ -72,6 +72,7 @@ pa::PoolDev dev_view(const pa_pool* p) {
   v.group_size = d.kv_dtype == pa::kInt4 ? d.group_size : d.head_dim;
   v.num_blocks = d.num_blocks;
   v.num_sink_blocks = d.num_sink_blocks;
+  v.sink_per_seq = d.sink_blocks_per_seq;
   for (int i = 0; i < pa::kNumArr; ++i) {
     v.off[i] = p->layout.offset[i];
     v.slab[i] = p->layout.slab[i];
@@ -137,14 +138,21 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
                int32_t q_dtype) {
   const pa::Desc& d = p->core.desc();
   Plan pl{};
+  const int32_t G = n_q_heads / d.n_kv_heads;
   const bool mfma_ok = (d.kv_dtype == pa::kBF16 || d.kv_dtype == pa::kF16) &&
-                       q_dtype == d.kv_dtype && d.head_dim == 128 &&
-                       n_q_heads / d.n_kv_heads <= 16 && d.num_sink_blocks == 0;
+                       q_dtype == d.kv_dtype && d.head_dim == 128 && G <= 16 &&
+                       d.num_sink_blocks == 0;
+  const bool quant_ok = ((d.kv_dtype == pa::kInt4 && d.group_size == d.head_dim) ||
+                         d.kv_dtype == pa::kFp8) &&
+                        q_dtype == pa::kF16 && d.head_dim == 128 && G <= 16;
   const char* force = std::getenv("PA_DECODE_KERNEL");  // "generic" forces the VALU kernel
-  pl.kernel = (mfma_ok && !(force && std::strcmp(force, "generic") == 0)) ? pa::kKernMfma16
-                                                                          : pa::kKernGeneric;
+  const bool generic = force && std::strcmp(force, "generic") == 0;
+  pl.kernel = generic ? pa::kKernGeneric
+              : mfma_ok ? pa::kKernMfma16
+              : quant_ok ? pa::kKernQuant
+                         : pa::kKernGeneric;
   const int64_t nb = (int64_t(max_seq_len) + 15) / 16;
-  if (pl.kernel == pa::kKernMfma16) {
+  if (pl.kernel != pa::kKernGeneric) {
     // Fixed chunks of the flattened list; two partial slots per workgroup.
     const int64_t w = flat_upper(batch, d.n_kv_heads, max_seq_len);
     if (w >= (int64_t(1) << 31) - 4096) fail(pa::kInvalidArg, "batch * n_kv_heads * blocks too large");
@@ -153,10 +161,12 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
       pl.split_blocks = c;
       pl.max_splits = int32_t((w + c - 1) / c);
     } else {
-      // persistent grid: one 4-wave workgroup per resident slot; the chunk
-      // size is derived on the device from the actual lengths
+      // persistent grid: one 4-wave workgroup per resident slot (from the
+      // occupancy calculator); the chunk size is derived on the device from
+      // the actual lengths
       pl.split_blocks = 0;
-      const int per_cu = std::max(1, env_int("PA_WG_PER_CU", 3));
+      int per_cu = env_int("PA_WG_PER_CU", 0);  // tuning knob; default: resident slots
+      if (per_cu <= 0) per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype);
       pl.max_splits = int32_t(std::max<int64_t>(1, std::min<int64_t>(w, int64_t(cu_count()) * per_cu)));
     }
     const size_t g = size_t(n_q_heads / d.n_kv_heads);

@@ -234,3 +234,30 @@ def test_full_long_context_sampled():
     err = assert_close(out, expected(wl, pairs=pairs), "bf16", "long context full")
     assert np.all(np.isfinite(out))
     log(f"[gpu] long-context full sampled max err {err:.3g}")
+
+
+@pytest.mark.parametrize("kvdt", ["int4", "fp8"])
+@pytest.mark.parametrize("split", ["1", "3", "0"])
+def test_quantized_split_k_and_kernels_agree(kvdt, split):
+    """The matrix-core quantized kernel (many small pieces when the chunk is
+    forced small) and the generic kernel both match the oracle."""
+    wl = W.from_lengths([700, 16, 17, 1, 260], 32, 8, 128, kvdt, seed=61,
+                        group=128 if kvdt == "int4" else 0, sink=True, outliers=True)
+    env = {"PA_SPLIT_BLOCKS": split} if split != "0" else {}
+    _, out_q, _, _ = run(wl, env=env)
+    ref = expected(wl)
+    assert_close(out_q, ref, "f16", f"{kvdt} quant kernel split {split}")
+    _, out_g, _, _ = run(wl, env=dict(env, PA_DECODE_KERNEL="generic"))
+    assert_close(out_g, ref, "f16", f"{kvdt} generic kernel split {split}")
+
+
+@pytest.mark.parametrize("kvdt", ["int4", "fp8"])
+def test_full_mixed_precision(kvdt):
+    """Full mixed-precision workload (65,536 + 64 appended tokens, FP16 sink,
+    1 % outlier channels): codes bit-exact for all tokens, every output head
+    within tolerance."""
+    wl = W.mixed_precision(kv=kvdt)
+    kv, out, t, l = run(wl)
+    check_stored(kv, wl, t, l)
+    err = assert_close(out, expected(wl), "f16", f"mixed {kvdt} full")
+    log(f"[gpu] mixed {kvdt} full max err {err:.3g}")
