@@ -115,6 +115,9 @@ def main():
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--cold", action="store_true",
                     help="also time the split kernel with a 512 MiB cache flush between steps")
+    ap.add_argument("--identity-tables", action="store_true",
+                    help="physical blocks in logical order (free order 0..N-1): the contiguous "
+                         "comparator for the paging overhead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -131,7 +134,8 @@ def main():
     torch.cuda.set_device(0)
     wl = W.by_name(args.config)
     print(f"[bench] {args.config}: prefill ...", file=sys.stderr, flush=True)
-    kv = PagedKV(wl, dev)
+    order = np.arange(wl.num_blocks) if args.identity_tables else None
+    kv = PagedKV(wl, dev, body_free_order=order)
     kv.replay()
     tdev, ldev, t, l = kv.device_tables()
     lens = [int(x) for x in l]
@@ -139,7 +143,7 @@ def main():
     q = torch.from_numpy(wl.q()).to(torch_dtype(wl.q_dtype)).to(dev)
     out = torch.empty_like(q)
     ws_bytes = B.pa_decode_workspace_bytes(kv.pool, wl.batch, wl.n_q_heads, max_len)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     # the step's append: every sequence's newest token, rewritten in its slot
     k_new, v_new = [], []
@@ -257,7 +261,8 @@ def main():
         "vs_baseline": None,
         "dtype": {"int4": "int4+f16", "fp8": "fp8e4m3+f16"}.get(wl.kv_dtype, wl.kv_dtype),
         "data": "synthetic (seeded N(0,1))",
-        "config": {"workload": WORKLOADS[args.config], "batch": wl.batch,
+        "config": {"workload": WORKLOADS[args.config]
+                   + (", identity block order" if args.identity_tables else ""), "batch": wl.batch,
                    "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
                    "head_dim": wl.head_dim, "block_size": 16, "kv_dtype": wl.kv_dtype,
                    "total_tokens": int(sum(lens)), "max_seq_len": max_len,

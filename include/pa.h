@@ -228,22 +228,34 @@ pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t 
  *  scale: softmax scale (1/sqrt(head_dim) in the usual case).
  *  out: device [batch][n_q_heads][head_dim] of q_dtype; rows of empty
  *       sequences are zero.
- *  workspace: device, >= pa_decode_workspace_bytes bytes, any contents.
+ *  workspace: device, >= pa_decode_workspace_bytes bytes (0 when no split
+ *       is needed), 256-byte aligned; the caller owns it and keeps it for the
+ *       library between calls.  Its first 512 KiB hold arrival counters of
+ *       the matrix-core kernels, which must be zero when a call starts and
+ *       which every call leaves at zero; the rest holds split partials.
+ *       Zero-fill it once when allocating it: it then stays valid for any
+ *       later shapes.  A workspace with nonzero counters gives wrong rows
+ *       (never an out-of-bounds access).  Calls that share a workspace must
+ *       be ordered (the same stream, or synchronized).
  * Equivalent to pa_decode_split followed by pa_decode_combine. */
 pa_status pa_decode_attention(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
                               const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
                               int32_t q_dtype, int32_t max_blocks_per_seq, int32_t max_seq_len,
                               float scale, void* out, void* workspace, size_t workspace_bytes,
                               void* stream);
-/* Phase 1: per (sequence, kv head, split of the logical blocks), partial
- * softmax statistics and weighted sums into the workspace; sequences with a
- * single split are written to `out` directly. */
+/* Phase 1: split-K attention.  The matrix-core kernels (bf16/fp16 pools, and
+ * INT4 with group = head_dim or FP8 pools, head_dim 128, Hq/Hkv <= 16) give
+ * every workgroup an equal chunk of all sequences' blocks; a (sequence, kv
+ * head) that spans several chunks is merged by the workgroup completing it,
+ * so this phase alone writes every output row.  Other shapes use per-sequence
+ * splits whose partials pa_decode_combine merges. */
 pa_status pa_decode_split(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
                           const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
                           int32_t q_dtype, int32_t max_blocks_per_seq, int32_t max_seq_len,
                           float scale, void* out, void* workspace, size_t workspace_bytes,
                           void* stream);
-/* Phase 2: log-sum-exp merge of the splits of multi-split sequences into out. */
+/* Phase 2: log-sum-exp merge of the per-sequence splits (generic kernel);
+ * nothing to do after the matrix-core kernels. */
 pa_status pa_decode_combine(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
                             const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
                             int32_t q_dtype, int32_t max_blocks_per_seq, int32_t max_seq_len,

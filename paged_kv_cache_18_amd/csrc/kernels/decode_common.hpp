@@ -7,7 +7,9 @@
 // [c*C, (c+1)*C).  A segment inside one chunk is finished in place
 // (normalized, written to out); a segment crossing chunk boundaries leaves a
 // partial (max, sum, weighted sum) in the chunk's slot 0 (its first piece) or
-// slot 1 (its last piece), merged later by the combine kernel.
+// slot 1 (its last piece), and the workgroup that writes the segment's last
+// partial (counted on an arrival counter) merges them all: one launch does
+// the whole decode.
 #pragma once
 
 #include "common.hpp"
@@ -82,9 +84,21 @@ __device__ inline int chunk_size(const DecodeArgs& a, int lane, int grid) {
 struct Shared {
   float m[kWaves][16];
   float l[kWaves][16];
-  float o[kWaves][16][kD + 1];
+  alignas(16) float o[kWaves][16][kD + 1];
   int b, fb, c;
+  int last;
 };
+
+// Zero the output rows of empty sequences (no piece covers them); workgroup
+// c takes sequences c, c + grid, ...
+template <typename TO>
+__device__ inline void zero_empty_rows(const DecodeArgs& a) {
+  const int Hq = a.n_q_heads;
+  TO* out = static_cast<TO*>(a.out);
+  for (int b = blockIdx.x; b < a.batch; b += gridDim.x)
+    if (seq_blocks(a, b) == 0)
+      for (int i = threadIdx.x; i < Hq * kD; i += kWaves * 64) out[size_t(b) * Hq * kD + i] = TO(0.f);
+}
 
 // Wave 0 finds the sequence holding this workgroup's first position.  Returns
 // false (for every thread) when the chunk lies past the end of the work.
@@ -127,6 +141,8 @@ __device__ inline bool locate_chunk(const DecodeArgs& a, Shared& sh, int w, int 
   return b >= 0;
 }
 
+__device__ inline int chunk_of(const Shared& sh) { return sh.c; }
+
 // The next piece [jbeg, jend) of segment (b, h) starting at position pos;
 // advances (b, fb) past finished or empty sequences.  False when done.
 __device__ inline bool next_piece(const DecodeArgs& a, int pos, int pos1, int& b, int& fb, int& h,
@@ -147,15 +163,170 @@ __device__ inline bool next_piece(const DecodeArgs& a, int pos, int pos1, int& b
   return false;
 }
 
+// Partials cross workgroups (and the XCDs' separate L2 caches) through
+// agent-scope relaxed atomic stores and loads: these write through to, and
+// read from, the level every XCD shares, so no L2 write-back or invalidate
+// (what an agent-scope fence costs, for every line of the cache) is needed.
+// The writer waits for its stores to complete before it counts its arrival;
+// the reader loads only after the arrival that completes the segment.
+__device__ inline void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Count this workgroup's arrival on the counter of chunk c0, the first chunk
+// of a segment of np pieces (a chunk starts at most one segment that runs
+// past its end, so c0 names the segment); true for the arrival that
+// completes the segment, which resets the counter to 0 for the next call.
+__device__ inline bool arrive(const DecodeArgs& a, int c0, int np) {
+  unsigned* ctr = a.counters + size_t(c0) * a.ctr_stride;
+  const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool last = old + 1 == unsigned(np);
+  if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
+// Buffer resource word 3 for plain dword-addressed buffers on gfx950, and the
+// cache-policy bit of a buffer load that reads at agent scope (sc1).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kSc1 = 16;
+
+// Merge the np partials of segment (b, h), which starts at position S of the
+// list, and write out.  Chunk c0 = S/C holds its piece in slot 1 unless the
+// segment starts the chunk, every later chunk in slot 0.  Pieces are taken in
+// runs of kRun with a running max per head:
+//   m = max m_i, l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.
+// Partial sums are read 16 bytes per lane with 8 loads in flight per lane,
+// so a segment of many pieces costs a few memory round trips.
+template <typename TO>
+__device__ inline void merge_segment(const DecodeArgs& a, Shared& sh, int w, int lane, int b,
+                                     int h, int S, int np, int C) {
+  const int Hq = a.n_q_heads, G = Hq / a.pool.n_kv_heads;
+  const int c0 = S / C;
+  const bool split_first = S != c0 * C;
+  auto row_of = [&](int i) -> unsigned {  // workspace row of head 0 of piece i
+    return unsigned((c0 + i) * 2 + ((i == 0 && split_first) ? 1 : 0)) * unsigned(G);
+  };
+  const unsigned rows = gridDim.x * 2u * unsigned(G);
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(a.ws_o, (short)0, int(rows * kD * 4), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rml =
+      __builtin_amdgcn_make_buffer_rsrc(a.ws_ml, (short)0, int(rows * 8), kRsrcWord3);
+  const float ninf = -__builtin_inff();
+  constexpr int kRun = 128;                     // pieces per run
+  float* mm = &sh.o[0][0][0];                   // [kRun * G] m, then weights
+  float* ll = mm + kRun * 16;                   // [kRun * G] l
+  float* accs = ll + kRun * 16;                 // [G * kD] running output sums
+  f32x4* red = reinterpret_cast<f32x4*>(accs + 16 * kD);  // [256] cross-group sums
+  static_assert(2 * kRun * 16 + 16 * kD + 4 * 256 <= kWaves * 16 * (kD + 1), "LDS reuse");
+  const int tid = threadIdx.x;
+  if (tid < G) {
+    sh.m[0][tid] = ninf;
+    sh.l[0][tid] = 0.f;
+  }
+  for (int idx = tid; idx < G * kD; idx += kWaves * 64) accs[idx] = 0.f;
+  const int F = G * (kD / 4);                   // float4 columns of a piece
+  const int P = F >= 256 ? 1 : 256 / F;         // piece groups summed in parallel
+  const int Fc = F >= 256 ? 256 : F;
+  for (int q0 = 0; q0 < np; q0 += kRun) {
+    const int qn = min(kRun, np - q0);
+    for (int t = tid; t < qn * G; t += kWaves * 64) {
+      const int i = t / G, hc = t % G;
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rml, (row_of(q0 + i) + hc) * 8u, 0, kSc1);
+      mm[t] = __uint_as_float(v[0]);
+      ll[t] = __uint_as_float(v[1]);
+    }
+    __syncthreads();
+    for (int hc = w; hc < G; hc += kWaves) {
+      float M = ninf;
+      for (int i = lane; i < qn; i += 64) M = fmaxf(M, mm[i * G + hc]);
+      M = wave_max(M);
+      const float m_old = sh.m[0][hc];
+      const float m_new = fmaxf(m_old, M);
+      float lsum = 0.f;
+      for (int i = lane; i < qn; i += 64) {
+        const float m = mm[i * G + hc];
+        const float wt = m != ninf ? exp2f(m - m_new) : 0.f;
+        mm[i * G + hc] = wt;
+        lsum += ll[i * G + hc] * wt;
+      }
+      lsum = wave_sum(lsum);
+      if (lane == 0) {
+        const float sc = m_old != ninf ? exp2f(m_old - m_new) : 0.f;
+        sh.l[1][hc] = sc;
+        sh.l[0][hc] = sh.l[0][hc] * sc + lsum;
+        sh.m[0][hc] = m_new;
+      }
+    }
+    __syncthreads();
+    const int pg = tid / Fc, c = tid % Fc;
+    if (pg < P) {
+      for (int col = c; col < F; col += Fc) {
+        const int hc = col / (kD / 4);
+        const unsigned cb = unsigned(col % (kD / 4)) * 16u + unsigned(hc) * kD * 4u;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        int i = pg;
+        for (; i + 7 * P < qn; i += 8 * P) {
+          u32x4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(ro, row_of(q0 + i + u * P) * kD * 4u + cb, 0, kSc1);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float wt = mm[(i + u * P) * G + hc];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(v[u][e]) * wt;
+          }
+        }
+        for (; i < qn; i += P) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ro, row_of(q0 + i) * kD * 4u + cb, 0, kSc1);
+          const float wt = mm[i * G + hc];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(v[e]) * wt;
+        }
+        if (P == 1) {
+          const float sc = sh.l[1][hc];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) accs[col * 4 + e] = accs[col * 4 + e] * sc + acc[e];
+        } else {
+          red[tid] = acc;
+        }
+      }
+    }
+    if (P > 1) {
+      __syncthreads();
+      if (tid < F) {
+        const float sc = sh.l[1][tid / (kD / 4)];
+        f32x4 s = red[tid];
+        for (int g2 = 1; g2 < P; ++g2) s += red[g2 * F + tid];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accs[tid * 4 + e] = accs[tid * 4 + e] * sc + s[e];
+      }
+    }
+    __syncthreads();
+  }
+  TO* out = static_cast<TO*>(a.out);
+  for (int idx = tid; idx < G * kD; idx += kWaves * 64) {
+    const float L = sh.l[0][idx / kD];
+    out[(size_t(b) * Hq + h * G) * kD + idx] = TO(L > 0.f ? accs[idx] / L : 0.f);
+  }
+}
+
 // Merge the 4 waves' (max, sum, acc) of one piece through LDS and write the
 // piece: normalized to `out` (type TO) when it is a whole segment, else as a
-// partial in the workgroup's slot.  l_run must already be summed over the
-// lane groups.  Ends with a barrier (LDS is reused by the next piece).
+// partial in the workgroup's slot, counted on the segment's arrival counter;
+// the completing arrival merges the segment.  l_run must already be summed
+// over the lane groups.  S = the segment's start position, nb its blocks,
+// C the chunk size.  Ends with a barrier (LDS is reused by the next piece).
 template <typename TO>
 __device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g, int c,
                                    const f32x4 (&o)[kNT], float m_ref, float l_run, bool complete,
-                                   int slot, int b, int h) {
+                                   int slot, int b, int h, int S, int nb, int C) {
   const int Hq = a.n_q_heads, G = Hq / a.pool.n_kv_heads;
+  const int lane = threadIdx.x & 63;
   if (g == 0) {
     sh.m[w][c] = m_ref;
     sh.l[w][c] = l_run;
@@ -183,11 +354,21 @@ __device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g
       out[(size_t(b) * Hq + h * G + hc) * kD + d] = TO(lsum > 0.f ? osum / lsum : 0.f);
     } else {
       const size_t row = (size_t(blockIdx.x) * 2 + slot) * G + hc;
-      a.ws_o[row * kD + d] = osum;
+      st_agent(&a.ws_o[row * kD + d], osum);
       if (d == 0) {
-        a.ws_ml[row * 2] = M;
-        a.ws_ml[row * 2 + 1] = lsum;
+        st_agent(&a.ws_ml[row * 2], M);
+        st_agent(&a.ws_ml[row * 2 + 1], lsum);
       }
+    }
+  }
+  if (!complete) {
+    const int np = (S + nb - 1) / C - S / C + 1;
+    wait_stores();  // this workgroup's partial is complete before its arrival counts
+    __syncthreads();
+    if (threadIdx.x == 0) sh.last = arrive(a, S / C, np) ? 1 : 0;
+    __syncthreads();
+    if (sh.last) {
+      merge_segment<TO>(a, sh, w, lane, b, h, S, np, C);
     }
   }
   __syncthreads();

@@ -196,7 +196,6 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_split_mfma16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_split_quant(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_decode_combine_mfma16(const DecodeArgs& a, hipStream_t s);
 
 int occupancy_mfma16(int32_t kv_dtype);
 int occupancy_quant(int32_t kv_dtype);
@@ -218,7 +217,8 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
-  if (a.kernel == kKernMfma16 || a.kernel == kKernQuant) return launch_decode_combine_mfma16(a, s);
+  // the matrix-core kernels merge split segments themselves
+  if (a.kernel == kKernMfma16 || a.kernel == kKernQuant) return hipSuccess;
   if (a.max_splits <= 1) return hipSuccess;
   dim3 grid(unsigned(a.n_q_heads), unsigned(a.batch));
   hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(64), 0, s, a);

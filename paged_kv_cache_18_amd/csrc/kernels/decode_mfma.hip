@@ -18,7 +18,8 @@
 // is finished there (normalized and written to out).  A segment crossing chunk
 // boundaries leaves one partial (max, sum, weighted sum) per chunk it touches;
 // a chunk holds at most two such pieces (its first and its last), so the
-// workspace is two slots per workgroup.  The combine kernel merges them.
+// workspace is two slots per workgroup; the workgroup that completes a
+// segment merges its partials.
 //
 // Inside a workgroup (4 wavefronts) a piece's blocks go round-robin to the
 // waves.  All G = Hq/Hkv query heads of the KV head are packed into one
@@ -42,7 +43,8 @@
 //    rescale is a per-lane scalar.
 // The loads of a wave's next block are issued before its current block is
 // consumed (two register buffers).  After each piece the 4 waves merge
-// (max, sum, acc) through LDS.
+// (max, sum, acc) through LDS; segments split across chunks are merged by the
+// workgroup that completes them (decode_common.hpp).
 #include "decode_common.hpp"
 
 namespace pa {
@@ -52,7 +54,7 @@ namespace {
 using namespace dec;
 
 template <typename T>
-__global__ __launch_bounds__(kWaves * 64) void decode_split_mfma16(DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_mfma16(DecodeArgs a) {
   typedef typename Mfma<T>::v8 v8;
   typedef typename Mfma<T>::v4 v4;
   __shared__ Shared sh;
@@ -62,6 +64,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_mfma16(DecodeArgs a)
   const int g = lane >> 4, c = lane & 15;
   const PoolDev& p = a.pool;
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H;
+  zero_empty_rows<T>(a);
   int b, fb, pos0, pos1;
   if (!locate_chunk(a, sh, w, lane, b, fb, pos0, pos1)) return;  // past the work
 
@@ -209,79 +212,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_mfma16(DecodeArgs a)
     // ---- merge the 4 waves of this piece, write it -----------------------------
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
-    merge_piece<T>(a, sh, w, g, c, o, m_ref, l_run, jbeg == 0 && jend == nb, first ? 0 : 1, b, h);
+    merge_piece<T>(a, sh, w, g, c, o, m_ref, l_run, jbeg == 0 && jend == nb, first ? 0 : 1, b, h,
+                   fb + h * nb, nb, pos1 - pos0);
     pos += jend - jbeg;
     first = false;
   }
-}
-
-// Merge the pieces of one (sequence b, query head hq) left by the split
-// kernel: chunks c0..c1 touch the segment; chunk c0 holds it in slot 1 unless
-// the segment starts its chunk, every later chunk in slot 0.
-//   m = max m_i, l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.
-// Rows of empty sequences are zeroed here.
-constexpr int kCombineChunk = 256;
-
-template <typename T>
-__global__ __launch_bounds__(64) void decode_combine_mfma16(DecodeArgs a) {
-  __shared__ float wsh[kCombineChunk];
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int H = a.pool.n_kv_heads, Hq = a.n_q_heads, G = Hq / H, h = hq / G, hc = hq % G;
-  T* out = static_cast<T*>(a.out) + (size_t(b) * Hq + hq) * kD;
-  const int nb = seq_blocks(a, b);
-  if (nb == 0) {
-    for (int d = lane; d < kD; d += 64) out[d] = T(0.f);
-    return;
-  }
-  const int C = chunk_size(a, lane, a.max_splits);  // the split kernel's chunk size
-  const int S = seq_start(a, b, lane) + h * nb, E = S + nb;
-  const int c0 = S / C, c1 = (E - 1) / C;
-  if (c0 == c1) return;  // finished inside one chunk
-  const int np = c1 - c0 + 1;
-  auto row_of = [&](int i) {
-    const int slot = (i == 0 && S != c0 * C) ? 1 : 0;
-    return (size_t(c0 + i) * 2 + slot) * G + hc;
-  };
-  const float ninf = -__builtin_inff();
-  float M = ninf;
-  for (int i = lane; i < np; i += 64) M = fmaxf(M, a.ws_ml[row_of(i) * 2]);
-  M = wave_max(M);
-  float lsum = 0.f;
-  for (int i = lane; i < np; i += 64) {
-    const size_t r = row_of(i);
-    const float m = a.ws_ml[r * 2];
-    if (m != ninf) lsum += a.ws_ml[r * 2 + 1] * exp2f(m - M);
-  }
-  lsum = wave_sum(lsum);
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  float acc0 = 0.f, acc1 = 0.f;
-  for (int q0 = 0; q0 < np; q0 += kCombineChunk) {
-    const int qn = min(kCombineChunk, np - q0);
-    __syncthreads();
-    for (int i = lane; i < qn; i += 64) {
-      const float m = a.ws_ml[row_of(q0 + i) * 2];
-      wsh[i] = m != ninf ? exp2f(m - M) * inv : 0.f;
-    }
-    __syncthreads();
-    int i = 0;
-    for (; i + 4 <= qn; i += 4) {  // independent loads in flight
-      const float* s0 = a.ws_o + row_of(q0 + i + 0) * kD;
-      const float* s1 = a.ws_o + row_of(q0 + i + 1) * kD;
-      const float* s2 = a.ws_o + row_of(q0 + i + 2) * kD;
-      const float* s3 = a.ws_o + row_of(q0 + i + 3) * kD;
-      const float x0 = s0[lane], x1 = s1[lane], x2 = s2[lane], x3 = s3[lane];
-      const float y0 = s0[lane + 64], y1 = s1[lane + 64], y2 = s2[lane + 64], y3 = s3[lane + 64];
-      acc0 += (x0 * wsh[i] + x1 * wsh[i + 1]) + (x2 * wsh[i + 2] + x3 * wsh[i + 3]);
-      acc1 += (y0 * wsh[i] + y1 * wsh[i + 1]) + (y2 * wsh[i + 2] + y3 * wsh[i + 3]);
-    }
-    for (; i < qn; ++i) {
-      const float* src = a.ws_o + row_of(q0 + i) * kD;
-      acc0 += src[lane] * wsh[i];
-      acc1 += src[lane + 64] * wsh[i];
-    }
-  }
-  out[lane] = T(acc0);
-  out[lane + 64] = T(acc1);
 }
 
 }  // namespace
@@ -306,15 +241,6 @@ int occupancy_mfma16(int32_t kv_dtype) {
     cache[i] = (e == hipSuccess && n > 0) ? n : 2;
   }
   return cache[i];
-}
-
-hipError_t launch_decode_combine_mfma16(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(unsigned(a.n_q_heads), unsigned(a.batch));
-  if (a.pool.kv_dtype == kBF16)
-    hipLaunchKernelGGL(decode_combine_mfma16<__bf16>, grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_combine_mfma16<_Float16>, grid, dim3(64), 0, s, a);
-  return hipGetLastError();
 }
 
 }  // namespace pa

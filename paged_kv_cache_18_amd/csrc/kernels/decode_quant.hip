@@ -82,7 +82,7 @@ struct Quant<kFp8> {
 
 // NB = register buffers per wave (NB-1 blocks prefetched ahead).
 template <int KIND, int NB>
-__global__ __launch_bounds__(kWaves * 64) void decode_split_quant(DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 3 : 2))) void decode_split_quant(DecodeArgs a) {
   typedef typename Quant<KIND>::Buf Buf;
   typedef Mfma<_Float16> MF;
   __shared__ Shared sh;
@@ -93,6 +93,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_quant(DecodeArgs a) 
   const PoolDev& p = a.pool;
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H, N = p.num_blocks;
   const int SP = p.sink_per_seq;
+  zero_empty_rows<_Float16>(a);
   int b, fb, pos0, pos1;
   if (!locate_chunk(a, sh, w, lane, b, fb, pos0, pos1)) return;  // past the work
 
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_quant(DecodeArgs a) 
       for (int T_ = 0; T_ < kNT; ++T_) o[T_] -= corr;
     }
     merge_piece<_Float16>(a, sh, w, g, c, o, m_ref, l_run, jbeg == 0 && jend == nb,
-                          first ? 0 : 1, b, h);
+                          first ? 0 : 1, b, h, fb + h * nb, nb, pos1 - pos0);
     pos += jend - jbeg;
     first = false;
   }

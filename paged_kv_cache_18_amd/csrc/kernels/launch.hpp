@@ -35,6 +35,10 @@ struct DecodeArgs {
   void* out;
   float* ws_o;           // [batch][n_q_heads][max_splits][head_dim] partial sums
   float* ws_ml;          // [batch][n_q_heads][max_splits][2] (max, sum), log2 domain
+  // matrix-core kernels: one arrival counter per chunk (the first chunk of
+  // a segment that spans several), ctr_stride words apart; zero between calls
+  unsigned* counters;
+  int ctr_stride;
   int32_t split_blocks;  // logical blocks per split
   int32_t max_splits;
   int32_t kernel;        // DecodeKernel

@@ -125,8 +125,18 @@ int cu_count() {
 
 struct Plan {
   int32_t split_blocks, max_splits, kernel;
-  size_t ws_bytes, ws_ml_offset;  // bytes; ws_ml_offset = float index of the (max, sum) area
+  size_t ws_bytes;      // bytes the call needs
+  size_t ws_o_offset;   // byte offset of the partial sums
+  size_t ws_ml_offset;  // float index (from ws_o) of the (max, sum) pairs
 };
+
+// The workspace starts with kCtrCap arrival counters of the matrix-core
+// kernels, kCtrStride 32-bit words apart (one per 128-byte line), at the same
+// place for every call and shape: a zero-filled workspace stays valid because
+// every call leaves them at zero and nothing else is written there.
+constexpr int32_t kCtrCap = 4096;
+constexpr int32_t kCtrStride = 32;
+constexpr size_t kCtrBytes = size_t(kCtrCap) * kCtrStride * sizeof(unsigned);
 
 // Upper bound of the flattened work list (blocks of all (sequence, kv head)
 // segments) from the shapes alone.
@@ -156,10 +166,11 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
     // Fixed chunks of the flattened list; two partial slots per workgroup.
     const int64_t w = flat_upper(batch, d.n_kv_heads, max_seq_len);
     if (w >= (int64_t(1) << 31) - 4096) fail(pa::kInvalidArg, "batch * n_kv_heads * blocks too large");
-    const int32_t c = env_int("PA_SPLIT_BLOCKS", 0);  // fixed chunk size (tuning/tests)
+    int32_t c = env_int("PA_SPLIT_BLOCKS", 0);  // fixed chunk size (tuning/tests)
     if (c > 0) {
+      c = int32_t(std::max<int64_t>(c, (w + kCtrCap - 1) / kCtrCap));  // <= kCtrCap chunks
       pl.split_blocks = c;
-      pl.max_splits = int32_t((w + c - 1) / c);
+      pl.max_splits = int32_t(std::max<int64_t>(1, (w + c - 1) / c));
     } else {
       // persistent grid: one 4-wave workgroup per resident slot (from the
       // occupancy calculator); the chunk size is derived on the device from
@@ -167,19 +178,22 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
       pl.split_blocks = 0;
       int per_cu = env_int("PA_WG_PER_CU", 0);  // tuning knob; default: resident slots
       if (per_cu <= 0) per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype);
-      pl.max_splits = int32_t(std::max<int64_t>(1, std::min<int64_t>(w, int64_t(cu_count()) * per_cu)));
+      pl.max_splits = int32_t(std::max<int64_t>(
+          1, std::min<int64_t>({w, int64_t(cu_count()) * per_cu, int64_t(kCtrCap)})));
     }
     const size_t g = size_t(n_q_heads / d.n_kv_heads);
     const size_t rows = size_t(pl.max_splits) * 2 * g;
+    pl.ws_o_offset = kCtrBytes;
     pl.ws_ml_offset = rows * size_t(d.head_dim);
-    pl.ws_bytes = rows * (size_t(d.head_dim) + 2) * sizeof(float);
+    pl.ws_bytes = kCtrBytes + rows * (size_t(d.head_dim) + 2) * sizeof(float);
     return pl;
   }
   pl.split_blocks = plan_split_blocks(batch, d.n_kv_heads, max_seq_len);
   pl.max_splits = int32_t(std::max<int64_t>(1, (nb + pl.split_blocks - 1) / pl.split_blocks));
   const size_t rows = size_t(batch) * size_t(n_q_heads) * size_t(pl.max_splits);
+  pl.ws_o_offset = kCtrBytes;  // partials never overwrite the counters
   pl.ws_ml_offset = rows * size_t(d.head_dim);
-  pl.ws_bytes = pl.max_splits > 1 ? rows * (size_t(d.head_dim) + 2) * sizeof(float) : 0;
+  pl.ws_bytes = pl.max_splits > 1 ? kCtrBytes + rows * (size_t(d.head_dim) + 2) * sizeof(float) : 0;
   return pl;
 }
 
@@ -221,7 +235,7 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
       need(ws, "workspace");
       if (ws_bytes < pl.ws_bytes)
         fail(pa::kInvalidArg, "workspace too small: need " + std::to_string(pl.ws_bytes) + " bytes");
-      if (reinterpret_cast<uintptr_t>(ws) % 16) fail(pa::kInvalidArg, "workspace must be 16-byte aligned");
+      if (reinterpret_cast<uintptr_t>(ws) % 256) fail(pa::kInvalidArg, "workspace must be 256-byte aligned");
     }
     pa::DecodeArgs a{};
     a.pool = dev_view(pool);
@@ -235,8 +249,12 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     a.max_seq_len = max_seq_len;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out = out;
-    a.ws_o = static_cast<float*>(ws);
-    a.ws_ml = pl.ws_bytes ? a.ws_o + pl.ws_ml_offset : nullptr;
+    if (pl.ws_bytes) {
+      a.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.ws_o_offset);
+      a.ws_ml = a.ws_o + pl.ws_ml_offset;
+      a.counters = static_cast<unsigned*>(ws);
+      a.ctr_stride = kCtrStride;
+    }
     a.split_blocks = pl.split_blocks;
     a.max_splits = pl.max_splits;
     a.kernel = pl.kernel;

@@ -134,7 +134,7 @@ class PagedKV:
             out = torch.empty_like(q)
         need = B.pa_decode_workspace_bytes(self.pool, b, hq, max_seq_len)
         if workspace is None:
-            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
+            workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=self.device)
         fn = {"both": B.pa_decode_attention, "split": B.pa_decode_split,
               "combine": B.pa_decode_combine}[phase]
         fn(q, self.pool, tables_dev, lens_dev, b, hq, self.wl.q_dtype, tables_dev.shape[1],

@@ -57,6 +57,7 @@ def run(wl, order=None, env=None, canary=True):
         out_full = torch.full((bq + 1, hq, d), 7.0, dtype=q.dtype, device=DEV)
         need = B.pa_decode_workspace_bytes(kv.pool, bq, hq, max_len)
         ws = torch.full((need + 4096,), 0xAB, dtype=torch.uint8, device=DEV)
+        ws[:need] = 0  # the contract: zero-filled once; bytes past `need` are a canary
         kv.decode(q, tdev, ldev, max_len, out=out_full[:bq], workspace=ws)
         torch.cuda.synchronize()
         if canary:
@@ -261,3 +262,34 @@ def test_full_mixed_precision(kvdt):
     check_stored(kv, wl, t, l)
     err = assert_close(out, expected(wl), "f16", f"mixed {kvdt} full")
     log(f"[gpu] mixed {kvdt} full max err {err:.3g}")
+
+
+def test_workspace_reuse_across_calls_and_shapes():
+    """One zero-filled workspace serves repeated calls and changing shapes: the
+    arrival counters reset themselves, results stay bit-identical and correct."""
+    wl_a = W.from_lengths([900, 33, 2000, 1], 32, 8, 128, "bf16", seed=71)
+    wl_b = W.from_lengths([5000, 17], 64, 8, 128, "bf16", seed=72)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    runs = {}
+    for wl in (wl_a, wl_b):
+        kv = PagedKV(wl, DEV)
+        kv.replay()
+        tdev, ldev, t, l = kv.device_tables()
+        q = torch.from_numpy(wl.q()).to(TORCH_DT[wl.q_dtype]).to(DEV)
+        runs[wl.name + str(wl.seed)] = (wl, kv, tdev, ldev, q, int(l.max()))
+    outs = {}
+    for rep in range(3):
+        for key, (wl, kv, tdev, ldev, q, ml) in runs.items():
+            for split in ("0", "2"):
+                os.environ["PA_SPLIT_BLOCKS"] = split
+                try:
+                    o = kv.decode(q, tdev, ldev, ml, workspace=ws)
+                finally:
+                    os.environ.pop("PA_SPLIT_BLOCKS", None)
+                torch.cuda.synchronize()
+                o = o.double().cpu().numpy()
+                if (key, split) in outs:
+                    assert np.array_equal(o, outs[(key, split)]), f"{key} split {split} rep {rep}"
+                else:
+                    assert_close(o, expected(wl), "bf16", f"{key} split {split}")
+                    outs[(key, split)] = o
