@@ -230,7 +230,7 @@ pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t 
  *       sequences are zero.
  *  workspace: device, >= pa_decode_workspace_bytes bytes (0 when no split
  *       is needed), 256-byte aligned; the caller owns it and keeps it for the
- *       library between calls.  Its first 512 KiB hold arrival counters of
+ *       library between calls.  Its first 1 MiB holds the counters of
  *       the matrix-core kernels, which must be zero when a call starts and
  *       which every call leaves at zero; the rest holds split partials.
  *       Zero-fill it once when allocating it: it then stays valid for any

@@ -1,15 +1,20 @@
 // Shared pieces of the matrix-core decode split kernels (decode_mfma.hip for
-// 16-bit pools, decode_quant.hip for INT4/FP8 pools): the flattened,
-// evenly chunked work list, the per-piece iteration, and the 4-wave merge.
+// 16-bit pools, decode_quant.hip for INT4/FP8 pools): the flattened work
+// list and its units, the per-piece iteration, and the 4-wave merge.
 //
 // Work list: the blocks of every (sequence b, KV head h) segment laid end to
-// end (b major, then h, then logical block j).  Workgroup c owns positions
-// [c*C, (c+1)*C).  A segment inside one chunk is finished in place
-// (normalized, written to out); a segment crossing chunk boundaries leaves a
-// partial (max, sum, weighted sum) in the chunk's slot 0 (its first piece) or
-// slot 1 (its last piece), and the workgroup that writes the segment's last
-// partial (counted on an arrival counter) merges them all: one launch does
-// the whole decode.
+// end (b major, then h, then logical block j).  It is cut into regions of C
+// blocks, one per workgroup of the persistent grid.  The first Cs blocks of a
+// region are its owner's; the rest are cut into units of U blocks that any
+// workgroup takes, in order, from a queue once it has streamed its own prefix
+// (compute units and XCDs do not stream at the same rate, so equal shares
+// would not finish together).  The cut is fixed by the shapes alone; only who
+// streams a unit varies.  A segment inside one unit is finished in place
+// (normalized, written to out); a segment crossing units leaves a partial
+// (max, sum, weighted sum) in the unit's slot 0 (its first piece there) or
+// slot 1 (a later one), and the workgroup that writes the segment's last
+// partial (counted on an arrival counter) merges them all, in unit order: one
+// launch does the whole decode and the result does not depend on the timing.
 #pragma once
 
 #include "common.hpp"
@@ -75,40 +80,81 @@ __device__ inline int total_work(const DecodeArgs& a, int lane) {
   return wave_sum_int(tot);
 }
 
-// Chunk size: fixed (a.split_blocks > 0) or the work shared evenly by the grid.
-__device__ inline int chunk_size(const DecodeArgs& a, int lane, int grid) {
-  if (a.split_blocks > 0) return a.split_blocks;
-  return max(1, (total_work(a, lane) + grid - 1) / grid);
-}
-
 struct Shared {
   float m[kWaves][16];
   float l[kWaves][16];
   alignas(16) float o[kWaves][16][kD + 1];
-  int b, fb, c;
+  int b, fb;
+  int units[6];
+  int next;
   int last;
 };
 
-// Zero the output rows of empty sequences (no piece covers them); workgroup
-// c takes sequences c, c + grid, ...
-template <typename TO>
-__device__ inline void zero_empty_rows(const DecodeArgs& a) {
-  const int Hq = a.n_q_heads;
-  TO* out = static_cast<TO*>(a.out);
-  for (int b = blockIdx.x; b < a.batch; b += gridDim.x)
-    if (seq_blocks(a, b) == 0)
-      for (int i = threadIdx.x; i < Hq * kD; i += kWaves * 64) out[size_t(b) * Hq * kD + i] = TO(0.f);
+// The cut of the work list (see the top of this file).  Unit ids grow with
+// position: region r holds units r*(1+m) (its prefix) .. r*(1+m)+m.
+struct Units {
+  int W;   // blocks in the list
+  int R;   // regions (= the grid)
+  int C;   // blocks per region
+  int Cs;  // owner's prefix of a region, >= 1
+  int U;   // blocks per queued unit
+  int m;   // queued units per region
+  __device__ int per() const { return 1 + m; }
+  __device__ int total() const { return R * per(); }
+  __device__ int unit_of(int p) const {
+    const int r = p / C, o = p - r * C;
+    return r * per() + (o < Cs ? 0 : 1 + (o - Cs) / U);
+  }
+  __device__ int start(int u) const {
+    const int r = u / per(), k = u - r * per();
+    return r * C + (k == 0 ? 0 : Cs + (k - 1) * U);
+  }
+  __device__ int end(int u) const {
+    const int r = u / per(), k = u - r * per();
+    return min(W, r * C + (k == 0 ? Cs : min(C, Cs + k * U)));
+  }
+  // q-th unit of the queue: the first queued unit of every region, then the
+  // second, ...
+  __device__ int queued(int q) const { return (q % R) * per() + 1 + q / R; }
+};
+
+// Wave 0 sizes the cut from the lengths; every thread gets it.
+__device__ inline Units setup_units(const DecodeArgs& a, Shared& sh, int w, int lane) {
+  if (w == 0) {
+    const int W = total_work(a, lane);
+    const int R = int(gridDim.x);
+    int C, Cs, U = 1, m = 0;
+    if (a.split_blocks > 0) {
+      C = Cs = a.split_blocks;
+    } else {
+      C = max(1, (W + R - 1) / R);
+      Cs = C;
+      if (a.unit_blocks > 0 && a.static_permille < 1000) {
+        U = a.unit_blocks;
+        Cs = max(1, int(int64_t(C) * max(a.static_permille, 0) / 1000));
+        m = (C - Cs + U - 1) / U;
+      }
+    }
+    if (lane == 0) {
+      sh.units[0] = W;
+      sh.units[1] = R;
+      sh.units[2] = C;
+      sh.units[3] = Cs;
+      sh.units[4] = U;
+      sh.units[5] = m;
+    }
+  }
+  __syncthreads();
+  return Units{sh.units[0], sh.units[1], sh.units[2], sh.units[3], sh.units[4], sh.units[5]};
 }
 
-// Wave 0 finds the sequence holding this workgroup's first position.  Returns
-// false (for every thread) when the chunk lies past the end of the work.
-__device__ inline bool locate_chunk(const DecodeArgs& a, Shared& sh, int w, int lane, int& b,
-                                    int& fb, int& pos0, int& pos1) {
+// Wave 0 finds the sequence b holding position p0 and the position fb of its
+// first block; every thread gets them.
+__device__ inline void locate(const DecodeArgs& a, Shared& sh, int w, int lane, int p0, int& b,
+                              int& fb) {
   const int H = a.pool.n_kv_heads, B = a.batch;
   if (w == 0) {
-    const int C = chunk_size(a, lane, int(gridDim.x));
-    const int p0 = int(blockIdx.x) * C;
-    int run = 0, f = 0, fbi = -1;
+    int run = 0, f = 0, fbi = B;
     for (int base = 0; base < B; base += 64) {
       const int bb = base + lane;
       const int sz = bb < B ? seq_blocks(a, bb) * H : 0;
@@ -130,18 +176,57 @@ __device__ inline bool locate_chunk(const DecodeArgs& a, Shared& sh, int w, int 
     if (lane == 0) {
       sh.b = fbi;
       sh.fb = f;
-      sh.c = C;
     }
   }
   __syncthreads();
   b = sh.b;
   fb = sh.fb;
-  pos0 = int(blockIdx.x) * sh.c;
-  pos1 = pos0 + sh.c;
-  return b >= 0;
 }
 
-__device__ inline int chunk_of(const Shared& sh) { return sh.c; }
+// Arrival counters: word 0 is the unit queue, unit u's counter is word
+// (1 + u) (times the stride).
+__device__ inline unsigned* unit_counter(const DecodeArgs& a, int u) {
+  return a.counters + size_t(1 + u) * a.ctr_stride;
+}
+
+// The next unit this workgroup streams: its own prefix first (start = its
+// region's prefix id), then units from the queue; -1 when the queue is empty.
+// Every workgroup ends with exactly one refused take, so the take that sees
+// count R*m + R - 1 is the call's last and resets the queue to 0.
+__device__ inline int next_unit(const DecodeArgs& a, Shared& sh, const Units& um) {
+  if (um.m == 0) return -1;
+  if (threadIdx.x == 0) {
+    const unsigned nq = unsigned(um.R) * unsigned(um.m);
+    int u = -1;
+    while (true) {
+      const unsigned q = __hip_atomic_fetch_add(a.counters, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (q + 1 == nq + unsigned(um.R)) __hip_atomic_store(a.counters, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (q >= nq) break;
+      const int cand = um.queued(int(q));
+      if (um.start(cand) < um.end(cand)) {
+        u = cand;
+        break;
+      }
+    }
+    sh.next = u;
+  }
+  __syncthreads();
+  const int u = sh.next;
+  __syncthreads();
+  return u;
+}
+
+
+// Zero the output rows of empty sequences (no piece covers them); workgroup
+// c takes sequences c, c + grid, ...
+template <typename TO>
+__device__ inline void zero_empty_rows(const DecodeArgs& a) {
+  const int Hq = a.n_q_heads;
+  TO* out = static_cast<TO*>(a.out);
+  for (int b = blockIdx.x; b < a.batch; b += gridDim.x)
+    if (seq_blocks(a, b) == 0)
+      for (int i = threadIdx.x; i < Hq * kD; i += kWaves * 64) out[size_t(b) * Hq * kD + i] = TO(0.f);
+}
 
 // The next piece [jbeg, jend) of segment (b, h) starting at position pos;
 // advances (b, fb) past finished or empty sequences.  False when done.
@@ -163,6 +248,24 @@ __device__ inline bool next_piece(const DecodeArgs& a, int pos, int pos1, int& b
   return false;
 }
 
+// Wave issue priority from the share of its chunk a workgroup still has to
+// stream (done of C blocks): bands above 1/2, 1/4 and 1/16 remaining.  With
+// equal chunks, the workgroups a compute unit holds would otherwise progress
+// in dispatch order (older waves win issue arbitration) and the youngest
+// would finish last; this lets the ones behind catch up.
+__device__ inline void prio_from_progress(const DecodeArgs& a, int done, int C) {
+  if (!a.prio) return;
+  const int r = max(C - done, 0);
+  if (2 * r > C)
+    __builtin_amdgcn_s_setprio(3);
+  else if (4 * r > C)
+    __builtin_amdgcn_s_setprio(2);
+  else if (16 * r > C)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // Partials cross workgroups (and the XCDs' separate L2 caches) through
 // agent-scope relaxed atomic stores and loads: these write through to, and
 // read from, the level every XCD shares, so no L2 write-back or invalidate
@@ -177,12 +280,12 @@ __device__ inline float ld_agent(const float* p) {
 }
 __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Count this workgroup's arrival on the counter of chunk c0, the first chunk
-// of a segment of np pieces (a chunk starts at most one segment that runs
-// past its end, so c0 names the segment); true for the arrival that
-// completes the segment, which resets the counter to 0 for the next call.
+// Count this workgroup's arrival on the counter of unit c0, the first unit of
+// a segment of np pieces (a unit starts at most one segment that runs past its
+// end, so c0 names the segment); true for the arrival that completes the
+// segment, which resets the counter to 0 for the next call.
 __device__ inline bool arrive(const DecodeArgs& a, int c0, int np) {
-  unsigned* ctr = a.counters + size_t(c0) * a.ctr_stride;
+  unsigned* ctr = unit_counter(a, c0);
   const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool last = old + 1 == unsigned(np);
   if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -195,22 +298,22 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kSc1 = 16;
 
 // Merge the np partials of segment (b, h), which starts at position S of the
-// list, and write out.  Chunk c0 = S/C holds its piece in slot 1 unless the
-// segment starts the chunk, every later chunk in slot 0.  Pieces are taken in
+// list, and write out.  Its first unit c0 holds its piece in slot 1 unless
+// the segment starts the unit, every later unit in slot 0.  Pieces are taken in
 // runs of kRun with a running max per head:
 //   m = max m_i, l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.
 // Partial sums are read 16 bytes per lane with 8 loads in flight per lane,
 // so a segment of many pieces costs a few memory round trips.
 template <typename TO>
 __device__ inline void merge_segment(const DecodeArgs& a, Shared& sh, int w, int lane, int b,
-                                     int h, int S, int np, int C) {
+                                     int h, int S, int np, const Units& um) {
   const int Hq = a.n_q_heads, G = Hq / a.pool.n_kv_heads;
-  const int c0 = S / C;
-  const bool split_first = S != c0 * C;
+  const int c0 = um.unit_of(S);
+  const bool split_first = S != um.start(c0);
   auto row_of = [&](int i) -> unsigned {  // workspace row of head 0 of piece i
     return unsigned((c0 + i) * 2 + ((i == 0 && split_first) ? 1 : 0)) * unsigned(G);
   };
-  const unsigned rows = gridDim.x * 2u * unsigned(G);
+  const unsigned rows = unsigned(um.total()) * 2u * unsigned(G);
   const __amdgpu_buffer_rsrc_t ro =
       __builtin_amdgcn_make_buffer_rsrc(a.ws_o, (short)0, int(rows * kD * 4), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rml =
@@ -317,14 +420,15 @@ __device__ inline void merge_segment(const DecodeArgs& a, Shared& sh, int w, int
 
 // Merge the 4 waves' (max, sum, acc) of one piece through LDS and write the
 // piece: normalized to `out` (type TO) when it is a whole segment, else as a
-// partial in the workgroup's slot, counted on the segment's arrival counter;
-// the completing arrival merges the segment.  l_run must already be summed
-// over the lane groups.  S = the segment's start position, nb its blocks,
-// C the chunk size.  Ends with a barrier (LDS is reused by the next piece).
+// partial in slot `slot` of unit `unit`, counted on the segment's arrival
+// counter; the completing arrival merges the segment.  l_run must already be
+// summed over the lane groups.  S = the segment's start position, nb its
+// blocks.  Ends with a barrier (LDS is reused by the next piece).
 template <typename TO>
 __device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g, int c,
                                    const f32x4 (&o)[kNT], float m_ref, float l_run, bool complete,
-                                   int slot, int b, int h, int S, int nb, int C) {
+                                   int slot, int unit, int b, int h, int S, int nb,
+                                   const Units& um) {
   const int Hq = a.n_q_heads, G = Hq / a.pool.n_kv_heads;
   const int lane = threadIdx.x & 63;
   if (g == 0) {
@@ -353,7 +457,7 @@ __device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g
     if (complete) {
       out[(size_t(b) * Hq + h * G + hc) * kD + d] = TO(lsum > 0.f ? osum / lsum : 0.f);
     } else {
-      const size_t row = (size_t(blockIdx.x) * 2 + slot) * G + hc;
+      const size_t row = (size_t(unit) * 2 + slot) * G + hc;
       st_agent(&a.ws_o[row * kD + d], osum);
       if (d == 0) {
         st_agent(&a.ws_ml[row * 2], M);
@@ -362,13 +466,14 @@ __device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g
     }
   }
   if (!complete) {
-    const int np = (S + nb - 1) / C - S / C + 1;
+    const int c0 = um.unit_of(S);
+    const int np = um.unit_of(S + nb - 1) - c0 + 1;
     wait_stores();  // this workgroup's partial is complete before its arrival counts
     __syncthreads();
-    if (threadIdx.x == 0) sh.last = arrive(a, S / C, np) ? 1 : 0;
+    if (threadIdx.x == 0) sh.last = arrive(a, c0, np) ? 1 : 0;
     __syncthreads();
     if (sh.last) {
-      merge_segment<TO>(a, sh, w, lane, b, h, S, np, C);
+      merge_segment<TO>(a, sh, w, lane, b, h, S, np, um);
     }
   }
   __syncthreads();

@@ -65,8 +65,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   const PoolDev& p = a.pool;
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H;
   zero_empty_rows<T>(a);
-  int b, fb, pos0, pos1;
-  if (!locate_chunk(a, sh, w, lane, b, fb, pos0, pos1)) return;  // past the work
+  const Units um = setup_units(a, sh, w, lane);
+  int b = 0, fb = 0;
 
   const T* kbase = reinterpret_cast<const T*>(p.base + p.off[kArrK]);
   const T* vbase = reinterpret_cast<const T*>(p.base + p.off[kArrV]);
@@ -166,6 +166,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     }
   };
 
+  const int own_unit = int(blockIdx.x) * um.per();
+  for (int unit = own_unit; unit >= 0; unit = next_unit(a, sh, um)) {
+  const int pos0 = um.start(unit), pos1 = um.end(unit);
+  if (pos0 >= pos1) continue;  // a region past the end of the work
+  locate(a, sh, w, lane, pos0, b, fb);
+  // progress-based priority in the owner's prefix; queued units run at the
+  // base priority, behind the workgroups still streaming their own prefix
+  const int prio_span = unit == own_unit ? pos1 - pos0 : 0;
   int pos = pos0;
   bool first = true;
   int jbeg = 0, jend = 0, nb = 0;
@@ -197,6 +205,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
       fetch(ida, ka, va);
       int k = 0;
       for (; k + 1 < n; k += 2) {
+        prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
         const int idb = id_of(k + 1);
         fetch(idb, kb, vb);
         consume(valid_of(k, ida), ka, va);
@@ -212,10 +221,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     // ---- merge the 4 waves of this piece, write it -----------------------------
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
-    merge_piece<T>(a, sh, w, g, c, o, m_ref, l_run, jbeg == 0 && jend == nb, first ? 0 : 1, b, h,
-                   fb + h * nb, nb, pos1 - pos0);
+    merge_piece<T>(a, sh, w, g, c, o, m_ref, l_run, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, h,
+                   fb + h * nb, nb, um);
     pos += jend - jbeg;
     first = false;
+  }
   }
 }
 

@@ -94,8 +94,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H, N = p.num_blocks;
   const int SP = p.sink_per_seq;
   zero_empty_rows<_Float16>(a);
-  int b, fb, pos0, pos1;
-  if (!locate_chunk(a, sh, w, lane, b, fb, pos0, pos1)) return;  // past the work
+  const Units um = setup_units(a, sh, w, lane);
+  int b = 0, fb = 0;
 
   const float sl2 = a.scale_log2;
   const uint8_t* base = p.base;
@@ -273,6 +273,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     }
   };
 
+  const int own_unit = int(blockIdx.x) * um.per();
+  for (int unit = own_unit; unit >= 0; unit = next_unit(a, sh, um)) {
+  const int pos0 = um.start(unit), pos1 = um.end(unit);
+  if (pos0 >= pos1) continue;  // a region past the end of the work
+  locate(a, sh, w, lane, pos0, b, fb);
+  // progress-based priority in the owner's prefix; queued units run at the
+  // base priority, behind the workgroups still streaming their own prefix
+  const int prio_span = unit == own_unit ? pos1 - pos0 : 0;
   int pos = pos0;
   bool first = true;
   int jbeg = 0, jend = 0, nb = 0;
@@ -328,6 +336,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       }
       int k = 0;
       for (; k + NB <= n; k += NB) {
+        prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
 #pragma unroll
         for (int s = 0; s < NB; ++s) {
           const int nxt = (s + NB - 1) % NB;
@@ -351,9 +360,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       for (int T_ = 0; T_ < kNT; ++T_) o[T_] -= corr;
     }
     merge_piece<_Float16>(a, sh, w, g, c, o, m_ref, l_run, jbeg == 0 && jend == nb,
-                          first ? 0 : 1, b, h, fb + h * nb, nb, pos1 - pos0);
+                          first ? 0 : 1, unit, b, h, fb + h * nb, nb, um);
     pos += jend - jbeg;
     first = false;
+  }
   }
 }
 

@@ -35,13 +35,17 @@ struct DecodeArgs {
   void* out;
   float* ws_o;           // [batch][n_q_heads][max_splits][head_dim] partial sums
   float* ws_ml;          // [batch][n_q_heads][max_splits][2] (max, sum), log2 domain
-  // matrix-core kernels: one arrival counter per chunk (the first chunk of
-  // a segment that spans several), ctr_stride words apart; zero between calls
+  // matrix-core kernels: the unit queue, then one arrival counter per unit
+  // (the first unit of a segment that spans several), ctr_stride words
+  // apart; zero between calls
   unsigned* counters;
   int ctr_stride;
   int32_t split_blocks;  // logical blocks per split
   int32_t max_splits;
   int32_t kernel;        // DecodeKernel
+  int32_t prio;          // matrix-core kernels: 1 = progress-based wave priority
+  int32_t unit_blocks;   // matrix-core kernels: blocks per queued unit (0: none)
+  int32_t static_permille;  // share of a region its owner streams, in 1/1000
 };
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);

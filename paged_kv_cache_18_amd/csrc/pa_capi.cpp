@@ -5,6 +5,7 @@
 // work goes to the kernels behind kernels/launch.hpp on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -125,18 +126,28 @@ int cu_count() {
 
 struct Plan {
   int32_t split_blocks, max_splits, kernel;
+  int32_t unit_blocks, static_permille;  // the cut of the matrix-core kernels
   size_t ws_bytes;      // bytes the call needs
   size_t ws_o_offset;   // byte offset of the partial sums
   size_t ws_ml_offset;  // float index (from ws_o) of the (max, sum) pairs
 };
 
-// The workspace starts with kCtrCap arrival counters of the matrix-core
-// kernels, kCtrStride 32-bit words apart (one per 128-byte line), at the same
-// place for every call and shape: a zero-filled workspace stays valid because
-// every call leaves them at zero and nothing else is written there.
-constexpr int32_t kCtrCap = 4096;
+// The workspace starts with kCtrCap counters of the matrix-core kernels (the
+// unit queue, then one arrival counter per unit), kCtrStride 32-bit words
+// apart (one per 128-byte line), at the same place for every call and shape:
+// a zero-filled workspace stays valid because every call leaves them at zero
+// and nothing else is written there.
+constexpr int32_t kCtrCap = 8192;
 constexpr int32_t kCtrStride = 32;
 constexpr size_t kCtrBytes = size_t(kCtrCap) * kCtrStride * sizeof(unsigned);
+// Default cut of the matrix-core kernels' work list: each workgroup streams
+// this share (per mille) of its region, the rest is queued in units of
+// kUnitBlocks blocks.  Queued units balance the finish times of compute units
+// and XCDs, but a unit starts with an empty load pipeline, so at ~6 us of
+// loaded HBM latency they cost more than they win; off by default
+// (PA_STATIC_PERMILLE / PA_UNIT_BLOCKS turn them on).
+constexpr int32_t kStaticPermille = 1000;
+constexpr int32_t kUnitBlocks = 16;
 
 // Upper bound of the flattened work list (blocks of all (sequence, kv head)
 // segments) from the shapes alone.
@@ -167,10 +178,12 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
     const int64_t w = flat_upper(batch, d.n_kv_heads, max_seq_len);
     if (w >= (int64_t(1) << 31) - 4096) fail(pa::kInvalidArg, "batch * n_kv_heads * blocks too large");
     int32_t c = env_int("PA_SPLIT_BLOCKS", 0);  // fixed chunk size (tuning/tests)
+    int64_t units = 0;                          // units of the cut, at most
     if (c > 0) {
-      c = int32_t(std::max<int64_t>(c, (w + kCtrCap - 1) / kCtrCap));  // <= kCtrCap chunks
+      c = int32_t(std::max<int64_t>(c, (w + kCtrCap - 2) / (kCtrCap - 1)));  // < kCtrCap units
       pl.split_blocks = c;
       pl.max_splits = int32_t(std::max<int64_t>(1, (w + c - 1) / c));
+      units = pl.max_splits;
     } else {
       // persistent grid: one 4-wave workgroup per resident slot (from the
       // occupancy calculator); the chunk size is derived on the device from
@@ -179,10 +192,24 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
       int per_cu = env_int("PA_WG_PER_CU", 0);  // tuning knob; default: resident slots
       if (per_cu <= 0) per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype);
       pl.max_splits = int32_t(std::max<int64_t>(
-          1, std::min<int64_t>({w, int64_t(cu_count()) * per_cu, int64_t(kCtrCap)})));
+          1, std::min<int64_t>({w, int64_t(cu_count()) * per_cu, int64_t(kCtrCap / 2)})));
+      // queued units: the owner streams static_permille/1000 of its region,
+      // the rest goes to the queue in units of unit_blocks (doubled until the
+      // units fit the counters)
+      const int64_t r = pl.max_splits, cmax = (w + r - 1) / r;
+      pl.static_permille = std::clamp(env_int("PA_STATIC_PERMILLE", kStaticPermille), 0, 1000);
+      int64_t u = std::max(1, env_int("PA_UNIT_BLOCKS", kUnitBlocks));
+      if (pl.static_permille < 1000) {
+        while (1 + r * (1 + (cmax + u - 1) / u) > kCtrCap) u *= 2;
+        pl.unit_blocks = int32_t(u);
+        units = r * (1 + (cmax + u - 1) / u);
+      } else {
+        pl.unit_blocks = 0;
+        units = r;
+      }
     }
     const size_t g = size_t(n_q_heads / d.n_kv_heads);
-    const size_t rows = size_t(pl.max_splits) * 2 * g;
+    const size_t rows = size_t(units) * 2 * g;
     pl.ws_o_offset = kCtrBytes;
     pl.ws_ml_offset = rows * size_t(d.head_dim);
     pl.ws_bytes = kCtrBytes + rows * (size_t(d.head_dim) + 2) * sizeof(float);
@@ -255,6 +282,9 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
       a.counters = static_cast<unsigned*>(ws);
       a.ctr_stride = kCtrStride;
     }
+    a.prio = env_int("PA_PRIO", 1) != 0 ? 1 : 0;  // tuning knob
+    a.unit_blocks = pl.unit_blocks;
+    a.static_permille = pl.static_permille;
     a.split_blocks = pl.split_blocks;
     a.max_splits = pl.max_splits;
     a.kernel = pl.kernel;

@@ -264,6 +264,29 @@ def test_full_mixed_precision(kvdt):
     log(f"[gpu] mixed {kvdt} full max err {err:.3g}")
 
 
+QUEUE_ENVS = [
+    {"PA_WG_PER_CU": "1", "PA_UNIT_BLOCKS": "2", "PA_STATIC_PERMILLE": "500"},
+    {"PA_WG_PER_CU": "2", "PA_UNIT_BLOCKS": "5", "PA_STATIC_PERMILLE": "0"},
+    {"PA_STATIC_PERMILLE": "1000"},
+]
+
+
+@pytest.mark.parametrize("kvdt", ["bf16", "int4", "fp8"])
+@pytest.mark.parametrize("qenv", range(len(QUEUE_ENVS)))
+def test_queued_units_match_oracle_and_are_deterministic(kvdt, qenv):
+    """Work-list cuts with many queued units (segments spanning dozens of
+    units, taken in whatever order the workgroups finish) and with none: the
+    output matches the oracle and is bit-identical run to run."""
+    env = QUEUE_ENVS[qenv]
+    wl = W.from_lengths([3000, 1, 700, 2500, 16, 17, 1200, 900], 32, 8, 128, kvdt, seed=81,
+                        group=128 if kvdt == "int4" else 0, sink=kvdt != "bf16",
+                        outliers=kvdt != "bf16")
+    _, out_a, _, _ = run(wl, env=env)
+    _, out_b, _, _ = run(wl, env=env)
+    assert np.array_equal(out_a, out_b), f"{kvdt} {env}: not deterministic"
+    assert_close(out_a, expected(wl), "bf16" if kvdt == "bf16" else "f16", f"{kvdt} {env}")
+
+
 def test_workspace_reuse_across_calls_and_shapes():
     """One zero-filled workspace serves repeated calls and changing shapes: the
     arrival counters reset themselves, results stay bit-identical and correct."""
@@ -278,14 +301,16 @@ def test_workspace_reuse_across_calls_and_shapes():
         q = torch.from_numpy(wl.q()).to(TORCH_DT[wl.q_dtype]).to(DEV)
         runs[wl.name + str(wl.seed)] = (wl, kv, tdev, ldev, q, int(l.max()))
     outs = {}
+    modes = {"0": {}, "2": {"PA_SPLIT_BLOCKS": "2"}, "q": QUEUE_ENVS[0]}
     for rep in range(3):
         for key, (wl, kv, tdev, ldev, q, ml) in runs.items():
-            for split in ("0", "2"):
-                os.environ["PA_SPLIT_BLOCKS"] = split
+            for split, env in modes.items():
+                os.environ.update(env)
                 try:
                     o = kv.decode(q, tdev, ldev, ml, workspace=ws)
                 finally:
-                    os.environ.pop("PA_SPLIT_BLOCKS", None)
+                    for k in env:
+                        os.environ.pop(k, None)
                 torch.cuda.synchronize()
                 o = o.double().cpu().numpy()
                 if (key, split) in outs:
