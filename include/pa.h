@@ -266,6 +266,12 @@ pa_status pa_decode_combine(const void* q, const pa_pool* pool, const int32_t* b
 pa_status pa_decode_split_blocks(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
                                  int32_t max_seq_len, int32_t* out);
 
+/* Measurement aid (not a step of the method): read `bytes` bytes of device
+ * memory at src (16-byte aligned, bytes a multiple of 16) with a plain
+ * grid-stride streaming kernel, the achievable read rate to report beside the
+ * decode.  sink: device, >= 4 bytes, may be written.  Asynchronous on stream. */
+pa_status pa_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 const char* pa_last_error(void);
 

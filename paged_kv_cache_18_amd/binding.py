@@ -76,6 +76,7 @@ _PROTOS = {
     "pa_append_kv": [vp, vp, vp, i32, P32, i32, vp],
     "pa_decode_workspace_bytes": [vp, i32, i32, i32, C.POINTER(sz)],
     "pa_decode_split_blocks": [vp, i32, i32, i32, P32],
+    "pa_stream_read": [vp, sz, vp, vp],
     "pa_decode_attention": _DECODE_ARGS,
     "pa_decode_split": _DECODE_ARGS,
     "pa_decode_combine": _DECODE_ARGS,
@@ -300,6 +301,11 @@ def pa_decode_combine(q, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype, 
                       max_seq_len, scale, out, workspace, workspace_bytes, stream=None):
     _decode(lib().pa_decode_combine, q, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype,
             max_blocks, max_seq_len, scale, out, workspace, workspace_bytes, stream)
+
+
+def pa_stream_read(src, nbytes, sink, stream=None):
+    """Measurement aid: stream-read nbytes of device memory at src."""
+    _check(lib().pa_stream_read(_ptr(src), nbytes, _ptr(sink), _ptr(stream)))
 
 
 def pa_last_error():

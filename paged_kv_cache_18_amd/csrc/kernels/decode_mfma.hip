@@ -45,6 +45,8 @@
 // consumed (two register buffers).  After each piece the 4 waves merge
 // (max, sum, acc) through LDS; segments split across chunks are merged by the
 // workgroup that completes them (decode_common.hpp).
+#include <cstdlib>
+
 #include "decode_common.hpp"
 
 namespace pa {
@@ -53,8 +55,11 @@ namespace {
 
 using namespace dec;
 
-template <typename T>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_mfma16(DecodeArgs a) {
+// NB register buffers per wave: NB - 1 blocks in flight while one is
+// consumed.  NB = 2 fits three waves per SIMD (12 per compute unit); deeper
+// pipelines trade waves for blocks in flight per wave.
+template <typename T, int NB>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 3 : 2))) void decode_split_mfma16(DecodeArgs a) {
   typedef typename Mfma<T>::v8 v8;
   typedef typename Mfma<T>::v4 v4;
   __shared__ Shared sh;
@@ -192,30 +197,36 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
     l_run = 0.f;
 
     // Software pipeline over this wave's blocks jw+4k, k = 0..n-1: the loads
-    // of block k+1 are in flight while block k is consumed.  Two register
-    // buffers alternate (pairs of blocks per trip, one exit), so no copies and
-    // no full waits.  The prefetch past the last block re-reads it (an L2 hit).
+    // of blocks k+1 .. k+NB-1 are in flight while block k is consumed.  The
+    // buffers rotate inside a fully unrolled trip of NB blocks (no copies, no
+    // full waits); loads are unconditional, and past the last block they
+    // re-read it (an L2 hit, never consumed).
     const int jw = jbeg + w;
     const int n = jw < jend ? (jend - jw + kWaves - 1) / kWaves : 0;
-    auto id_of = [&](int k) { return trow[jw + kWaves * k]; };
+    auto id_of = [&](int k) { return trow[jw + kWaves * min(k, n - 1)]; };
     auto valid_of = [&](int k, int id) { return ok(id) ? L - 16 * (jw + kWaves * k) : 0; };
-    v8 ka[4], va[4], kb[4], vb[4];
     if (n > 0) {
-      int ida = id_of(0);
-      fetch(ida, ka, va);
-      int k = 0;
-      for (; k + 1 < n; k += 2) {
-        prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
-        const int idb = id_of(k + 1);
-        fetch(idb, kb, vb);
-        consume(valid_of(k, ida), ka, va);
-        const int kn = min(k + 2, n - 1);
-        const int idn = id_of(kn);
-        fetch(idn, ka, va);
-        consume(valid_of(k + 1, idb), kb, vb);
-        ida = idn;
+      v8 kb[NB][4], vb[NB][4];
+      int ids[NB];
+#pragma unroll
+      for (int s = 0; s < NB - 1; ++s) {
+        ids[s] = id_of(s);
+        fetch(ids[s], kb[s], vb[s]);
       }
-      if (k < n) consume(valid_of(k, ida), ka, va);
+      int k = 0;
+      for (; k + NB <= n; k += NB) {
+        prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+          const int nxt = (s + NB - 1) % NB;
+          ids[nxt] = id_of(k + s + NB - 1);
+          fetch(ids[nxt], kb[nxt], vb[nxt]);
+          consume(valid_of(k + s, ids[s]), kb[s], vb[s]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NB - 1; ++s)
+        if (k + s < n) consume(valid_of(k + s, ids[s]), kb[s], vb[s]);
     }
 
     // ---- merge the 4 waves of this piece, write it -----------------------------
@@ -229,27 +240,50 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3))
   }
 }
 
+// Prefetch depth (PA_MFMA_NB = 2, 3 or 4; default 2).
+int mfma_nb() {
+  static int nb = 0;
+  if (nb == 0) {
+    const char* e = std::getenv("PA_MFMA_NB");
+    const int v = e ? std::atoi(e) : 2;
+    nb = (v == 3 || v == 4) ? v : 2;
+  }
+  return nb;
+}
+
+template <typename T>
+hipError_t launch_nb(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(unsigned(a.max_splits)), block(kWaves * 64);
+  switch (mfma_nb()) {
+    case 3: hipLaunchKernelGGL((decode_split_mfma16<T, 3>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_mfma16<T, 4>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_split_mfma16<T, 2>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+int occupancy_nb() {
+  int n = 0;
+  hipError_t e;
+  switch (mfma_nb()) {
+    case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 3>, kWaves * 64, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 4>, kWaves * 64, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2>, kWaves * 64, 0); break;
+  }
+  return (e == hipSuccess && n > 0) ? n : 2;
+}
+
 }  // namespace
 
 hipError_t launch_decode_split_mfma16(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(unsigned(a.max_splits));
-  if (a.pool.kv_dtype == kBF16)
-    hipLaunchKernelGGL(decode_split_mfma16<__bf16>, grid, dim3(kWaves * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_split_mfma16<_Float16>, grid, dim3(kWaves * 64), 0, s, a);
-  return hipGetLastError();
+  return a.pool.kv_dtype == kBF16 ? launch_nb<__bf16>(a, s) : launch_nb<_Float16>(a, s);
 }
 
 int occupancy_mfma16(int32_t kv_dtype) {
   static int cache[2] = {0, 0};
   const int i = kv_dtype == kBF16 ? 0 : 1;
-  if (cache[i] == 0) {
-    int n = 0;
-    const hipError_t e =
-        i == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<__bf16>, kWaves * 64, 0)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<_Float16>, kWaves * 64, 0);
-    cache[i] = (e == hipSuccess && n > 0) ? n : 2;
-  }
+  if (cache[i] == 0) cache[i] = i == 0 ? occupancy_nb<__bf16>() : occupancy_nb<_Float16>();
   return cache[i];
 }
 

@@ -54,4 +54,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
 int decode_split_occupancy(int32_t kernel, int32_t kv_dtype);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 
+// Streaming read of `bytes` (a multiple of 16) at src with `grid` workgroups.
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, int grid, hipStream_t s);
+
 }  // namespace pa

@@ -551,6 +551,18 @@ pa_status pa_decode_combine(const void* q, const pa_pool* pool, const int32_t* t
                 max_seq_len, scale, out, ws, ws_bytes, stream);
 }
 
+pa_status pa_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  return guard([&] {
+    need(src, "src");
+    need(sink, "sink");
+    if (bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+      fail(pa::kInvalidArg, "src must be 16-byte aligned and bytes a multiple of 16");
+    if (bytes == 0) return;
+    check_hip(pa::launch_stream_read(src, bytes, sink, cu_count() * 8, static_cast<hipStream_t>(stream)),
+              "stream read launch");
+  });
+}
+
 const char* pa_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"
