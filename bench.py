@@ -4,14 +4,18 @@ One step = one decode step of one attention layer for the whole batch:
   1. append each sequence's newest K/V token into its slot (quantize-on-write
      for INT4/FP8 pools),
   2. split-K decode over all cached tokens (gathered through block tables),
-  3. log-sum-exp combine of the splits.
+     including the log-sum-exp merge of split segments (fused into the
+     matrix-core kernels; a second launch for the generic kernel).
 Inputs are seeded synthetic data already resident in HBM when timing starts.
 
 `value` is KV GB/s: the algorithmic K/V bytes one decode step must read
 (sum over sequences of L * Hkv * 2 * D * bytes/element, or the packed
 INT4/FP8 bytes plus their fp16 scales) divided by the measured step time.
 `roofline` prices the dominant kernel (the split kernel) against 8 TB/s with
-its own launch durations, measured with HIP events on the launch stream.
+its own launch durations, measured with HIP events on the launch stream;
+`roofline.traffic` is the HBM bytes rocprofv3 counted for one launch
+(profiles/hbm_traffic.json) over the same duration.  `stream_read_gbs` is a
+plain streaming read of the same byte count (the achievable rate).
 `cpu_baseline` times the CPU oracle (logical rebuild through the tables +
 float64 attention) on a bounded sample of the same batch.
 
@@ -274,7 +278,8 @@ def main():
                    "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
                    "head_dim": wl.head_dim, "block_size": 16, "kv_dtype": wl.kv_dtype,
                    "total_tokens": int(sum(lens)), "max_seq_len": max_len,
-                   "split_blocks": split_blocks},
+                   **({"split_blocks": split_blocks} if split_blocks > 0
+                      else {"persistent_workgroups": -split_blocks})},
         "queries_per_s": round(wl.batch / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": byts,

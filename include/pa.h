@@ -262,7 +262,10 @@ pa_status pa_decode_combine(const void* q, const pa_pool* pool, const int32_t* b
                             float scale, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
-/* Blocks per split the decode uses for these shapes (informational). */
+/* How the decode splits its work for these shapes (informational): > 0 is a
+ * fixed number of blocks per chunk; < 0 is minus the number of workgroups of
+ * the persistent grid, whose chunks are sized on the device from the
+ * lengths. */
 pa_status pa_decode_split_blocks(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
                                  int32_t max_seq_len, int32_t* out);
 
