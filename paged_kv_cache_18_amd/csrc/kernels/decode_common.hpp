@@ -122,7 +122,7 @@ struct Units {
 __device__ inline Units setup_units(const DecodeArgs& a, Shared& sh, int w, int lane) {
   if (w == 0) {
     const int W = total_work(a, lane);
-    const int R = int(gridDim.x);
+    const int R = a.max_splits;  // the split kernel's grid
     int C, Cs, U = 1, m = 0;
     if (a.split_blocks > 0) {
       C = Cs = a.split_blocks;
@@ -299,14 +299,32 @@ constexpr int kSc1 = 16;
 
 // Merge the np partials of segment (b, h), which starts at position S of the
 // list, and write out.  Its first unit c0 holds its piece in slot 1 unless
-// the segment starts the unit, every later unit in slot 0.  Pieces are taken in
-// runs of kRun with a running max per head:
+// the segment starts the unit, every later unit in slot 0.  Thread (pg, col)
+// folds pieces pg, pg + P, ... of one 16-byte output column with a running
+// log-sum-exp (m, l, acc), kMergeBatch pieces in flight; each batch's (max,
+// sum) pairs are loaded once (one per thread, issued with the partial sums)
+// and shared through LDS.  The P piece groups of a column are then folded in
+// order through LDS:
 //   m = max m_i, l = sum l_i 2^(m_i - m), o = sum o_i 2^(m_i - m) / l.
-// Partial sums are read 16 bytes per lane with 8 loads in flight per lane,
-// so a segment of many pieces costs a few memory round trips.
+// The order is fixed, so the result does not depend on arrival order.
+constexpr int kMergeBatch = 12;  // 16 spills at three waves per SIMD
+
+struct Lse {
+  float m, l;
+  f32x4 o;
+  __device__ void add(float mi, float li, f32x4 oi) {
+    if (mi == -__builtin_inff()) return;  // a piece of no token
+    const float mn = fmaxf(m, mi);
+    const float sa = exp2f(m - mn), sb = exp2f(mi - mn);
+    o = o * sa + oi * sb;
+    l = l * sa + li * sb;
+    m = mn;
+  }
+};
+
 template <typename TO>
-__device__ inline void merge_segment(const DecodeArgs& a, Shared& sh, int w, int lane, int b,
-                                     int h, int S, int np, const Units& um) {
+__device__ inline void merge_segment(const DecodeArgs& a, Shared& sh, int b, int h, int S, int np,
+                                     const Units& um, int col0, int ncol) {
   const int Hq = a.n_q_heads, G = Hq / a.pool.n_kv_heads;
   const int c0 = um.unit_of(S);
   const bool split_first = S != um.start(c0);
@@ -318,103 +336,73 @@ __device__ inline void merge_segment(const DecodeArgs& a, Shared& sh, int w, int
       __builtin_amdgcn_make_buffer_rsrc(a.ws_o, (short)0, int(rows * kD * 4), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rml =
       __builtin_amdgcn_make_buffer_rsrc(a.ws_ml, (short)0, int(rows * 8), kRsrcWord3);
-  const float ninf = -__builtin_inff();
-  constexpr int kRun = 128;                     // pieces per run
-  float* mm = &sh.o[0][0][0];                   // [kRun * G] m, then weights
-  float* ll = mm + kRun * 16;                   // [kRun * G] l
-  float* accs = ll + kRun * 16;                 // [G * kD] running output sums
-  f32x4* red = reinterpret_cast<f32x4*>(accs + 16 * kD);  // [256] cross-group sums
-  static_assert(2 * kRun * 16 + 16 * kD + 4 * 256 <= kWaves * 16 * (kD + 1), "LDS reuse");
-  const int tid = threadIdx.x;
-  if (tid < G) {
-    sh.m[0][tid] = ninf;
-    sh.l[0][tid] = 0.f;
-  }
-  for (int idx = tid; idx < G * kD; idx += kWaves * 64) accs[idx] = 0.f;
-  const int F = G * (kD / 4);                   // float4 columns of a piece
-  const int P = F >= 256 ? 1 : 256 / F;         // piece groups summed in parallel
+  constexpr int kCols = kD / 4;           // float4 columns of one head
+  const int F = ncol;                     // float4 columns merged here (multiple of kCols)
+  const int h0 = col0 / kCols, nh = F / kCols;
+  const int P = F >= 256 ? 1 : 256 / F;   // piece groups
   const int Fc = F >= 256 ? 256 : F;
-  for (int q0 = 0; q0 < np; q0 += kRun) {
-    const int qn = min(kRun, np - q0);
-    for (int t = tid; t < qn * G; t += kWaves * 64) {
-      const int i = t / G, hc = t % G;
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rml, (row_of(q0 + i) + hc) * 8u, 0, kSc1);
-      mm[t] = __uint_as_float(v[0]);
-      ll[t] = __uint_as_float(v[1]);
-    }
-    __syncthreads();
-    for (int hc = w; hc < G; hc += kWaves) {
-      float M = ninf;
-      for (int i = lane; i < qn; i += 64) M = fmaxf(M, mm[i * G + hc]);
-      M = wave_max(M);
-      const float m_old = sh.m[0][hc];
-      const float m_new = fmaxf(m_old, M);
-      float lsum = 0.f;
-      for (int i = lane; i < qn; i += 64) {
-        const float m = mm[i * G + hc];
-        const float wt = m != ninf ? exp2f(m - m_new) : 0.f;
-        mm[i * G + hc] = wt;
-        lsum += ll[i * G + hc] * wt;
+  const int tid = threadIdx.x;
+  const int pg = tid / Fc, c = tid % Fc;
+  const int span = kMergeBatch * P;       // pieces per batch (span * nh <= 256 pairs)
+  float* red = &sh.o[0][0][0];            // [256][6]: m, l, o of each thread
+  float2* mls = reinterpret_cast<float2*>(red + 256 * 6);  // [span][nh] (max, sum) of the batch
+  static_assert(256 * 6 + 2 * 256 <= kWaves * 16 * (kD + 1), "LDS reuse");
+  TO* out = static_cast<TO*>(a.out) + (size_t(b) * Hq + h * G) * kD;
+  for (int cc = c; cc < F; cc += Fc) {  // one trip unless F > 256 (two columns per thread)
+    const int col = col0 + cc;
+    const int hc = col / kCols;
+    const unsigned cb = unsigned(hc) * kD * 4u + unsigned(col % kCols) * 16u;
+    Lse r{-__builtin_inff(), 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int q0 = 0; q0 < np; q0 += span) {
+      // one (max, sum) pair per thread, issued with this thread's partial sums
+      // (unconditionally: a load under a branch makes the compiler wait for it
+      // before the loads that follow)
+      const int pt = min(tid, span * nh - 1);
+      const u32x2 pair = __builtin_amdgcn_raw_buffer_load_b64(
+          rml, (row_of(min(q0 + pt / nh, np - 1)) + h0 + pt % nh) * 8u, 0, kSc1);
+      u32x4 ov[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int i = min(q0 + u * P + pg, np - 1);  // past the end: a re-read, never used
+        ov[u] = __builtin_amdgcn_raw_buffer_load_b128(ro, row_of(i) * kD * 4u + cb, 0, kSc1);
       }
-      lsum = wave_sum(lsum);
-      if (lane == 0) {
-        const float sc = m_old != ninf ? exp2f(m_old - m_new) : 0.f;
-        sh.l[1][hc] = sc;
-        sh.l[0][hc] = sh.l[0][hc] * sc + lsum;
-        sh.m[0][hc] = m_new;
-      }
-    }
-    __syncthreads();
-    const int pg = tid / Fc, c = tid % Fc;
-    if (pg < P) {
-      for (int col = c; col < F; col += Fc) {
-        const int hc = col / (kD / 4);
-        const unsigned cb = unsigned(col % (kD / 4)) * 16u + unsigned(hc) * kD * 4u;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        int i = pg;
-        for (; i + 7 * P < qn; i += 8 * P) {
-          u32x4 v[8];
+      if (tid < span * nh) mls[tid] = float2{__uint_as_float(pair[0]), __uint_as_float(pair[1])};
+      __syncthreads();
+      if (pg < P) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            v[u] = __builtin_amdgcn_raw_buffer_load_b128(ro, row_of(q0 + i + u * P) * kD * 4u + cb, 0, kSc1);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const float wt = mm[(i + u * P) * G + hc];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(v[u][e]) * wt;
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const int i = q0 + u * P + pg;
+          if (i < np) {
+            const float2 ml = mls[(u * P + pg) * nh + hc - h0];
+            r.add(ml.x, ml.y, f32x4{__uint_as_float(ov[u][0]), __uint_as_float(ov[u][1]),
+                                    __uint_as_float(ov[u][2]), __uint_as_float(ov[u][3])});
           }
         }
-        for (; i < qn; i += P) {
-          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ro, row_of(q0 + i) * kD * 4u + cb, 0, kSc1);
-          const float wt = mm[i * G + hc];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(v[e]) * wt;
-        }
-        if (P == 1) {
-          const float sc = sh.l[1][hc];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) accs[col * 4 + e] = accs[col * 4 + e] * sc + acc[e];
-        } else {
-          red[tid] = acc;
-        }
       }
+      __syncthreads();  // mls is rewritten by the next batch
     }
     if (P > 1) {
+      float* e = red + tid * 6;
+      e[0] = r.m;
+      e[1] = r.l;
+      e[2] = r.o[0];
+      e[3] = r.o[1];
+      e[4] = r.o[2];
+      e[5] = r.o[3];
       __syncthreads();
       if (tid < F) {
-        const float sc = sh.l[1][tid / (kD / 4)];
-        f32x4 s = red[tid];
-        for (int g2 = 1; g2 < P; ++g2) s += red[g2 * F + tid];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) accs[tid * 4 + e] = accs[tid * 4 + e] * sc + s[e];
+        r = Lse{-__builtin_inff(), 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int g2 = 0; g2 < P; ++g2) {
+          const float* q = red + (g2 * Fc + tid) * 6;
+          r.add(q[0], q[1], f32x4{q[2], q[3], q[4], q[5]});
+        }
       }
     }
-    __syncthreads();
-  }
-  TO* out = static_cast<TO*>(a.out);
-  for (int idx = tid; idx < G * kD; idx += kWaves * 64) {
-    const float L = sh.l[0][idx / kD];
-    out[(size_t(b) * Hq + h * G) * kD + idx] = TO(L > 0.f ? accs[idx] / L : 0.f);
+    if (pg == 0) {
+      const float inv = r.l > 0.f ? 1.f / r.l : 0.f;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) out[col * 4 + e2] = TO(r.o[e2] * inv);
+    }
   }
 }
 
@@ -430,7 +418,6 @@ __device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g
                                    int slot, int unit, int b, int h, int S, int nb,
                                    const Units& um) {
   const int Hq = a.n_q_heads, G = Hq / a.pool.n_kv_heads;
-  const int lane = threadIdx.x & 63;
   if (g == 0) {
     sh.m[w][c] = m_ref;
     sh.l[w][c] = l_run;
@@ -465,7 +452,7 @@ __device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g
       }
     }
   }
-  if (!complete) {
+  if (!complete && !a.defer_merge) {
     const int c0 = um.unit_of(S);
     const int np = um.unit_of(S + nb - 1) - c0 + 1;
     wait_stores();  // this workgroup's partial is complete before its arrival counts
@@ -473,7 +460,7 @@ __device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g
     if (threadIdx.x == 0) sh.last = arrive(a, c0, np) ? 1 : 0;
     __syncthreads();
     if (sh.last) {
-      merge_segment<TO>(a, sh, w, lane, b, h, S, np, um);
+      merge_segment<TO>(a, sh, b, h, S, np, um, 0, G * (kD / 4));
     }
   }
   __syncthreads();

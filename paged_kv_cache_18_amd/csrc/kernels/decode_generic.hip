@@ -217,8 +217,10 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
-  // the matrix-core kernels merge split segments themselves
-  if (a.kernel == kKernMfma16 || a.kernel == kKernQuant) return hipSuccess;
+  // the matrix-core kernels merge split segments themselves, or leave them to
+  // the merge launch
+  if (a.kernel == kKernMfma16 || a.kernel == kKernQuant)
+    return a.defer_merge ? launch_decode_merge(a, s) : hipSuccess;
   if (a.max_splits <= 1) return hipSuccess;
   dim3 grid(unsigned(a.n_q_heads), unsigned(a.batch));
   hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(64), 0, s, a);

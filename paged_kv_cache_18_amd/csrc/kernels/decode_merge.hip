@@ -1,0 +1,48 @@
+// Merge launch of the matrix-core decode: the log-sum-exp merge of every
+// (sequence, KV head) segment that the split kernel left in pieces
+// (defer_merge = 1; chosen when segments span many workgroups, so that one
+// merge per segment would leave a long serial tail at the end of the split).
+//
+// One workgroup per (sequence b, KV head h, query head c of the group): it
+// rebuilds the work-list cut from the lengths exactly as the split kernel
+// did, finds the segment's pieces and folds the 32 16-byte columns of head c
+// over them (decode_common.hpp, merge_segment), in list order.  A segment of
+// one piece was written by the split kernel and is skipped.
+#include "decode_common.hpp"
+
+namespace pa {
+
+namespace {
+
+using namespace dec;
+
+template <typename TO>
+__global__ __launch_bounds__(kWaves * 64) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ Shared sh;
+  const int H = a.pool.n_kv_heads, G = a.n_q_heads / H;
+  const int hc = int(blockIdx.x) % G, bh = int(blockIdx.x) / G;
+  const int b = bh / H, h = bh % H;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nb = seq_blocks(a, b);
+  if (nb == 0) return;  // workgroup-uniform
+  const Units um = setup_units(a, sh, w, lane);
+  const int S = seq_start(a, b, lane) + h * nb;  // every wave computes it
+  const int np = um.unit_of(S + nb - 1) - um.unit_of(S) + 1;
+  if (np <= 1) return;
+  merge_segment<TO>(a, sh, b, h, S, np, um, hc * (kD / 4), kD / 4);
+}
+
+}  // namespace
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
+  const int G = a.n_q_heads / a.pool.n_kv_heads;
+  const dim3 grid(unsigned(a.batch) * unsigned(a.pool.n_kv_heads) * unsigned(G));
+  if (a.q_dtype == kBF16)
+    hipLaunchKernelGGL(decode_merge_kernel<__bf16>, grid, dim3(kWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<_Float16>, grid, dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

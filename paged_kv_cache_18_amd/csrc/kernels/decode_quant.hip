@@ -369,13 +369,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
 
 }  // namespace
 
-// Prefetch depth: two buffers by default (3 waves per SIMD); PA_QUANT_NB=3
-// selects three.
+// Prefetch depth: PA_QUANT_NB = 2 (default, 3 waves per SIMD), 3, 4 or 6
+// (2 waves per SIMD).
 int quant_nb() {
   static int nb = 0;
   if (nb == 0) {
     const char* e = std::getenv("PA_QUANT_NB");
-    nb = (e && std::atoi(e) == 3) ? 3 : 2;
+    const int v = e ? std::atoi(e) : 2;
+    nb = (v == 3 || v == 4 || v == 6) ? v : 2;
   }
   return nb;
 }
@@ -388,26 +389,39 @@ int occ_of() {
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 
+template <int KIND>
+int occ_kind() {
+  switch (quant_nb()) {
+    case 3: return occ_of<KIND, 3>();
+    case 4: return occ_of<KIND, 4>();
+    case 6: return occ_of<KIND, 6>();
+    default: return occ_of<KIND, 2>();
+  }
+}
+
+template <int KIND>
+void launch_kind(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(unsigned(a.max_splits)), block(kWaves * 64);
+  switch (quant_nb()) {
+    case 3: hipLaunchKernelGGL((decode_split_quant<KIND, 3>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_quant<KIND, 4>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((decode_split_quant<KIND, 6>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_split_quant<KIND, 2>), grid, block, 0, s, a); break;
+  }
+}
+
 int occupancy_quant(int32_t kv_dtype) {
-  static int cache[2][2] = {{0, 0}, {0, 0}};
-  const int i = kv_dtype == kInt4 ? 0 : 1, j = quant_nb() == 3 ? 1 : 0;
-  if (cache[i][j] == 0)
-    cache[i][j] = i == 0 ? (j ? occ_of<kInt4, 3>() : occ_of<kInt4, 2>())
-                         : (j ? occ_of<kFp8, 3>() : occ_of<kFp8, 2>());
-  return cache[i][j];
+  static int cache[2] = {0, 0};
+  const int i = kv_dtype == kInt4 ? 0 : 1;
+  if (cache[i] == 0) cache[i] = i == 0 ? occ_kind<kInt4>() : occ_kind<kFp8>();
+  return cache[i];
 }
 
 hipError_t launch_decode_split_quant(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(unsigned(a.max_splits));
-  const bool i4 = a.pool.kv_dtype == kInt4, deep = quant_nb() == 3;
-  if (i4 && deep)
-    hipLaunchKernelGGL((decode_split_quant<kInt4, 3>), grid, dim3(kWaves * 64), 0, s, a);
-  else if (i4)
-    hipLaunchKernelGGL((decode_split_quant<kInt4, 2>), grid, dim3(kWaves * 64), 0, s, a);
-  else if (deep)
-    hipLaunchKernelGGL((decode_split_quant<kFp8, 3>), grid, dim3(kWaves * 64), 0, s, a);
+  if (a.pool.kv_dtype == kInt4)
+    launch_kind<kInt4>(a, s);
   else
-    hipLaunchKernelGGL((decode_split_quant<kFp8, 2>), grid, dim3(kWaves * 64), 0, s, a);
+    launch_kind<kFp8>(a, s);
   return hipGetLastError();
 }
 

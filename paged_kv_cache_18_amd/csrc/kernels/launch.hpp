@@ -46,6 +46,7 @@ struct DecodeArgs {
   int32_t prio;          // matrix-core kernels: 1 = progress-based wave priority
   int32_t unit_blocks;   // matrix-core kernels: blocks per queued unit (0: none)
   int32_t static_permille;  // share of a region its owner streams, in 1/1000
+  int32_t defer_merge;   // matrix-core kernels: 1 = leave split segments to the merge launch
 };
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
@@ -53,6 +54,8 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
 // of kv_dtype (from the runtime's occupancy calculator; cached).
 int decode_split_occupancy(int32_t kernel, int32_t kv_dtype);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
+// Merge launch of the matrix-core kernels (defer_merge = 1).
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
 
 // Streaming read of `bytes` (a multiple of 16) at src with `grid` workgroups.
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, int grid, hipStream_t s);

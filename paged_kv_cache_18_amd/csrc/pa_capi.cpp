@@ -127,6 +127,7 @@ int cu_count() {
 struct Plan {
   int32_t split_blocks, max_splits, kernel;
   int32_t unit_blocks, static_permille;  // the cut of the matrix-core kernels
+  int32_t defer_merge;                   // split segments merged by a second launch
   size_t ws_bytes;      // bytes the call needs
   size_t ws_o_offset;   // byte offset of the partial sums
   size_t ws_ml_offset;  // float index (from ws_o) of the (max, sum) pairs
@@ -148,6 +149,9 @@ constexpr size_t kCtrBytes = size_t(kCtrCap) * kCtrStride * sizeof(unsigned);
 // (PA_STATIC_PERMILLE / PA_UNIT_BLOCKS turn them on).
 constexpr int32_t kStaticPermille = 1000;
 constexpr int32_t kUnitBlocks = 16;
+// Average pieces per segment above which split segments are merged by a
+// second launch instead of inside the split kernel.
+constexpr int32_t kFuseMaxPieces = 16;
 
 // Upper bound of the flattened work list (blocks of all (sequence, kv head)
 // segments) from the shapes alone.
@@ -208,6 +212,13 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
         units = r;
       }
     }
+    // Merging a segment is one round of loads per kMergeBatch pieces per
+    // thread, done by the workgroup that completes it; when segments span
+    // many workgroups on average those rounds form a serial tail, and a
+    // second launch with one workgroup per (segment, query head) is shorter.
+    const int64_t segs = std::max<int64_t>(1, int64_t(batch) * d.n_kv_heads);
+    const int fuse_max = env_int("PA_FUSE_MAX_PIECES", kFuseMaxPieces);
+    pl.defer_merge = units / segs + 1 > fuse_max ? 1 : 0;
     const size_t g = size_t(n_q_heads / d.n_kv_heads);
     const size_t rows = size_t(units) * 2 * g;
     pl.ws_o_offset = kCtrBytes;
@@ -285,6 +296,7 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     a.prio = env_int("PA_PRIO", 1) != 0 ? 1 : 0;  // tuning knob
     a.unit_blocks = pl.unit_blocks;
     a.static_permille = pl.static_permille;
+    a.defer_merge = pl.defer_merge;
     a.split_blocks = pl.split_blocks;
     a.max_splits = pl.max_splits;
     a.kernel = pl.kernel;

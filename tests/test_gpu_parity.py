@@ -268,6 +268,11 @@ QUEUE_ENVS = [
     {"PA_WG_PER_CU": "1", "PA_UNIT_BLOCKS": "2", "PA_STATIC_PERMILLE": "500"},
     {"PA_WG_PER_CU": "2", "PA_UNIT_BLOCKS": "5", "PA_STATIC_PERMILLE": "0"},
     {"PA_STATIC_PERMILLE": "1000"},
+    # split segments merged by the second launch / always inside the split
+    {"PA_FUSE_MAX_PIECES": "1"},
+    {"PA_FUSE_MAX_PIECES": "1", "PA_WG_PER_CU": "1", "PA_UNIT_BLOCKS": "2",
+     "PA_STATIC_PERMILLE": "500"},
+    {"PA_FUSE_MAX_PIECES": "100000", "PA_WG_PER_CU": "1"},
 ]
 
 
@@ -301,7 +306,7 @@ def test_workspace_reuse_across_calls_and_shapes():
         q = torch.from_numpy(wl.q()).to(TORCH_DT[wl.q_dtype]).to(DEV)
         runs[wl.name + str(wl.seed)] = (wl, kv, tdev, ldev, q, int(l.max()))
     outs = {}
-    modes = {"0": {}, "2": {"PA_SPLIT_BLOCKS": "2"}, "q": QUEUE_ENVS[0]}
+    modes = {"0": {}, "2": {"PA_SPLIT_BLOCKS": "2"}, "q": QUEUE_ENVS[0], "d": QUEUE_ENVS[4]}
     for rep in range(3):
         for key, (wl, kv, tdev, ldev, q, ml) in runs.items():
             for split, env in modes.items():
