@@ -262,6 +262,32 @@ pa_status pa_decode_combine(const void* q, const pa_pool* pool, const int32_t* b
                             float scale, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* ---- speculative verify step ----------------------------------------------- */
+
+/* Workspace bytes pa_verify_attention needs for these shapes. */
+pa_status pa_verify_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
+                                    int32_t n_query, int32_t max_seq_len, size_t* bytes);
+
+/* Verify attention of a speculative step ([8GB] section 6: the target model
+ * runs one pass over the gamma + 1 tokens -- the last accepted one and gamma
+ * draft tokens -- at once; the flowchart of section 5 then rolls back the
+ * rejected tail).  The n_query new tokens of every sequence are already
+ * appended (pa_seq_reserve + pa_append_kv), so they are its last n_query
+ * cached tokens; query i (0-based) of sequence b attends to tokens
+ * 0 .. L_b - n_query + i, i.e. the whole cache before the step plus the new
+ * tokens up to itself (causal among the new ones).  Query i = n_query - 1 is
+ * exactly the decode of the whole sequence.  A query whose position falls
+ * before the start of the cache (L_b < n_query) has no token: zero output.
+ *  q, out: device [batch][n_query][n_q_heads][head_dim] of q_dtype.
+ *  n_query: 1..64 (gamma + 1).  Other arguments and the workspace contract
+ *  are those of pa_decode_attention.  Rollback of rejected tokens is
+ *  pa_seq_truncate (their blocks return to the free stack last-first). */
+pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
+                              const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
+                              int32_t n_query, int32_t q_dtype, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, float scale, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* How the decode splits its work for these shapes (informational): > 0 is a
  * fixed number of blocks per chunk; < 0 is minus the number of workgroups of
  * the persistent grid, whose chunks are sized on the device from the

@@ -53,6 +53,30 @@ def attention_one(q, K, V, scale):
     return out
 
 
+def verify_attention_one(q, K, V, scale):
+    """Attention of a speculative verify step for one sequence.
+
+    The target model scores the gamma + 1 new tokens (the last accepted one
+    and the gamma draft tokens) in one pass (8GB page, section 6,
+    "Speculative Decoding: Breaking the Bandwidth Wall").  Reading: their K/V
+    are already appended, so they are the last ``nq`` of the ``L`` cached
+    tokens, and query i sees the cache up to and including its own token,
+    tokens ``0 .. L - nq + i`` (causal among the new tokens).  A query whose
+    position lies before the cache start sees nothing: zero row.
+
+    q: [nq][Hq][D]; K, V: [L][Hkv][D].  Returns [nq][Hq][D] float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    nq = q.shape[0]
+    L = np.asarray(K).shape[0]
+    out = np.zeros(q.shape, dtype=np.float64)
+    for i in range(nq):
+        n = L - nq + i + 1
+        if n > 0:
+            out[i] = attention_one(q[i], np.asarray(K)[:n], np.asarray(V)[:n], scale)
+    return out
+
+
 def decode_attention(q, kv, scale):
     """q: [B][Hq][D]; kv: list of (K, V) per sequence, each [L_b][Hkv][D]."""
     return np.stack([attention_one(q[b], K, V, scale) for b, (K, V) in enumerate(kv)])

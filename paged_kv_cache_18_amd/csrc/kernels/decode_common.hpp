@@ -80,15 +80,35 @@ __device__ inline int total_work(const DecodeArgs& a, int lane) {
   return wave_sum_int(tot);
 }
 
-struct Shared {
-  float m[kWaves][16];
-  float l[kWaves][16];
-  alignas(16) float o[kWaves][16][kD + 1];
+// LDS of a workgroup: per wave and output column (max, sum, acc) of the
+// current piece, reused as scratch by the segment merge.
+template <int CAP>
+struct SharedT {
+  float m[kWaves][CAP];
+  float l[kWaves][CAP];
+  alignas(16) float o[kWaves][CAP][kD + 1];
   int b, fb;
   int units[6];
   int next;
   int last;
 };
+using Shared = SharedT<16>;
+
+// Output columns of a segment (b, h): column col = qi*G + gi is query qi of
+// the sequence's n_query (1 for decode) and query head h*G + gi, stored at
+// row (b*n_query + qi)*Hq + h*G + gi of out ([batch][n_query][Hq][D]).
+struct OutMap {
+  int G, Hq, nq;
+  __device__ int ncol() const { return nq * G; }
+  __device__ size_t row(int b, int h, int col) const {
+    return (size_t(b) * nq + col / G) * Hq + h * G + col % G;
+  }
+};
+
+__device__ inline OutMap out_map(const DecodeArgs& a) {
+  const int G = a.n_q_heads / a.pool.n_kv_heads;
+  return OutMap{G, a.n_q_heads, max(a.n_query, 1)};
+}
 
 // The cut of the work list (see the top of this file).  Unit ids grow with
 // position: region r holds units r*(1+m) (its prefix) .. r*(1+m)+m.
@@ -119,7 +139,8 @@ struct Units {
 };
 
 // Wave 0 sizes the cut from the lengths; every thread gets it.
-__device__ inline Units setup_units(const DecodeArgs& a, Shared& sh, int w, int lane) {
+template <class SH>
+__device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane) {
   if (w == 0) {
     const int W = total_work(a, lane);
     const int R = a.max_splits;  // the split kernel's grid
@@ -150,7 +171,8 @@ __device__ inline Units setup_units(const DecodeArgs& a, Shared& sh, int w, int 
 
 // Wave 0 finds the sequence b holding position p0 and the position fb of its
 // first block; every thread gets them.
-__device__ inline void locate(const DecodeArgs& a, Shared& sh, int w, int lane, int p0, int& b,
+template <class SH>
+__device__ inline void locate(const DecodeArgs& a, SH& sh, int w, int lane, int p0, int& b,
                               int& fb) {
   const int H = a.pool.n_kv_heads, B = a.batch;
   if (w == 0) {
@@ -193,7 +215,8 @@ __device__ inline unsigned* unit_counter(const DecodeArgs& a, int u) {
 // region's prefix id), then units from the queue; -1 when the queue is empty.
 // Every workgroup ends with exactly one refused take, so the take that sees
 // count R*m + R - 1 is the call's last and resets the queue to 0.
-__device__ inline int next_unit(const DecodeArgs& a, Shared& sh, const Units& um) {
+template <class SH>
+__device__ inline int next_unit(const DecodeArgs& a, SH& sh, const Units& um) {
   if (um.m == 0) return -1;
   if (threadIdx.x == 0) {
     const unsigned nq = unsigned(um.R) * unsigned(um.m);
@@ -221,11 +244,12 @@ __device__ inline int next_unit(const DecodeArgs& a, Shared& sh, const Units& um
 // c takes sequences c, c + grid, ...
 template <typename TO>
 __device__ inline void zero_empty_rows(const DecodeArgs& a) {
-  const int Hq = a.n_q_heads;
+  const int Hq = a.n_q_heads, nq = max(a.n_query, 1);
   TO* out = static_cast<TO*>(a.out);
   for (int b = blockIdx.x; b < a.batch; b += gridDim.x)
     if (seq_blocks(a, b) == 0)
-      for (int i = threadIdx.x; i < Hq * kD; i += kWaves * 64) out[size_t(b) * Hq * kD + i] = TO(0.f);
+      for (int i = threadIdx.x; i < nq * Hq * kD; i += kWaves * 64)
+        out[size_t(b) * nq * Hq * kD + i] = TO(0.f);
 }
 
 // The next piece [jbeg, jend) of segment (b, h) starting at position pos;
@@ -322,36 +346,35 @@ struct Lse {
   }
 };
 
-template <typename TO>
-__device__ inline void merge_segment(const DecodeArgs& a, Shared& sh, int b, int h, int S, int np,
-                                     const Units& um, int col0, int ncol) {
-  const int Hq = a.n_q_heads, G = Hq / a.pool.n_kv_heads;
+template <typename TO, class SH>
+__device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& om, int b, int h,
+                                     int S, int np, const Units& um, int col0, int ncol) {
+  const int NC = om.ncol();
   const int c0 = um.unit_of(S);
   const bool split_first = S != um.start(c0);
-  auto row_of = [&](int i) -> unsigned {  // workspace row of head 0 of piece i
-    return unsigned((c0 + i) * 2 + ((i == 0 && split_first) ? 1 : 0)) * unsigned(G);
+  auto row_of = [&](int i) -> unsigned {  // workspace row of column 0 of piece i
+    return unsigned((c0 + i) * 2 + ((i == 0 && split_first) ? 1 : 0)) * unsigned(NC);
   };
-  const unsigned rows = unsigned(um.total()) * 2u * unsigned(G);
+  const unsigned rows = unsigned(um.total()) * 2u * unsigned(NC);
   const __amdgpu_buffer_rsrc_t ro =
       __builtin_amdgcn_make_buffer_rsrc(a.ws_o, (short)0, int(rows * kD * 4), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rml =
       __builtin_amdgcn_make_buffer_rsrc(a.ws_ml, (short)0, int(rows * 8), kRsrcWord3);
-  constexpr int kCols = kD / 4;           // float4 columns of one head
-  const int F = ncol;                     // float4 columns merged here (multiple of kCols)
-  const int h0 = col0 / kCols, nh = F / kCols;
-  const int P = F >= 256 ? 1 : 256 / F;   // piece groups
-  const int Fc = F >= 256 ? 256 : F;
-  const int tid = threadIdx.x;
-  const int pg = tid / Fc, c = tid % Fc;
-  const int span = kMergeBatch * P;       // pieces per batch (span * nh <= 256 pairs)
+  constexpr int kCols = kD / 4;           // float4 columns of one output column
   float* red = &sh.o[0][0][0];            // [256][6]: m, l, o of each thread
-  float2* mls = reinterpret_cast<float2*>(red + 256 * 6);  // [span][nh] (max, sum) of the batch
+  float2* mls = reinterpret_cast<float2*>(red + 256 * 6);  // [span][nh] (max, sum) of a batch
   static_assert(256 * 6 + 2 * 256 <= kWaves * 16 * (kD + 1), "LDS reuse");
-  TO* out = static_cast<TO*>(a.out) + (size_t(b) * Hq + h * G) * kD;
-  for (int cc = c; cc < F; cc += Fc) {  // one trip unless F > 256 (two columns per thread)
-    const int col = col0 + cc;
-    const int hc = col / kCols;
-    const unsigned cb = unsigned(hc) * kD * 4u + unsigned(col % kCols) * 16u;
+  TO* out = static_cast<TO*>(a.out);
+  const int tid = threadIdx.x;
+  // float4 columns [col0, col0 + 32*ncol) in trips of at most 256
+  for (int base = col0 * kCols; base < (col0 + ncol) * kCols; base += 256) {
+    const int Ft = min(256, (col0 + ncol) * kCols - base);
+    const int P = 256 / Ft;               // piece groups
+    const int pg = tid / Ft, cc = base + tid % Ft;
+    const int h0 = base / kCols, nh = Ft / kCols;
+    const int span = kMergeBatch * P;     // pieces per batch (span * nh <= 96 pairs)
+    const int hc = cc / kCols;
+    const unsigned cb = unsigned(hc) * kD * 4u + unsigned(cc % kCols) * 16u;
     Lse r{-__builtin_inff(), 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
     for (int q0 = 0; q0 < np; q0 += span) {
       // one (max, sum) pair per thread, issued with this thread's partial sums
@@ -390,45 +413,54 @@ __device__ inline void merge_segment(const DecodeArgs& a, Shared& sh, int b, int
       e[4] = r.o[2];
       e[5] = r.o[3];
       __syncthreads();
-      if (tid < F) {
+      if (tid < Ft) {
         r = Lse{-__builtin_inff(), 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
         for (int g2 = 0; g2 < P; ++g2) {
-          const float* q = red + (g2 * Fc + tid) * 6;
+          const float* q = red + (g2 * Ft + tid) * 6;
           r.add(q[0], q[1], f32x4{q[2], q[3], q[4], q[5]});
         }
       }
+      __syncthreads();  // red is rewritten by the next trip
     }
     if (pg == 0) {
       const float inv = r.l > 0.f ? 1.f / r.l : 0.f;
+      TO* o = out + om.row(b, h, hc) * kD + (cc % kCols) * 4;
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) out[col * 4 + e2] = TO(r.o[e2] * inv);
+      for (int e2 = 0; e2 < 4; ++e2) o[e2] = TO(r.o[e2] * inv);
     }
   }
 }
 
-// Merge the 4 waves' (max, sum, acc) of one piece through LDS and write the
-// piece: normalized to `out` (type TO) when it is a whole segment, else as a
-// partial in slot `slot` of unit `unit`, counted on the segment's arrival
-// counter; the completing arrival merges the segment.  l_run must already be
-// summed over the lane groups.  S = the segment's start position, nb its
-// blocks.  Ends with a barrier (LDS is reused by the next piece).
-template <typename TO>
-__device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g, int c,
-                                   const f32x4 (&o)[kNT], float m_ref, float l_run, bool complete,
-                                   int slot, int unit, int b, int h, int S, int nb,
-                                   const Units& um) {
-  const int Hq = a.n_q_heads, G = Hq / a.pool.n_kv_heads;
+// A wave's (max, sum, acc) of its share of a piece for the 16 columns of one
+// tile into LDS (column col0 + c for lane (g, c)); l_run must already be
+// summed over the lane groups.
+template <class SH>
+__device__ inline void stash_piece(SH& sh, int w, int g, int col, const f32x4 (&o)[kNT], float m_ref,
+                                   float l_run) {
   if (g == 0) {
-    sh.m[w][c] = m_ref;
-    sh.l[w][c] = l_run;
+    sh.m[w][col] = m_ref;
+    sh.l[w][col] = l_run;
   }
 #pragma unroll
   for (int T_ = 0; T_ < kNT; ++T_)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sh.o[w][c][kNT * (4 * g + i) + T_] = o[T_][i];
+    for (int i = 0; i < 4; ++i) sh.o[w][col][kNT * (4 * g + i) + T_] = o[T_][i];
+}
+
+// Merge the 4 waves' stashed piece through LDS and write it: normalized to
+// `out` (type TO) when it is a whole segment, else as a partial in slot
+// `slot` of unit `unit`, counted on the segment's arrival counter; the
+// completing arrival merges the segment (unless the merge launch will).  S =
+// the segment's start position, nb its blocks.  Ends with a barrier (LDS is
+// reused by the next piece).
+template <typename TO, class SH>
+__device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& om, bool complete,
+                                    int slot, int unit, int b, int h, int S, int nb,
+                                    const Units& um) {
+  const int NC = om.ncol();
   __syncthreads();
   TO* out = static_cast<TO*>(a.out);
-  for (int idx = threadIdx.x; idx < G * kD; idx += kWaves * 64) {
+  for (int idx = threadIdx.x; idx < NC * kD; idx += kWaves * 64) {
     const int hc = idx / kD, d = idx % kD;
     float M = -__builtin_inff();
 #pragma unroll
@@ -436,15 +468,15 @@ __device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g
     float lsum = 0.f, osum = 0.f;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) {
-      if (sh.m[v][hc] == -__builtin_inff()) continue;  // wave saw no block
+      if (sh.m[v][hc] == -__builtin_inff()) continue;  // wave saw no block (or no visible token)
       const float wt = exp2f(sh.m[v][hc] - M);
       lsum += sh.l[v][hc] * wt;
       osum += sh.o[v][hc][d] * wt;
     }
     if (complete) {
-      out[(size_t(b) * Hq + h * G + hc) * kD + d] = TO(lsum > 0.f ? osum / lsum : 0.f);
+      out[om.row(b, h, hc) * kD + d] = TO(lsum > 0.f ? osum / lsum : 0.f);
     } else {
-      const size_t row = (size_t(unit) * 2 + slot) * G + hc;
+      const size_t row = (size_t(unit) * 2 + slot) * NC + hc;
       st_agent(&a.ws_o[row * kD + d], osum);
       if (d == 0) {
         st_agent(&a.ws_ml[row * 2], M);
@@ -459,9 +491,7 @@ __device__ inline void merge_piece(const DecodeArgs& a, Shared& sh, int w, int g
     __syncthreads();
     if (threadIdx.x == 0) sh.last = arrive(a, c0, np) ? 1 : 0;
     __syncthreads();
-    if (sh.last) {
-      merge_segment<TO>(a, sh, b, h, S, np, um, 0, G * (kD / 4));
-    }
+    if (sh.last) merge_segment<TO>(a, sh, om, b, h, S, np, um, 0, NC);
   }
   __syncthreads();
 }

@@ -8,7 +8,8 @@
 // written back (section 5, "On-the-Fly Register Dequantization").
 //
 // The generic kernel handles every dtype, head_dim and GQA ratio, one query
-// head per wavefront, one token at a time.  It is the path for fp32 pools and
+// head per wavefront, one token at a time, and the verify step's several
+// queries per sequence (each attending to the cache up to its own token).  It is the path for fp32 pools and
 // for shapes the matrix-core kernel does not take.  Both kernels share the
 // split/workspace contract: scores live in the log2 domain (scale folded with
 // log2 e), split s of sequence b writes (max, sum) and the unnormalized sum of
@@ -21,6 +22,15 @@ namespace pa {
 namespace {
 
 constexpr int kMaxDimPerLane = 4;  // head_dim <= 256
+
+// Tokens query qi of sequence b attends to: a verify step's n_query new tokens
+// are the last of the sequence's L cached tokens, and query qi sees the cache
+// up to and including its own token (causal among the new ones); decode is
+// n_query = 1 (all L tokens).
+__device__ inline int query_len(const DecodeArgs& a, int b, int qi) {
+  const int L = min(max(a.lens[b], 0), a.max_seq_len);
+  return max(0, L - max(a.n_query, 1) + 1 + qi);
+}
 
 __device__ inline void store_out(void* out, size_t i, float x, int dt) {
   if (dt == kF32)
@@ -66,13 +76,14 @@ __device__ inline float read_elem(const PoolDev& p, int id, int h, int t, int d,
 }
 
 __global__ __launch_bounds__(64) void decode_split_generic(DecodeArgs a) {
-  const int split = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int split = blockIdx.x, hq = blockIdx.y, r = blockIdx.z, lane = threadIdx.x;
   const PoolDev& p = a.pool;
   const int D = p.head_dim, Hq = a.n_q_heads, G = Hq / p.n_kv_heads, h = hq / G;
-  const int L = min(max(a.lens[b], 0), a.max_seq_len);
+  const int nq = max(a.n_query, 1), b = r / nq;
+  const int L = query_len(a, b, r % nq);
   const int nb = (L + 15) >> 4, S = a.split_blocks;
   const int j0 = split * S;
-  const size_t orow = (size_t(b) * Hq + hq) * D;
+  const size_t orow = (size_t(r) * Hq + hq) * D;
   if (j0 >= nb) {
     if (split == 0)
       for (int d = lane; d < D; d += 64) store_out(a.out, orow + d, 0.f, a.q_dtype);
@@ -121,7 +132,7 @@ __global__ __launch_bounds__(64) void decode_split_generic(DecodeArgs a) {
     }
     return;
   }
-  const size_t wrow = (size_t(b) * Hq + hq) * a.max_splits + split;
+  const size_t wrow = (size_t(r) * Hq + hq) * a.max_splits + split;
 #pragma unroll
   for (int m = 0; m < kMaxDimPerLane; ++m) {
     const int d = lane + 64 * m;
@@ -142,12 +153,13 @@ constexpr int kCombineChunk = 256;
 
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float wsh[kCombineChunk];
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int hq = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
   const int D = a.pool.head_dim, Hq = a.n_q_heads, S = a.split_blocks;
-  const int L = min(max(a.lens[b], 0), a.max_seq_len);
+  const int nq = max(a.n_query, 1);
+  const int L = query_len(a, r / nq, r % nq);
   const int nsplit = (((L + 15) >> 4) + S - 1) / S;
   if (nsplit <= 1) return;
-  const size_t row = (size_t(b) * Hq + hq) * a.max_splits;
+  const size_t row = (size_t(r) * Hq + hq) * a.max_splits;
   const float* ml = a.ws_ml + row * 2;
   const float ninf = -__builtin_inff();
   float M = ninf;
@@ -188,7 +200,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < kMaxDimPerLane; ++k) {
     const int d = lane + 64 * k;
-    if (d < D) store_out(a.out, (size_t(b) * Hq + hq) * D + d, acc[k], a.q_dtype);
+    if (d < D) store_out(a.out, (size_t(r) * Hq + hq) * D + d, acc[k], a.q_dtype);
   }
 }
 
@@ -197,11 +209,11 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
 hipError_t launch_decode_split_mfma16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_split_quant(const DecodeArgs& a, hipStream_t s);
 
-int occupancy_mfma16(int32_t kv_dtype);
+int occupancy_mfma16(int32_t kv_dtype, int nct);
 int occupancy_quant(int32_t kv_dtype);
 
-int decode_split_occupancy(int32_t kernel, int32_t kv_dtype) {
-  if (kernel == kKernMfma16) return occupancy_mfma16(kv_dtype);
+int decode_split_occupancy(int32_t kernel, int32_t kv_dtype, int nct) {
+  if (kernel == kKernMfma16) return occupancy_mfma16(kv_dtype, nct);
   if (kernel == kKernQuant) return occupancy_quant(kv_dtype);
   return 1;
 }
@@ -210,7 +222,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
   if (a.kernel == kKernMfma16) return a.max_splits > 0 ? launch_decode_split_mfma16(a, s) : hipSuccess;
   if (a.kernel == kKernQuant) return a.max_splits > 0 ? launch_decode_split_quant(a, s) : hipSuccess;
-  dim3 grid(unsigned(a.max_splits), unsigned(a.n_q_heads), unsigned(a.batch));
+  dim3 grid(unsigned(a.max_splits), unsigned(a.n_q_heads), unsigned(a.batch) * unsigned(max(a.n_query, 1)));
   hipLaunchKernelGGL(decode_split_generic, grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
@@ -222,7 +234,7 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s) {
   if (a.kernel == kKernMfma16 || a.kernel == kKernQuant)
     return a.defer_merge ? launch_decode_merge(a, s) : hipSuccess;
   if (a.max_splits <= 1) return hipSuccess;
-  dim3 grid(unsigned(a.n_q_heads), unsigned(a.batch));
+  dim3 grid(unsigned(a.n_q_heads), unsigned(a.batch) * unsigned(max(a.n_query, 1)));
   hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }

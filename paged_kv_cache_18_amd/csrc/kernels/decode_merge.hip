@@ -3,10 +3,11 @@
 // (defer_merge = 1; chosen when segments span many workgroups, so that one
 // merge per segment would leave a long serial tail at the end of the split).
 //
-// One workgroup per (sequence b, KV head h, query head c of the group): it
-// rebuilds the work-list cut from the lengths exactly as the split kernel
-// did, finds the segment's pieces and folds the 32 16-byte columns of head c
-// over them (decode_common.hpp, merge_segment), in list order.  A segment of
+// One workgroup per (sequence b, KV head h, output column c: query head of the
+// group, times the query of a verify step): it rebuilds the work-list cut from
+// the lengths exactly as the split kernel did, finds the segment's pieces and
+// folds the 32 16-byte columns of column c over them (decode_common.hpp,
+// merge_segment), in list order.  A segment of
 // one piece was written by the split kernel and is skipped.
 #include "decode_common.hpp"
 
@@ -19,8 +20,9 @@ using namespace dec;
 template <typename TO>
 __global__ __launch_bounds__(kWaves * 64) void decode_merge_kernel(DecodeArgs a) {
   __shared__ Shared sh;
-  const int H = a.pool.n_kv_heads, G = a.n_q_heads / H;
-  const int hc = int(blockIdx.x) % G, bh = int(blockIdx.x) / G;
+  const int H = a.pool.n_kv_heads;
+  const OutMap om = out_map(a);
+  const int hc = int(blockIdx.x) % om.ncol(), bh = int(blockIdx.x) / om.ncol();
   const int b = bh / H, h = bh % H;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -30,14 +32,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_merge_kernel(DecodeArgs a)
   const int S = seq_start(a, b, lane) + h * nb;  // every wave computes it
   const int np = um.unit_of(S + nb - 1) - um.unit_of(S) + 1;
   if (np <= 1) return;
-  merge_segment<TO>(a, sh, b, h, S, np, um, hc * (kD / 4), kD / 4);
+  merge_segment<TO>(a, sh, om, b, h, S, np, um, hc, 1);
 }
 
 }  // namespace
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
-  const int G = a.n_q_heads / a.pool.n_kv_heads;
-  const dim3 grid(unsigned(a.batch) * unsigned(a.pool.n_kv_heads) * unsigned(G));
+  const int ncol = max(a.n_query, 1) * (a.n_q_heads / a.pool.n_kv_heads);
+  const dim3 grid(unsigned(a.batch) * unsigned(a.pool.n_kv_heads) * unsigned(ncol));
   if (a.q_dtype == kBF16)
     hipLaunchKernelGGL(decode_merge_kernel<__bf16>, grid, dim3(kWaves * 64), 0, s, a);
   else

@@ -58,17 +58,24 @@ using namespace dec;
 // NB register buffers per wave: NB - 1 blocks in flight while one is
 // consumed.  NB = 2 fits three waves per SIMD (12 per compute unit); deeper
 // pipelines trade waves for blocks in flight per wave.
-template <typename T, int NB>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 3 : 2))) void decode_split_mfma16(DecodeArgs a) {
+//
+// NCT column tiles of 16 and CAUSAL: decode packs the G query heads of a KV
+// head into one tile; the verify step packs n_query x G (query, head) columns
+// into one or two tiles and masks, per column, the tokens after its own
+// query's position (causal among the step's new tokens).
+template <typename T, int NB, int NCT, bool CAUSAL>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 && !CAUSAL ? 3 : 2))) void decode_split_mfma16(DecodeArgs a) {
   typedef typename Mfma<T>::v8 v8;
   typedef typename Mfma<T>::v4 v4;
-  __shared__ Shared sh;
+  __shared__ SharedT<16 * NCT> sh;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4, c = lane & 15;
   const PoolDev& p = a.pool;
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H;
+  const OutMap om = out_map(a);
+  const int nq = om.nq, ncol = om.ncol();
   zero_empty_rows<T>(a);
   const Units um = setup_units(a, sh, w, lane);
   int b = 0, fb = 0;
@@ -81,11 +88,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   // per-piece state, captured by the lambdas below
   int h = 0, L = 0;
   const int32_t* trow = a.tables;
-  v8 qf[4];
-  f32x4 o[kNT];
-  // Running statistics per lane (= per packed head c): m_ref is the reference
-  // the weights are taken against, l_run the running sum of weights.
-  float m_ref = -__builtin_inff(), l_run = 0.f;
+  v8 qf[NCT][4];
+  f32x4 o[NCT][kNT];
+  // Running statistics per lane and tile (= per packed column): m_ref is the
+  // reference the weights are taken against, l_run the running sum of weights.
+  float m_ref[NCT], l_run[NCT];
+  int lim[NCT];  // CAUSAL: last position column 16t + c may see
 
   // K/V of one block into registers (8 x 16-byte loads, 1 KiB contiguous per
   // load across the wave).  The loads are issued unconditionally -- an
@@ -103,70 +111,73 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   };
   auto ok = [&](int id) { return id >= 0 && id < nbk; };
 
-  // One block: S^T = K Q^T, online softmax, O^T += V^T P^T.  `valid` tokens
-  // of the block count (0 for a skipped table entry: every weight is zero).
-  // It always runs, so every load is waited on along every path.
-  auto consume = [&](int valid, const v8(&kf)[4], v8(&vf)[4]) {
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  // One block (logical index jl): S^T = K Q^T, online softmax, O^T += V^T
+  // P^T.  `valid` tokens of the block count (0 for a skipped table entry:
+  // every weight is zero).  It always runs, so every load is waited on along
+  // every path.
+  auto consume = [&](int valid, int jl, const v8(&kf)[4], v8(&vf)[4]) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) sc = Mfma<T>::qk(kf[kk], qf[kk], sc);
-    float x[4];
-    float bm = -__builtin_inff();
+    for (int t = 0; t < NCT; ++t) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (4 * g + i < valid) ? sc[i] * sl2 : -__builtin_inff();
-      bm = fmaxf(bm, x[i]);
-    }
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    // The reference only moves when a block's max exceeds it by more than 8
-    // (weights stay <= 2^8, far inside fp32 and the two-part 16-bit split),
-    // so the accumulators are rarely rescaled.  The result is unchanged:
-    // numerator and denominator share the reference.
-    const bool move = bm > m_ref + 8.f;
-    if (__any(move)) {
-      const float m_new = move ? bm : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_run *= alpha;
+      for (int kk = 0; kk < 4; ++kk) sc = Mfma<T>::qk(kf[kk], qf[t][kk], sc);
+      float x[4];
+      bool vis[4];
+      float bm = -__builtin_inff();
 #pragma unroll
-      for (int T_ = 0; T_ < kNT; ++T_) o[T_] *= alpha;
-      m_ref = m_new;
-    }
-    float pw[4];
+      for (int i = 0; i < 4; ++i) {
+        vis[i] = 4 * g + i < valid;
+        if constexpr (CAUSAL) vis[i] = vis[i] && 16 * jl + 4 * g + i <= lim[t];
+        x[i] = vis[i] ? sc[i] * sl2 : -__builtin_inff();
+        bm = fmaxf(bm, x[i]);
+      }
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      // The reference only moves when a block's max exceeds it by more than 8
+      // (weights stay <= 2^8, far inside fp32 and the two-part 16-bit split),
+      // so the accumulators are rarely rescaled.  The result is unchanged:
+      // numerator and denominator share the reference.
+      const bool move = bm > m_ref[t] + 8.f;
+      if (__any(move)) {
+        const float m_new = move ? bm : m_ref[t];
+        const float alpha = __builtin_amdgcn_exp2f(m_ref[t] - m_new);
+        l_run[t] *= alpha;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pw[i] = (4 * g + i < valid) ? __builtin_amdgcn_exp2f(x[i] - m_ref) : 0.f;
-      l_run += pw[i];
-    }
-    if (valid < 16) {
-      // Unwritten tail slots may hold anything (even NaN bit patterns): zero
-      // them so a zero weight cannot meet a NaN.  Each dword holds two tokens.
-      const int t0 = 4 * g;
-      const uint32_t m01 = (t0 + 0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
-      const uint32_t m23 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+        for (int T_ = 0; T_ < kNT; ++T_) o[t][T_] *= alpha;
+        m_ref[t] = m_new;
+      }
+      if (t == 0 && valid < 16) {
+        // Unwritten tail slots may hold anything (even NaN bit patterns): zero
+        // them so a zero weight cannot meet a NaN.  Each dword holds two tokens.
+        const int t0 = 4 * g;
+        const uint32_t m01 = (t0 + 0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
+        const uint32_t m23 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          u32x4 dw = __builtin_bit_cast(u32x4, vf[u]);
+          dw[0] &= m01;
+          dw[1] &= m23;
+          dw[2] &= m01;
+          dw[3] &= m23;
+          vf[u] = __builtin_bit_cast(v8, dw);
+        }
+      }
+      v4 phi, plo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pw = vis[i] ? __builtin_amdgcn_exp2f(x[i] - m_ref[t]) : 0.f;
+        l_run[t] += pw;
+        phi[i] = T(pw);
+        plo[i] = T(pw - float(phi[i]));
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        u32x4 dw = __builtin_bit_cast(u32x4, vf[u]);
-        dw[0] &= m01;
-        dw[1] &= m23;
-        dw[2] &= m01;
-        dw[3] &= m23;
-        vf[u] = __builtin_bit_cast(v8, dw);
-      }
-    }
-    v4 phi, plo;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      phi[i] = T(pw[i]);
-      plo[i] = T(pw[i] - float(phi[i]));
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int par = 0; par < 2; ++par) {
-        v4 vt = {vf[u][4 * par + 0], vf[u][4 * par + 1], vf[u][4 * par + 2], vf[u][4 * par + 3]};
-        o[2 * u + par] = Mfma<T>::pv(vt, phi, o[2 * u + par]);
-        o[2 * u + par] = Mfma<T>::pv(vt, plo, o[2 * u + par]);
+        for (int par = 0; par < 2; ++par) {
+          v4 vt = {vf[u][4 * par + 0], vf[u][4 * par + 1], vf[u][4 * par + 2], vf[u][4 * par + 3]};
+          o[t][2 * u + par] = Mfma<T>::pv(vt, phi, o[t][2 * u + par]);
+          o[t][2 * u + par] = Mfma<T>::pv(vt, plo, o[t][2 * u + par]);
+        }
       }
     }
   };
@@ -185,16 +196,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   while (next_piece(a, pos, pos1, b, fb, h, jbeg, jend, nb)) {
     L = seq_len(a, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
-    {
-      // Q^T fragment: lane (g, c) holds Q[h*G + c][32kk + 8g .. +7], zero for c >= G.
-      const T* qp = static_cast<const T*>(a.q) + (size_t(b) * Hq + h * G + c) * kD + 8 * g;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qf[kk] = c < G ? *reinterpret_cast<const v8*>(qp + 32 * kk) : v8{};
+    for (int t = 0; t < NCT; ++t) {
+      // Q^T fragment: lane (g, c) of tile t holds column col = 16t + c, i.e.
+      // Q[query col / G][head h*G + col % G][32kk + 8g .. +7]; zero past the
+      // last column
+      const int col = 16 * t + c, qi = col / G;
+      const T* qp = static_cast<const T*>(a.q) + om.row(b, h, col) * kD + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qf[t][kk] = col < ncol ? *reinterpret_cast<const v8*>(qp + 32 * kk) : v8{};
+      lim[t] = L - nq + qi;
+#pragma unroll
+      for (int T_ = 0; T_ < kNT; ++T_) o[t][T_] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_ref[t] = -__builtin_inff();
+      l_run[t] = 0.f;
     }
-#pragma unroll
-    for (int T_ = 0; T_ < kNT; ++T_) o[T_] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_ref = -__builtin_inff();
-    l_run = 0.f;
 
     // Software pipeline over this wave's blocks jw+4k, k = 0..n-1: the loads
     // of blocks k+1 .. k+NB-1 are in flight while block k is consumed.  The
@@ -221,19 +238,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
           const int nxt = (s + NB - 1) % NB;
           ids[nxt] = id_of(k + s + NB - 1);
           fetch(ids[nxt], kb[nxt], vb[nxt]);
-          consume(valid_of(k + s, ids[s]), kb[s], vb[s]);
+          consume(valid_of(k + s, ids[s]), jw + kWaves * (k + s), kb[s], vb[s]);
         }
       }
 #pragma unroll
       for (int s = 0; s < NB - 1; ++s)
-        if (k + s < n) consume(valid_of(k + s, ids[s]), kb[s], vb[s]);
+        if (k + s < n) consume(valid_of(k + s, ids[s]), jw + kWaves * (k + s), kb[s], vb[s]);
     }
 
     // ---- merge the 4 waves of this piece, write it -----------------------------
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-    merge_piece<T>(a, sh, w, g, c, o, m_ref, l_run, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, h,
-                   fb + h * nb, nb, um);
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) {
+      l_run[t] += __shfl_xor(l_run[t], 16, 64);
+      l_run[t] += __shfl_xor(l_run[t], 32, 64);
+      stash_piece(sh, w, g, 16 * t + c, o[t], m_ref[t], l_run[t]);
+    }
+    finish_piece<T>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, h, fb + h * nb,
+                    nb, um);
     pos += jend - jbeg;
     first = false;
   }
@@ -254,23 +275,36 @@ int mfma_nb() {
 template <typename T>
 hipError_t launch_nb(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.max_splits)), block(kWaves * 64);
+  if (a.n_query > 1) {  // the verify step: one or two column tiles, causal
+    const int ncol = a.n_query * (a.n_q_heads / a.pool.n_kv_heads);
+    if (ncol <= 16)
+      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 2, true>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   switch (mfma_nb()) {
-    case 3: hipLaunchKernelGGL((decode_split_mfma16<T, 3>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_mfma16<T, 4>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_split_mfma16<T, 2>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_split_mfma16<T, 3, 1, false>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_mfma16<T, 4, 1, false>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, false>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
 
 template <typename T>
-int occupancy_nb() {
+int occupancy_nb(int nct) {
   int n = 0;
   hipError_t e;
-  switch (mfma_nb()) {
-    case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 3>, kWaves * 64, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 4>, kWaves * 64, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2>, kWaves * 64, 0); break;
-  }
+  if (nct == 2)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 2, true>, kWaves * 64, 0);
+  else if (nct == 1)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 1, true>, kWaves * 64, 0);
+  else
+    switch (mfma_nb()) {
+      case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 3, 1, false>, kWaves * 64, 0); break;
+      case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 4, 1, false>, kWaves * 64, 0); break;
+      default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 1, false>, kWaves * 64, 0); break;
+    }
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 
@@ -280,11 +314,12 @@ hipError_t launch_decode_split_mfma16(const DecodeArgs& a, hipStream_t s) {
   return a.pool.kv_dtype == kBF16 ? launch_nb<__bf16>(a, s) : launch_nb<_Float16>(a, s);
 }
 
-int occupancy_mfma16(int32_t kv_dtype) {
-  static int cache[2] = {0, 0};
+// nct: 0 = decode, 1 or 2 = verify step with that many column tiles.
+int occupancy_mfma16(int32_t kv_dtype, int nct) {
+  static int cache[2][3] = {{0, 0, 0}, {0, 0, 0}};
   const int i = kv_dtype == kBF16 ? 0 : 1;
-  if (cache[i] == 0) cache[i] = i == 0 ? occupancy_nb<__bf16>() : occupancy_nb<_Float16>();
-  return cache[i];
+  if (cache[i][nct] == 0) cache[i][nct] = i == 0 ? occupancy_nb<__bf16>(nct) : occupancy_nb<_Float16>(nct);
+  return cache[i][nct];
 }
 
 }  // namespace pa

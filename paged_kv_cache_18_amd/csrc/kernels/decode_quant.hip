@@ -359,8 +359,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
 #pragma unroll
       for (int T_ = 0; T_ < kNT; ++T_) o[T_] -= corr;
     }
-    merge_piece<_Float16>(a, sh, w, g, c, o, m_ref, l_run, jbeg == 0 && jend == nb,
-                          first ? 0 : 1, unit, b, h, fb + h * nb, nb, um);
+    stash_piece(sh, w, g, c, o, m_ref, l_run);
+    finish_piece<_Float16>(a, sh, out_map(a), jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, h,
+                      fb + h * nb, nb, um);
     pos += jend - jbeg;
     first = false;
   }

@@ -31,6 +31,7 @@ struct DecodeArgs {
   const int32_t* tables;
   const int32_t* lens;
   int32_t batch, n_q_heads, q_dtype, max_blocks_per_seq, max_seq_len;
+  int32_t n_query;        // queries per sequence: 1 (decode) or the verify step's gamma + 1
   float scale_log2;      // softmax scale * log2(e): scores live in the log2 domain
   void* out;
   float* ws_o;           // [batch][n_q_heads][max_splits][head_dim] partial sums
@@ -52,7 +53,8 @@ struct DecodeArgs {
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
 // Resident workgroups per compute unit of the split kernel `kernel` for a pool
 // of kv_dtype (from the runtime's occupancy calculator; cached).
-int decode_split_occupancy(int32_t kernel, int32_t kv_dtype);
+// nct: 0 for decode, else the verify step's column tiles (1 or 2).
+int decode_split_occupancy(int32_t kernel, int32_t kv_dtype, int nct);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 // Merge launch of the matrix-core kernels (defer_merge = 1).
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);

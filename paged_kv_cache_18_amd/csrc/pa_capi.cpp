@@ -159,17 +159,19 @@ int64_t flat_upper(int32_t batch, int32_t hkv, int32_t max_seq_len) {
   return int64_t(batch) * hkv * ((int64_t(max_seq_len) + 15) / 16);
 }
 
+// n_query: queries per sequence (1 = decode; the verify step's gamma + 1).
 Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
-               int32_t q_dtype) {
+               int32_t q_dtype, int32_t n_query = 1) {
   const pa::Desc& d = p->core.desc();
   Plan pl{};
   const int32_t G = n_q_heads / d.n_kv_heads;
+  const int32_t ncol = n_query * G;  // output columns per (sequence, kv head)
   const bool mfma_ok = (d.kv_dtype == pa::kBF16 || d.kv_dtype == pa::kF16) &&
-                       q_dtype == d.kv_dtype && d.head_dim == 128 && G <= 16 &&
-                       d.num_sink_blocks == 0;
+                       q_dtype == d.kv_dtype && d.head_dim == 128 &&
+                       (n_query == 1 ? G <= 16 : ncol <= 32) && d.num_sink_blocks == 0;
   const bool quant_ok = ((d.kv_dtype == pa::kInt4 && d.group_size == d.head_dim) ||
                          d.kv_dtype == pa::kFp8) &&
-                        q_dtype == pa::kF16 && d.head_dim == 128 && G <= 16;
+                        q_dtype == pa::kF16 && d.head_dim == 128 && G <= 16 && n_query == 1;
   const char* force = std::getenv("PA_DECODE_KERNEL");  // "generic" forces the VALU kernel
   const bool generic = force && std::strcmp(force, "generic") == 0;
   pl.kernel = generic ? pa::kKernGeneric
@@ -194,7 +196,8 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
       // the actual lengths
       pl.split_blocks = 0;
       int per_cu = env_int("PA_WG_PER_CU", 0);  // tuning knob; default: resident slots
-      if (per_cu <= 0) per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype);
+      if (per_cu <= 0)
+        per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype, n_query == 1 ? 0 : ncol <= 16 ? 1 : 2);
       pl.max_splits = int32_t(std::max<int64_t>(
           1, std::min<int64_t>({w, int64_t(cu_count()) * per_cu, int64_t(kCtrCap / 2)})));
       // queued units: the owner streams static_permille/1000 of its region,
@@ -219,8 +222,7 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
     const int64_t segs = std::max<int64_t>(1, int64_t(batch) * d.n_kv_heads);
     const int fuse_max = env_int("PA_FUSE_MAX_PIECES", kFuseMaxPieces);
     pl.defer_merge = units / segs + 1 > fuse_max ? 1 : 0;
-    const size_t g = size_t(n_q_heads / d.n_kv_heads);
-    const size_t rows = size_t(units) * 2 * g;
+    const size_t rows = size_t(units) * 2 * size_t(ncol);
     pl.ws_o_offset = kCtrBytes;
     pl.ws_ml_offset = rows * size_t(d.head_dim);
     pl.ws_bytes = kCtrBytes + rows * (size_t(d.head_dim) + 2) * sizeof(float);
@@ -228,7 +230,7 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
   }
   pl.split_blocks = plan_split_blocks(batch, d.n_kv_heads, max_seq_len);
   pl.max_splits = int32_t(std::max<int64_t>(1, (nb + pl.split_blocks - 1) / pl.split_blocks));
-  const size_t rows = size_t(batch) * size_t(n_q_heads) * size_t(pl.max_splits);
+  const size_t rows = size_t(batch) * size_t(n_query) * size_t(n_q_heads) * size_t(pl.max_splits);
   pl.ws_o_offset = kCtrBytes;  // partials never overwrite the counters
   pl.ws_ml_offset = rows * size_t(d.head_dim);
   pl.ws_bytes = pl.max_splits > 1 ? kCtrBytes + rows * (size_t(d.head_dim) + 2) * sizeof(float) : 0;
@@ -246,13 +248,16 @@ void check_shapes(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t ma
 
 enum Phase { kBoth = 3, kSplit = 1, kCombine = 2 };
 
+constexpr int32_t kMaxQueries = 64;  // verify step: queries per sequence, at most
+
 pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* tables,
                  const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t q_dtype,
                  int32_t max_blocks, int32_t max_seq_len, float scale, void* out, void* ws,
-                 size_t ws_bytes, void* stream) {
+                 size_t ws_bytes, void* stream, int32_t n_query = 1) {
   return guard([&] {
     need_device(pool);
     check_shapes(pool, batch, n_q_heads, max_seq_len);
+    if (n_query < 1 || n_query > kMaxQueries) fail(pa::kInvalidArg, "n_query must be in [1, 64]");
     const pa::Desc& d = pool->core.desc();
     if (pa::is_raw(d.kv_dtype)) {
       if (q_dtype != d.kv_dtype) fail(pa::kInvalidArg, "q_dtype must equal the pool's kv_dtype");
@@ -268,7 +273,9 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     need(tables, "block_tables_dev");
     need(lens, "seq_lens_dev");
     need(out, "out");
-    const Plan pl = make_plan(pool, batch, n_q_heads, max_seq_len, q_dtype);
+    const Plan pl = make_plan(pool, batch, n_q_heads, max_seq_len, q_dtype, n_query);
+    if (pl.kernel == pa::kKernGeneric && int64_t(batch) * n_query > 65535)
+      fail(pa::kUnsupported, "batch * n_query above 65535 on the generic kernel");
     if (pl.ws_bytes > 0) {
       need(ws, "workspace");
       if (ws_bytes < pl.ws_bytes)
@@ -285,6 +292,7 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     a.q_dtype = q_dtype;
     a.max_blocks_per_seq = max_blocks;
     a.max_seq_len = max_seq_len;
+    a.n_query = n_query;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out = out;
     if (pl.ws_bytes) {
@@ -561,6 +569,27 @@ pa_status pa_decode_combine(const void* q, const pa_pool* pool, const int32_t* t
                             void* ws, size_t ws_bytes, void* stream) {
   return decode(kCombine, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks,
                 max_seq_len, scale, out, ws, ws_bytes, stream);
+}
+
+pa_status pa_verify_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
+                                    int32_t n_query, int32_t max_seq_len, size_t* bytes) {
+  return guard([&] {
+    check_shapes(pool, batch, n_q_heads, max_seq_len);
+    need(bytes, "bytes");
+    if (n_query < 1 || n_query > kMaxQueries) fail(pa::kInvalidArg, "n_query must be in [1, 64]");
+    const pa::Desc& d = pool->core.desc();
+    const int32_t qdt = pa::is_raw(d.kv_dtype) ? d.kv_dtype : int32_t(pa::kF16);
+    *bytes = make_plan(pool, batch, n_q_heads, max_seq_len, qdt, n_query).ws_bytes;
+  });
+}
+
+pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t* tables,
+                              const int32_t* lens, int32_t batch, int32_t n_q_heads,
+                              int32_t n_query, int32_t q_dtype, int32_t max_blocks,
+                              int32_t max_seq_len, float scale, void* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return decode(kBoth, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
+                scale, out, ws, ws_bytes, stream, n_query);
 }
 
 pa_status pa_stream_read(const void* src, size_t bytes, void* sink, void* stream) {

@@ -15,7 +15,9 @@ Recipe (one ``numpy.random.default_rng`` stream per purpose, keyed by
 * tag 3: Q (``[B][Hq][D]``);
 * tag 4: the outlier channels of the mixed-precision workload;
 * tag 5: the free-order permutation of the sink arena;
-* tag 6: K of appended decode tokens (index = step), tag 106: their V.
+* tag 6: K of appended decode tokens (index = step), tag 106: their V;
+* tag 7: the queries of a speculative verify step (index = queries per
+  sequence, shape ``[B][n_query][Hq][D]``).
 
 A ``reserve`` of n tokens on a sequence of length L writes tokens
 ``[L, L+n)`` of that sequence's logical content (``Workload.seq_tokens``); a
@@ -76,6 +78,11 @@ class Workload:
     def q(self):
         return rng(self.seed, 3).standard_normal(
             (self.batch, self.n_q_heads, self.head_dim), dtype=np.float32)
+
+    def q_verify(self, n_query):
+        """Queries of a verify step over the last n_query cached tokens."""
+        return rng(self.seed, 7, n_query).standard_normal(
+            (self.batch, n_query, self.n_q_heads, self.head_dim), dtype=np.float32)
 
     def kv_chunk(self, tag, index, count):
         """K and V (float32 [count][Hkv][D]) of one source chunk."""

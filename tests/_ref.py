@@ -74,6 +74,20 @@ def expected(wl, seqs=None, pairs=None):
     return out
 
 
+def expected_verify(wl, n_query, seqs=None, rows=None):
+    """Oracle verify-step outputs [B][n_query][Hq][D] (float64); with ``rows``
+    = list of b only those sequences are computed (others NaN)."""
+    seqs = wl.decode_seqs if seqs is None else seqs
+    q = cast64(wl.q_verify(n_query), wl.q_dtype)
+    out = np.full((len(seqs), n_query, wl.n_q_heads, wl.head_dim), np.nan)
+    for b, sid in enumerate(seqs):
+        if rows is not None and b not in rows:
+            continue
+        K, V, _ = stored_values(wl, sid)
+        out[b] = AT.verify_attention_one(q[b], K, V, wl.scale)
+    return out
+
+
 def tolerance(ref, out_dtype):
     """1e-5 for fp32 outputs; 2e-3 for 16-bit/quantized outputs, plus half an
     ulp of the output dtype (the single final rounding the output stores)."""

@@ -323,3 +323,108 @@ def test_workspace_reuse_across_calls_and_shapes():
                 else:
                     assert_close(o, expected(wl), "bf16", f"{key} split {split}")
                     outs[(key, split)] = o
+
+
+# ---- speculative verify step: gamma + 1 queries per sequence, causal -----------
+def run_verify(wl, nq, env=None):
+    """Prefill through the library, run one verify step over each sequence's
+    last nq cached tokens; returns (kv, out float64 [B][nq][Hq][D])."""
+    from _ref import cast64
+    log(f"[gpu] verify {wl.name} B={wl.batch} nq={nq} kv={wl.kv_dtype} env={env}")
+    old = {}
+    for k, v in (env or {}).items():
+        old[k] = os.environ.get(k)
+        os.environ[k] = v
+    try:
+        kv = PagedKV(wl, DEV)
+        kv.replay()
+        tdev, ldev, t, l = kv.device_tables()
+        q = torch.from_numpy(wl.q_verify(nq)).to(TORCH_DT[wl.q_dtype]).to(DEV)
+        max_len = int(max(l.max(), 1))
+        bq = q.shape[0]
+        out_full = torch.full((bq + 1, nq, wl.n_q_heads, wl.head_dim), 7.0, dtype=q.dtype,
+                              device=DEV)
+        need = B.pa_verify_workspace_bytes(kv.pool, bq, wl.n_q_heads, nq, max_len)
+        ws = torch.full((need + 4096,), 0xAB, dtype=torch.uint8, device=DEV)
+        ws[:need] = 0
+        B.pa_verify_attention(q, kv.pool, tdev, ldev, bq, wl.n_q_heads, nq, wl.q_dtype,
+                              tdev.shape[1], max_len, wl.scale, out_full[:bq], ws, ws.numel(),
+                              kv.stream())
+        torch.cuda.synchronize()
+        assert torch.all(out_full[bq] == 7.0), "write past out"
+        assert torch.all(ws[need:] == 0xAB), "write past workspace"
+        return kv, out_full[:bq].to(torch.float64).cpu().numpy()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+VERIFY_LENS = [1, 5, 6, 7, 16, 17, 100, 1000, 2500]
+
+
+@pytest.mark.parametrize("hq,hkv,nq,dt", [(32, 8, 6, "bf16"), (16, 8, 6, "bf16"), (32, 8, 4, "f16"),
+                                          (64, 8, 4, "bf16"), (8, 8, 6, "bf16")])
+def test_verify_matrix_core_matches_oracle(hq, hkv, nq, dt):
+    """Matrix-core verify (one or two 16-column tiles of (query, head)
+    columns), lengths around the block edges and below n_query."""
+    from _ref import expected_verify
+    wl = W.from_lengths(VERIFY_LENS, hq, hkv, 128, dt, seed=91 + nq + hq)
+    _, out = run_verify(wl, nq)
+    assert_close(out, expected_verify(wl, nq), dt, f"verify {hq}/{hkv} nq={nq} {dt}")
+
+
+@pytest.mark.parametrize("kvdt", ["f32", "int4", "fp8"])
+def test_verify_generic_matches_oracle(kvdt):
+    from _ref import expected_verify
+    if kvdt == "f32":
+        wl = W.from_lengths([1, 3, 4, 33, 300], 4, 4, 64, "f32", seed=95)
+        nq, odt = 3, "f32"
+    else:
+        wl = W.from_lengths([2, 6, 40, 700], 32, 8, 128, kvdt, seed=96,
+                            group=128 if kvdt == "int4" else 0, sink=True, outliers=True)
+        nq, odt = 6, "f16"
+    _, out = run_verify(wl, nq)
+    assert_close(out, expected_verify(wl, nq), odt, f"verify generic {kvdt}")
+
+
+@pytest.mark.parametrize("qenv", [{"PA_SPLIT_BLOCKS": "1"}, {"PA_SPLIT_BLOCKS": "3"},
+                                  {"PA_FUSE_MAX_PIECES": "1"}, QUEUE_ENVS[0], QUEUE_ENVS[4],
+                                  {"PA_DECODE_KERNEL": "generic"}])
+def test_verify_split_and_merge_modes(qenv):
+    from _ref import expected_verify
+    wl = W.from_lengths(VERIFY_LENS, 32, 8, 128, "bf16", seed=97)
+    _, out_a = run_verify(wl, 6, env=qenv)
+    _, out_b = run_verify(wl, 6, env=qenv)
+    assert np.array_equal(out_a, out_b), f"{qenv}: not deterministic"
+    assert_close(out_a, expected_verify(wl, 6), "bf16", f"verify {qenv}")
+
+
+def test_verify_one_query_is_decode():
+    wl = W.from_lengths([300, 17, 1], 32, 8, 128, "bf16", seed=98)
+    kv, out_d, t, l = run(wl)
+    kv2 = PagedKV(wl, DEV)
+    kv2.replay()
+    tdev, ldev, _, _ = kv2.device_tables()
+    q = torch.from_numpy(wl.q()).to(torch.bfloat16).to(DEV)[:, None]
+    out = torch.empty_like(q)
+    ml = int(l.max())
+    need = B.pa_verify_workspace_bytes(kv2.pool, wl.batch, wl.n_q_heads, 1, ml)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV)
+    B.pa_verify_attention(q, kv2.pool, tdev, ldev, wl.batch, wl.n_q_heads, 1, "bf16", tdev.shape[1],
+                          ml, wl.scale, out, ws, ws.numel(), kv2.stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(out[:, 0].double().cpu().numpy(), out_d)
+
+
+def test_verify_full_llama3_8b_sampled():
+    """The Llama-3-8B-shaped batch with gamma = 5 (6 queries per sequence):
+    12 sampled sequences against the oracle."""
+    from _ref import expected_verify
+    wl = W.llama3_8b()
+    _, out = run_verify(wl, 6)
+    rows = list(np.random.default_rng(7).choice(wl.batch, 12, replace=False))
+    ref = expected_verify(wl, 6, rows=rows)
+    assert_close(out, ref, "bf16", "verify llama3-8b sampled")
