@@ -136,6 +136,41 @@ def test_random_op_logs_match_oracle(libpa, seed):
     assert_same(kv, oracle, res_lib, res_or)
 
 
+def _spec_ops(rnd, n_seq, steps, gamma):
+    """Speculative decoding op log: prefill, a fork sharing a partial tail,
+    then steps that reserve gamma + 1 tokens per sequence and truncate the
+    rejected ones (8GB page, section 5 flowchart: rollback of the tail)."""
+    ops, lens = [], []
+    for s in range(n_seq):
+        L = rnd.randrange(1, 60)
+        ops += [("create",), ("reserve", s, L)]
+        lens.append(L)
+    ops.append(("fork", 0))
+    lens.append(lens[0])
+    for _ in range(steps):
+        for s in range(len(lens)):
+            ops.append(("reserve", s, gamma + 1))
+            acc = rnd.randrange(gamma + 2)          # accepted draft tokens + the target's token
+            lens[s] += acc
+            ops.append(("truncate", s, lens[s]))
+    return ops
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_speculative_rollback_op_logs_match_oracle(libpa, seed):
+    rnd = random.Random(100 + seed)
+    wl = W.tiny()
+    wl.num_blocks = 64
+    wl.body_free_order = np.array(rnd.sample(range(64), 64))
+    ops = _spec_ops(rnd, 3, 8, 5)
+    kv = PagedKV(wl, device=None)
+    res_lib = kv.replay(ops, write=False)
+    oracle = Pool(64, body_free_order=wl.body_free_order)
+    res_or = replay(oracle, ops)
+    assert_same(kv, oracle, res_lib, res_or)
+    assert B.pa_num_free(kv.pool, 0) == oracle.num_free(0)
+
+
 @pytest.mark.parametrize("kv_dtype,D,g,N,S", [
     ("f32", 64, 0, 64, 0), ("bf16", 128, 0, 10171, 0), ("f16", 32, 0, 5, 0),
     ("int4", 128, 128, 4509, 1), ("int4", 128, 64, 100, 3), ("int4", 256, 32, 7, 0),
