@@ -47,7 +47,11 @@ WORKLOADS = {
                      "heads, head_dim 128, bf16",
     "shared-prefix-partial": "shared prefix (1,992-token prompt, one CoW clone per writing fork), 64 q / "
                              "8 kv heads, head_dim 128, bf16",
+    "spec-verify": "speculative verify step (gamma = 5: 6 causal queries per sequence) on the "
+                   "Llama-3-8B-shaped batch: 64 sequences, lengths U[512,4096], 32 q / 8 kv heads, "
+                   "head_dim 128, bf16, shuffled tables",
 }
+N_QUERY = {"spec-verify": 6}   # queries per sequence of the step (1 = decode)
 
 
 def kv_bytes_per_token(wl):
@@ -72,7 +76,7 @@ def algorithmic_bytes(wl, lens):
     return int(sum(lens) * per)
 
 
-def cpu_baseline(kv, wl, t, l, budget_s):
+def cpu_baseline(kv, wl, t, l, budget_s, nq=1):
     """Time the oracle's decode on the first sequences of the batch: rebuild the
     logical K/V through the table from the copied-back pool bytes, then float64
     attention.  Stops after ~budget_s seconds."""
@@ -86,13 +90,17 @@ def cpu_baseline(kv, wl, t, l, budget_s):
                 num_sink_blocks=wl.num_sink_blocks)
     view = AT.PoolView(pool_bytes, desc)
     import torch
-    q = torch.from_numpy(wl.q()).to({"f32": torch.float32, "f16": torch.float16,
-                                     "bf16": torch.bfloat16}[wl.q_dtype]).double().numpy()
+    qsrc = wl.q() if nq == 1 else wl.q_verify(nq)
+    q = torch.from_numpy(qsrc).to({"f32": torch.float32, "f16": torch.float16,
+                                   "bf16": torch.bfloat16}[wl.q_dtype]).double().numpy()
     done, secs = 0, 0.0
     while done < wl.batch and secs < budget_s:
         t0 = time.perf_counter()
         K, V = view.logical_kv(t[done], int(l[done]))
-        AT.attention_one(q[done], K, V, wl.scale)
+        if nq == 1:
+            AT.attention_one(q[done], K, V, wl.scale)
+        else:
+            AT.verify_attention_one(q[done], K, V, wl.scale)
         secs += time.perf_counter() - t0
         done += 1
     byts = algorithmic_bytes(wl, [int(x) for x in l[:done]])
@@ -105,7 +113,7 @@ def cpu_baseline(kv, wl, t, l, budget_s):
             "kind": "oracle",
             "sample": f"{done} of {wl.batch} sequences ({int(sum(l[:done]))} tokens): logical "
                       f"rebuild from the pool bytes + float64 attention, {secs:.1f} s",
-            "queries_per_s": round(done / secs, 3),
+            "queries_per_s": round(done * nq / secs, 3),
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -144,34 +152,53 @@ def main():
     tdev, ldev, t, l = kv.device_tables()
     lens = [int(x) for x in l]
     max_len = max(lens)
-    q = torch.from_numpy(wl.q()).to(torch_dtype(wl.q_dtype)).to(dev)
+    nq = N_QUERY.get(args.config, 1)
+    if nq == 1:
+        q = torch.from_numpy(wl.q()).to(torch_dtype(wl.q_dtype)).to(dev)
+        ws_bytes = B.pa_decode_workspace_bytes(kv.pool, wl.batch, wl.n_q_heads, max_len)
+    else:
+        q = torch.from_numpy(wl.q_verify(nq)).to(torch_dtype(wl.q_dtype)).to(dev)
+        ws_bytes = B.pa_verify_workspace_bytes(kv.pool, wl.batch, wl.n_q_heads, nq, max_len)
     out = torch.empty_like(q)
-    ws_bytes = B.pa_decode_workspace_bytes(kv.pool, wl.batch, wl.n_q_heads, max_len)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
-    # the step's append: every sequence's newest token, rewritten in its slot
-    k_new, v_new = [], []
-    for s, L in zip(wl.decode_seqs, lens):
+    # the step's append: every sequence's nq newest tokens, rewritten in their
+    # slots (the work per step stays constant)
+    k_new, v_new, slots = [], [], []
+    for b, (s, L) in enumerate(zip(wl.decode_seqs, lens)):
         K, V = wl.seq_tokens(s)
-        k_new.append(K[L - 1])
-        v_new.append(V[L - 1])
+        for p in range(max(L - nq, 0), L):
+            k_new.append(K[p])
+            v_new.append(V[p])
+            slots.append(t[b, p // 16] * 16 + p % 16)
         del K, V
     k_new, v_new = np.stack(k_new), np.stack(v_new)
+    n_new = len(slots)
     in_dt = torch_dtype(wl.in_dtype)
     k_new = torch.from_numpy(k_new).to(in_dt).to(dev)
     v_new = torch.from_numpy(v_new).to(in_dt).to(dev)
-    slots = np.array([t[b, (L - 1) // 16] * 16 + (L - 1) % 16 for b, L in enumerate(lens)],
-                     dtype=np.int32)
-    slots_dev = torch.from_numpy(slots).to(dev)
+    slots_dev = torch.from_numpy(np.array(slots, dtype=np.int32)).to(dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     dargs = (q, kv.pool, tdev, ldev, wl.batch, wl.n_q_heads, wl.q_dtype, tdev.shape[1], max_len,
              wl.scale, out, ws, ws.numel(), sh)
+    vargs = (q, kv.pool, tdev, ldev, wl.batch, wl.n_q_heads, nq, wl.q_dtype, tdev.shape[1],
+             max_len, wl.scale, out, ws, ws.numel(), sh)
+
+    def attn_split():   # the dominant launch (the verify call is one launch at these shapes)
+        if nq == 1:
+            B.pa_decode_split(*dargs)
+        else:
+            B.pa_verify_attention(*vargs)
+
+    def attn_rest():
+        if nq == 1:
+            B.pa_decode_combine(*dargs)
 
     def step():
-        B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, wl.batch, sh)
-        B.pa_decode_split(*dargs)
-        B.pa_decode_combine(*dargs)
+        B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, n_new, sh)
+        attn_split()
+        attn_rest()
 
     print(f"[bench] warmup {args.warmup} ...", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -189,14 +216,14 @@ def main():
     # events on the launch stream around every split launch
     split_ev = []
     for _ in range(args.steps):
-        B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, wl.batch, sh)
+        B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, n_new, sh)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        B.pa_decode_split(*dargs)
+        attn_split()
         e1.record(stream)
         split_ev.append((e0, e1))
-        B.pa_decode_combine(*dargs)
+        attn_rest()
     torch.cuda.synchronize()
     split_ms = [a.elapsed_time(b) for a, b in split_ev]
     split_avg = float(np.mean(split_ms))
@@ -217,9 +244,9 @@ def main():
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            B.pa_decode_split(*dargs)
+            attn_split()
             e1.record(stream)
-            B.pa_decode_combine(*dargs)
+            attn_rest()
             torch.cuda.synchronize()
             cold.append(e0.elapsed_time(e1))
         extra["cold_split_ms_median"] = round(float(np.median(cold)), 4)
@@ -252,7 +279,7 @@ def main():
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(kv, wl, t, l, args.cpu_budget)
+        cpu = cpu_baseline(kv, wl, t, l, args.cpu_budget, nq)
 
     split_blocks = B.pa_decode_split_blocks(kv.pool, wl.batch, wl.n_q_heads, max_len)
     # HBM bytes per split launch from the committed rocprofv3 counters, while
@@ -277,10 +304,10 @@ def main():
                    + (", identity block order" if args.identity_tables else ""), "batch": wl.batch,
                    "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
                    "head_dim": wl.head_dim, "block_size": 16, "kv_dtype": wl.kv_dtype,
-                   "total_tokens": int(sum(lens)), "max_seq_len": max_len,
-                   **({"split_blocks": split_blocks} if split_blocks > 0
+                   "total_tokens": int(sum(lens)), "max_seq_len": max_len, "n_query": nq,
+                   **({} if nq > 1 else {"split_blocks": split_blocks} if split_blocks > 0
                       else {"persistent_workgroups": -split_blocks})},
-        "queries_per_s": round(wl.batch / (ms_step * 1e-3), 1),
+        "queries_per_s": round(wl.batch * nq / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": byts,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

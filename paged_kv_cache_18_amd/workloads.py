@@ -229,5 +229,6 @@ def by_name(name, **kw):
         "mixed-fp8": lambda **k: mixed_precision(kv="fp8", **k),
         "shared-prefix": shared_prefix,
         "shared-prefix-partial": lambda **k: shared_prefix(prefix=1992, **k),
+        "spec-verify": llama3_8b,   # the same batch, scored by a verify step
     }
     return table[name](**kw)
