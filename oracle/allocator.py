@@ -37,6 +37,20 @@ Readings where the pages are silent (each one also listed in the design doc):
   ``0 .. sink_blocks_per_seq-1`` of every sequence come from the sink arena
   (8GB page, section 5 flowchart, "Token Position Router": sink tokens go to
   the high-precision pool, the body to the compressed one).
+* A pool with a local window of W tokens (8GB page, section 4: the most
+  recent 128 tokens stay FP16 in dedicated high-precision blocks; section 5
+  flowchart, "Token Position Router") keeps in the FP16 arena every block
+  that is not entirely older than the last W tokens.  Block j is out of the
+  window at length L when 16(j+1) <= L - W.  A reserve takes each new block
+  from the arena its position has at the reserve's final length (so a long
+  prefill writes its old blocks straight into the body, quantized on write);
+  a block already in the FP16 arena that has left the window is moved by
+  ``seq_settle`` (called once its tokens are written): in increasing logical
+  order, pop a body block, record the (FP16 source, body target) migration,
+  point the table at the target and drop one reference of the source.  A
+  rollback never moves blocks back, so a sequence's table is always sink
+  blocks, then body blocks, then FP16 window blocks.  Migration is per
+  sequence: a shared FP16 block keeps serving its other users.
 """
 
 from __future__ import annotations
@@ -66,11 +80,16 @@ class Pool:
     """The pool's metadata (no device memory); ids are global."""
 
     def __init__(self, num_blocks, num_sink_blocks=0, sink_blocks_per_seq=0,
-                 body_free_order=None, sink_free_order=None, block_size=BLOCK):
+                 body_free_order=None, sink_free_order=None, block_size=BLOCK,
+                 window_tokens=0):
         if num_blocks < 0 or num_sink_blocks < 0 or block_size <= 0:
             raise PoolError("INVALID_ARG", "negative pool size")
         if sink_blocks_per_seq < 0 or (sink_blocks_per_seq > 0) != (num_sink_blocks > 0):
             raise PoolError("INVALID_ARG", "sink arena and sink_blocks_per_seq go together")
+        if window_tokens < 0 or (window_tokens > 0 and num_sink_blocks == 0):
+            raise PoolError("INVALID_ARG", "a window needs the FP16 arena")
+        self.window = window_tokens
+        self.migrations: list[tuple[int, int]] = []  # (FP16 source, body target)
         self.bs = block_size
         self.n_body = num_blocks
         self.n_sink = num_sink_blocks
@@ -149,8 +168,16 @@ class Pool:
             raise PoolError("BAD_ID", f"sequence {sid}")
         return self.seqs[sid]
 
-    def _arena_for_logical(self, j):
-        return SINK if j < self.sink_per_seq else BODY
+    def n_out(self, length):
+        """Logical blocks entirely older than the window at this length."""
+        if self.window == 0:
+            return 1 << 62
+        return max(0, (length - self.window) // self.bs)
+
+    def _arena_for_logical(self, j, length):
+        if j < self.sink_per_seq or j >= self.n_out(length):
+            return SINK
+        return BODY
 
     def seq_create(self):
         sid = self.next_seq
@@ -188,18 +215,35 @@ class Pool:
             need[self.arena_of(s.table[-1])] += 1
         first_new = len(s.table)
         last = (s.length + n + bs - 1) // bs
+        final = s.length + n
         for j in range(first_new, last):
-            need[self._arena_for_logical(j)] += 1
+            need[self._arena_for_logical(j, final)] += 1
         for a in (BODY, SINK):
             if need[a] > len(self.stacks[a]):
                 raise PoolError("OUT_OF_BLOCKS", f"arena {a} needs {need[a]}")
         if clone:
             s.table[-1] = self.cow_clone(s.table[-1])
         for j in range(first_new, last):
-            s.table.append(self.alloc(self._arena_for_logical(j)))
+            s.table.append(self.alloc(self._arena_for_logical(j, final)))
         slots = [s.table[p // bs] * bs + p % bs for p in range(s.length, s.length + n)]
         s.length += n
         return slots
+
+    def seq_settle(self, sid):
+        """Move the sequence's FP16 blocks that have left the window into the
+        body (all-or-nothing); returns how many moved."""
+        s = self._seq(sid)
+        todo = [j for j in range(self.sink_per_seq, min(self.n_out(s.length), len(s.table)))
+                if self.arena_of(s.table[j]) == SINK]
+        if len(todo) > len(self.stacks[BODY]):
+            raise PoolError("OUT_OF_BLOCKS", f"body arena needs {len(todo)}")
+        for j in todo:
+            src = s.table[j]
+            dst = self.alloc(BODY)
+            self.migrations.append((src, dst))
+            s.table[j] = dst
+            self.free(src)
+        return len(todo)
 
     def seq_truncate(self, sid, new_len):
         """Drop tokens beyond new_len; blocks no longer used go back last-first."""
@@ -262,6 +306,8 @@ def replay(pool: Pool, ops):
                 r = pool.free(*args)
             elif kind == "clone":
                 r = pool.cow_clone(*args)
+            elif kind == "settle":
+                r = pool.seq_settle(*args)
             else:
                 raise ValueError(kind)
         except PoolError as e:
