@@ -130,6 +130,11 @@ typedef struct {
                                   only with an INT4 or FP8 body                   */
   int32_t sink_blocks_per_seq; /* logical blocks 0..k-1 of every sequence come
                                   from the sink arena; > 0 iff num_sink_blocks > 0 */
+  int32_t window_tokens;        /* local FP16 window: a block not entirely older than
+                                  the last window_tokens tokens of its sequence is
+                                  taken from the FP16 (sink) arena; 0 = none.  Needs
+                                  the sink arena.  ([8GB] section 4: the most recent
+                                  128 tokens stay FP16.)                          */
 } pa_pool_desc;
 
 typedef struct {
@@ -184,12 +189,25 @@ pa_status pa_seq_create(pa_pool* pool, int32_t* out_seq);
 /* Child sharing all of parent's blocks (each gains one reference). */
 pa_status pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* out_child);
 /* Append n_tokens slots to `seq`: a new block only when the tail is full
- * ([60Y] "a ideia roubada"); logical blocks < sink_blocks_per_seq come from
- * the sink arena.  If the tail is partially filled and shared, it is cloned
+ * ([60Y] "a ideia roubada"); logical blocks < sink_blocks_per_seq, and with
+ * a window every new block not entirely older than the window at the final
+ * length, come from the sink (FP16) arena.  If the tail is partially filled and shared, it is cloned
  * first (pa_cow_clone on `stream`).  slots_out (host, n_tokens entries)
  * receives id*16 + offset per new token.  All-or-nothing. */
 pa_status pa_seq_reserve(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* slots_out,
                          void* stream);
+/* With a window: move every FP16 block of `seq` past its sink blocks that has
+ * left the window (block j with 16*(j+1) <= len - window_tokens) into the body
+ * arena, in increasing j: pop a body block, quantize the 16 FP16 tokens of
+ * every head into it on `stream` (the quantize-on-write rule), point the
+ * table at it, drop one reference of the FP16 block.  Call it after the
+ * tokens of the reserved slots are appended and before a decode reads the
+ * pool ([8GB] section 5 flowchart: the token-position router sends the middle
+ * body through the quantizer).  Later work on the FP16 block must follow on
+ * the same stream.  n_moved (may be NULL) receives the count.  All-or-nothing
+ * (PA_ERR_OUT_OF_BLOCKS when the body arena is short).  A no-op without a
+ * window.  A rollback never moves blocks back to FP16. */
+pa_status pa_seq_settle(pa_pool* pool, int32_t seq, void* stream, int32_t* n_moved);
 /* Shorten to new_len tokens; blocks no longer used are released last-first. */
 pa_status pa_seq_truncate(pa_pool* pool, int32_t seq, int32_t new_len);
 /* Release all blocks (last-first) and forget the sequence. */

@@ -36,7 +36,7 @@ P32 = C.POINTER(C.c_int32)
 class pa_pool_desc(C.Structure):
     _fields_ = [("block_size", i32), ("n_kv_heads", i32), ("head_dim", i32), ("kv_dtype", i32),
                 ("group_size", i32), ("num_blocks", i32), ("num_sink_blocks", i32),
-                ("sink_blocks_per_seq", i32)]
+                ("sink_blocks_per_seq", i32), ("window_tokens", i32)]
 
 
 class pa_layout(C.Structure):
@@ -77,6 +77,7 @@ _PROTOS = {
     "pa_decode_workspace_bytes": [vp, i32, i32, i32, C.POINTER(sz)],
     "pa_decode_split_blocks": [vp, i32, i32, i32, P32],
     "pa_stream_read": [vp, sz, vp, vp],
+    "pa_seq_settle": [vp, i32, vp, P32],
     "pa_decode_attention": _DECODE_ARGS,
     "pa_verify_workspace_bytes": [vp, i32, i32, i32, i32, C.POINTER(sz)],
     "pa_verify_attention": [vp, vp, P32, P32, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz, vp],
@@ -131,10 +132,10 @@ def _host_i32(arr):
 
 
 def make_desc(n_kv_heads, head_dim, kv_dtype, num_blocks, group_size=0, num_sink_blocks=0,
-              sink_blocks_per_seq=0, block_size=16):
+              sink_blocks_per_seq=0, block_size=16, window_tokens=0):
     kv = DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
     return pa_pool_desc(block_size, n_kv_heads, head_dim, kv, group_size, num_blocks,
-                        num_sink_blocks, sink_blocks_per_seq)
+                        num_sink_blocks, sink_blocks_per_seq, window_tokens)
 
 
 # ---- pool ---------------------------------------------------------------------------
@@ -303,6 +304,14 @@ def pa_decode_combine(q, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype, 
                       max_seq_len, scale, out, workspace, workspace_bytes, stream=None):
     _decode(lib().pa_decode_combine, q, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype,
             max_blocks, max_seq_len, scale, out, workspace, workspace_bytes, stream)
+
+
+def pa_seq_settle(pool, seq, stream=None):
+    """Move the sequence's FP16 blocks that left the window into the body;
+    returns how many moved."""
+    out = i32()
+    _check(lib().pa_seq_settle(pool, seq, _ptr(stream), C.byref(out)))
+    return out.value
 
 
 def pa_verify_workspace_bytes(pool, batch, n_q_heads, n_query, max_seq_len):

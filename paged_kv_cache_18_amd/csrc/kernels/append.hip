@@ -21,64 +21,13 @@ namespace {
 
 constexpr int kWaves = 4;  // waves per workgroup
 
-// One wave per (token, kv head, K-or-V).  Lane `l` holds the dimension pairs
-// k = l + 64*m (dims 2k, 2k+1): the two nibbles of a packed INT4 byte always
-// come from one lane, and a byte never mixes two tokens.
+// Quantize one (token t, kv head h, K-or-V) vector of a body block `id` and
+// store codes, scales and zeros: lane l holds dims 2k, 2k+1 for
+// k = l + 64*m (valid where has[m]).  Inputs are first rounded to fp16.
 template <int MP>
-__global__ __launch_bounds__(kWaves * 64) void append_kv_kernel(PoolDev p, const void* kin,
-                                                                const void* vin, int in_dt,
-                                                                const int32_t* slots, int n) {
-  const int lane = threadIdx.x & 63;
-  const long gw = (long(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-  const int H = p.n_kv_heads, D = p.head_dim, N = p.num_blocks;
-  const int kind = int(gw & 1);  // 0 = K, 1 = V
-  const long th = gw >> 1;
-  const long tok = th / H;
-  const int h = int(th % H);
-  if (tok >= n) return;
-  const int slot = slots[tok];
-  if (slot < 0) return;
-  const int id = slot >> 4, t = slot & 15;
-  if (id >= N + p.num_sink_blocks) return;
-
-  const void* src = kind ? vin : kin;
-  const size_t base = (size_t(tok) * H + h) * D;
-  const int npairs = D >> 1;
-  float x[MP][2];
-  bool has[MP];
-#pragma unroll
-  for (int m = 0; m < MP; ++m) {
-    const int k = lane + 64 * m;
-    has[m] = k < npairs;
-    x[m][0] = has[m] ? load_as_f32(src, base + 2 * k, in_dt) : 0.f;
-    x[m][1] = has[m] ? load_as_f32(src, base + 2 * k + 1, in_dt) : 0.f;
-  }
-
-  // ---- FP16 sink arena and raw bodies: plain stores --------------------------
-  const bool sink = id >= N;
-  if (sink || is_raw_dev(p.kv_dtype)) {
-    const int arr = sink ? (kind ? kArrSV : kArrSK) : (kind ? kArrV : kArrK);
-    const int dt = sink ? int(kF16) : p.kv_dtype;
-    uint8_t* slab = p.base + p.off[arr] + (size_t(sink ? id - N : id) * H + h) * p.slab[arr];
-#pragma unroll
-    for (int m = 0; m < MP; ++m) {
-      if (!has[m]) continue;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int d = 2 * (lane + 64 * m) + e;
-        const int idx = kind ? raw_v_elem(t, d, D) : raw_k_elem(t, d);
-        if (dt == kF32)
-          reinterpret_cast<float*>(slab)[idx] = x[m][e];
-        else if (dt == kF16)
-          reinterpret_cast<uint16_t*>(slab)[idx] = f32_to_f16_bits(x[m][e]);
-        else
-          reinterpret_cast<uint16_t*>(slab)[idx] = f32_to_bf16_bits(x[m][e]);
-      }
-    }
-    return;
-  }
-
-  // ---- quantized body: inputs are first rounded to fp16 ------------------------
+__device__ inline void quantize_store(const PoolDev& p, int id, int t, int h, int kind,
+                                      float (&x)[MP][2], const bool (&has)[MP], int lane) {
+  const int H = p.n_kv_heads, D = p.head_dim;
 #pragma unroll
   for (int m = 0; m < MP; ++m) {
     x[m][0] = f16_bits_to_f32(f32_to_f16_bits(x[m][0]));
@@ -168,6 +117,66 @@ __global__ __launch_bounds__(kWaves * 64) void append_kv_kernel(PoolDev p, const
   }
 }
 
+// One wave per (token, kv head, K-or-V).  Lane `l` holds the dimension pairs
+// k = l + 64*m (dims 2k, 2k+1): the two nibbles of a packed INT4 byte always
+// come from one lane, and a byte never mixes two tokens.
+template <int MP>
+__global__ __launch_bounds__(kWaves * 64) void append_kv_kernel(PoolDev p, const void* kin,
+                                                                const void* vin, int in_dt,
+                                                                const int32_t* slots, int n) {
+  const int lane = threadIdx.x & 63;
+  const long gw = (long(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int H = p.n_kv_heads, D = p.head_dim, N = p.num_blocks;
+  const int kind = int(gw & 1);  // 0 = K, 1 = V
+  const long th = gw >> 1;
+  const long tok = th / H;
+  const int h = int(th % H);
+  if (tok >= n) return;
+  const int slot = slots[tok];
+  if (slot < 0) return;
+  const int id = slot >> 4, t = slot & 15;
+  if (id >= N + p.num_sink_blocks) return;
+
+  const void* src = kind ? vin : kin;
+  const size_t base = (size_t(tok) * H + h) * D;
+  const int npairs = D >> 1;
+  float x[MP][2];
+  bool has[MP];
+#pragma unroll
+  for (int m = 0; m < MP; ++m) {
+    const int k = lane + 64 * m;
+    has[m] = k < npairs;
+    x[m][0] = has[m] ? load_as_f32(src, base + 2 * k, in_dt) : 0.f;
+    x[m][1] = has[m] ? load_as_f32(src, base + 2 * k + 1, in_dt) : 0.f;
+  }
+
+  // ---- FP16 sink arena and raw bodies: plain stores --------------------------
+  const bool sink = id >= N;
+  if (sink || is_raw_dev(p.kv_dtype)) {
+    const int arr = sink ? (kind ? kArrSV : kArrSK) : (kind ? kArrV : kArrK);
+    const int dt = sink ? int(kF16) : p.kv_dtype;
+    uint8_t* slab = p.base + p.off[arr] + (size_t(sink ? id - N : id) * H + h) * p.slab[arr];
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+      if (!has[m]) continue;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int d = 2 * (lane + 64 * m) + e;
+        const int idx = kind ? raw_v_elem(t, d, D) : raw_k_elem(t, d);
+        if (dt == kF32)
+          reinterpret_cast<float*>(slab)[idx] = x[m][e];
+        else if (dt == kF16)
+          reinterpret_cast<uint16_t*>(slab)[idx] = f32_to_f16_bits(x[m][e]);
+        else
+          reinterpret_cast<uint16_t*>(slab)[idx] = f32_to_bf16_bits(x[m][e]);
+      }
+    }
+    return;
+  }
+
+  quantize_store<MP>(p, id, t, h, kind, x, has, lane);
+}
+
 // Copy-on-write: every array's slabs of block `src` (all heads) to `dst`.
 struct CopyJob {
   size_t src[kNumArr], dst[kNumArr], bytes[kNumArr];
@@ -185,7 +194,51 @@ __global__ __launch_bounds__(256) void block_copy_kernel(uint8_t* base, CopyJob 
     d[u] = s[u];
 }
 
+constexpr int kMigrateMP = 2;  // dimension pairs per lane: head_dim <= 256
+
+// Window migration: the 16 FP16 tokens of sink-arena block src[i] (every
+// head, K and V) quantized into body block dst[i]; one wave per (pair, token,
+// head, K-or-V).
+__global__ __launch_bounds__(kWaves * 64) void migrate_kernel(PoolDev p, MigrateJob job) {
+  const int lane = threadIdx.x & 63;
+  const long gw = (long(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int H = p.n_kv_heads, D = p.head_dim, N = p.num_blocks;
+  const int kind = int(gw & 1);
+  long r = gw >> 1;
+  const int h = int(r % H);
+  r /= H;
+  const int t = int(r % 16);
+  const long pi = r / 16;
+  if (pi >= job.n) return;
+  const int src = job.src[pi], dst = job.dst[pi];
+  if (src < N || src >= N + p.num_sink_blocks || dst < 0 || dst >= N) return;
+  const int arr = kind ? kArrSV : kArrSK;
+  const uint16_t* slab = reinterpret_cast<const uint16_t*>(
+      p.base + p.off[arr] + (size_t(src - N) * H + h) * p.slab[arr]);
+  float x[kMigrateMP][2];
+  bool has[kMigrateMP];
+#pragma unroll
+  for (int m = 0; m < kMigrateMP; ++m) {
+    const int k = lane + 64 * m;
+    has[m] = 2 * k < D;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = 2 * k + e;
+      x[m][e] = has[m] ? f16_bits_to_f32(slab[kind ? raw_v_elem(t, d, D) : raw_k_elem(t, d)]) : 0.f;
+    }
+  }
+  quantize_store<kMigrateMP>(p, dst, t, h, kind, x, has, lane);
+}
+
 }  // namespace
+
+hipError_t launch_migrate(const PoolDev& p, const MigrateJob& job, hipStream_t s) {
+  if (job.n <= 0) return hipSuccess;
+  const long waves = long(job.n) * 16 * p.n_kv_heads * 2;
+  const unsigned grid = unsigned((waves + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL(migrate_kernel, dim3(grid), dim3(kWaves * 64), 0, s, p, job);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const PoolDev& p, const void* k, const void* v, int32_t in_dtype,
                          const int32_t* slots, int32_t n_tokens, hipStream_t s) {

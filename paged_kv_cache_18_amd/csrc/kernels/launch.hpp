@@ -18,6 +18,15 @@ struct PoolDev {
   size_t slab[kNumArr];
 };
 
+// Window migration (FP16 sink-arena block -> body block), up to
+// kMigrateMax pairs per launch.
+constexpr int kMigrateMax = 16;
+struct MigrateJob {
+  int32_t src[kMigrateMax], dst[kMigrateMax];
+  int32_t n;
+};
+hipError_t launch_migrate(const PoolDev& p, const MigrateJob& job, hipStream_t s);
+
 hipError_t launch_append(const PoolDev& p, const void* k, const void* v, int32_t in_dtype,
                          const int32_t* slots, int32_t n_tokens, hipStream_t s);
 

@@ -55,8 +55,9 @@ void need(const void* p, const char* what) {
 
 pa::Desc to_desc(const pa_pool_desc* d) {
   need(d, "desc");
-  return pa::Desc{d->block_size,      d->n_kv_heads,      d->head_dim,           d->kv_dtype,
-                  d->group_size,      d->num_blocks,      d->num_sink_blocks,    d->sink_blocks_per_seq};
+  return pa::Desc{d->block_size, d->n_kv_heads,      d->head_dim,
+                  d->kv_dtype,   d->group_size,      d->num_blocks,
+                  d->num_sink_blocks, d->sink_blocks_per_seq, d->window_tokens};
 }
 
 void check_hip(hipError_t e, const char* what) {
@@ -171,7 +172,8 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
                        (n_query == 1 ? G <= 16 : ncol <= 32) && d.num_sink_blocks == 0;
   const bool quant_ok = ((d.kv_dtype == pa::kInt4 && d.group_size == d.head_dim) ||
                          d.kv_dtype == pa::kFp8) &&
-                        q_dtype == pa::kF16 && d.head_dim == 128 && G <= 16 && n_query == 1;
+                        q_dtype == pa::kF16 && d.head_dim == 128 && G <= 16 && n_query == 1 &&
+                        d.window_tokens == 0;
   const char* force = std::getenv("PA_DECODE_KERNEL");  // "generic" forces the VALU kernel
   const bool generic = force && std::strcmp(force, "generic") == 0;
   pl.kernel = generic ? pa::kKernGeneric
@@ -459,6 +461,26 @@ pa_status pa_seq_reserve(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* 
     std::vector<int32_t> slots = pool->core.seq_reserve(seq, n_tokens, &clones);
     if (!slots.empty()) std::memcpy(slots_out, slots.data(), slots.size() * sizeof(int32_t));
     for (const auto& c : clones) enqueue_copy(pool, c.first, c.second, stream);
+  });
+}
+
+pa_status pa_seq_settle(pa_pool* pool, int32_t seq, void* stream, int32_t* n_moved) {
+  return guard([&] {
+    need(pool, "pool");
+    std::vector<std::pair<int32_t, int32_t>> moves;
+    const int32_t n = pool->core.seq_settle(seq, &moves);
+    if (n_moved) *n_moved = n;
+    if (!pool->dev) return;  // metadata-only pool
+    const pa::PoolDev p = dev_view(pool);
+    for (size_t i = 0; i < moves.size(); i += pa::kMigrateMax) {
+      pa::MigrateJob job{};
+      job.n = int32_t(std::min<size_t>(pa::kMigrateMax, moves.size() - i));
+      for (int32_t k = 0; k < job.n; ++k) {
+        job.src[k] = moves[i + size_t(k)].first;
+        job.dst[k] = moves[i + size_t(k)].second;
+      }
+      check_hip(pa::launch_migrate(p, job, static_cast<hipStream_t>(stream)), "migrate launch");
+    }
   });
 }
 

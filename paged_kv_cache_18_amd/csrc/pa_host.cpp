@@ -36,6 +36,9 @@ void validate_desc(const Desc& d) {
     fail(kInvalidArg, "num_sink_blocks and sink_blocks_per_seq go together");
   if (d.num_sink_blocks > 0 && is_raw(d.kv_dtype))
     fail(kUnsupported, "a sink arena needs an INT4 or FP8 body");
+  if (d.window_tokens < 0) fail(kInvalidArg, "negative window_tokens");
+  if (d.window_tokens > 0 && d.num_sink_blocks == 0)
+    fail(kInvalidArg, "a window needs the FP16 (sink) arena");
 }
 
 Layout compute_layout(const Desc& d) {
@@ -152,8 +155,15 @@ std::vector<int32_t> PoolCore::free_list(int32_t arena) const {
   return std::vector<int32_t>(stack_[arena].rbegin(), stack_[arena].rend());
 }
 
-int32_t PoolCore::arena_for_logical(int32_t j) const {
-  return j < d_.sink_blocks_per_seq ? kSink : kBody;
+int64_t PoolCore::n_out(int64_t length) const {
+  if (d_.window_tokens == 0) return std::numeric_limits<int64_t>::max();
+  return std::max<int64_t>(0, (length - d_.window_tokens) / kBlock);
+}
+
+// FP16 arena for the sink blocks and for every block not entirely older than
+// the window at `length` (the reserve's final length), body otherwise.
+int32_t PoolCore::arena_for_logical(int32_t j, int64_t length) const {
+  return (j < d_.sink_blocks_per_seq || j >= n_out(length)) ? kSink : kBody;
 }
 
 Seq& PoolCore::seq_mut(int32_t id) {
@@ -211,7 +221,8 @@ std::vector<int32_t> PoolCore::seq_reserve(int32_t sid, int32_t n,
   if (clone) ++need[arena_of(s.table.back())];
   const int32_t first_new = int32_t(s.table.size());
   const int32_t last = int32_t((int64_t(s.length) + n + kBlock - 1) / kBlock);
-  for (int32_t j = first_new; j < last; ++j) ++need[arena_for_logical(j)];
+  const int64_t final_len = int64_t(s.length) + n;
+  for (int32_t j = first_new; j < last; ++j) ++need[arena_for_logical(j, final_len)];
   for (int a = 0; a < 2; ++a)
     if (size_t(need[a]) > stack_[a].size())
       fail(kOutOfBlocks, std::string(a == kBody ? "body" : "sink") + " arena needs " +
@@ -223,7 +234,7 @@ std::vector<int32_t> PoolCore::seq_reserve(int32_t sid, int32_t n,
     s.table.back() = dst;
     if (clones) clones->emplace_back(src, dst);
   }
-  for (int32_t j = first_new; j < last; ++j) s.table.push_back(alloc(arena_for_logical(j)));
+  for (int32_t j = first_new; j < last; ++j) s.table.push_back(alloc(arena_for_logical(j, final_len)));
   slots.resize(size_t(n));
   for (int32_t i = 0; i < n; ++i) {
     int32_t p = s.length + i;
@@ -231,6 +242,25 @@ std::vector<int32_t> PoolCore::seq_reserve(int32_t sid, int32_t n,
   }
   s.length += n;
   return slots;
+}
+
+int32_t PoolCore::seq_settle(int32_t sid, std::vector<std::pair<int32_t, int32_t>>* moves) {
+  Seq& s = seq_mut(sid);
+  const int64_t end = std::min<int64_t>(n_out(s.length), int64_t(s.table.size()));
+  std::vector<int32_t> todo;
+  for (int64_t j = d_.sink_blocks_per_seq; j < end; ++j)
+    if (arena_of(s.table[size_t(j)]) == kSink) todo.push_back(int32_t(j));
+  if (todo.size() > stack_[kBody].size())
+    fail(kOutOfBlocks, "body arena needs " + std::to_string(todo.size()) + " blocks, has " +
+                           std::to_string(stack_[kBody].size()));
+  for (int32_t j : todo) {
+    const int32_t src = s.table[size_t(j)];
+    const int32_t dst = alloc(kBody);
+    s.table[size_t(j)] = dst;
+    free_block(src);
+    if (moves) moves->emplace_back(src, dst);
+  }
+  return int32_t(todo.size());
 }
 
 void PoolCore::seq_truncate(int32_t sid, int32_t new_len) {

@@ -42,7 +42,7 @@ struct Error {
 
 struct Desc {
   int32_t block_size, n_kv_heads, head_dim, kv_dtype, group_size, num_blocks, num_sink_blocks,
-      sink_blocks_per_seq;
+      sink_blocks_per_seq, window_tokens;
 };
 
 struct Layout {
@@ -86,6 +86,9 @@ class PoolCore {
   // Appends n slots; clones (src, dst) performed are appended to *clones.
   std::vector<int32_t> seq_reserve(int32_t seq, int32_t n,
                                    std::vector<std::pair<int32_t, int32_t>>* clones);
+  // Moves the sequence's FP16 blocks that have left the window into the body
+  // (pairs (FP16 source, body target) appended to *moves); all-or-nothing.
+  int32_t seq_settle(int32_t seq, std::vector<std::pair<int32_t, int32_t>>* moves);
   void seq_truncate(int32_t seq, int32_t new_len);
   void seq_release(int32_t seq);
   const Seq& seq(int32_t id) const;
@@ -94,7 +97,8 @@ class PoolCore {
   Seq& seq_mut(int32_t id);
   void check_id(int32_t id) const;
   void check_drop(const std::vector<int32_t>& blocks, size_t from) const;
-  int32_t arena_for_logical(int32_t j) const;
+  int64_t n_out(int64_t length) const;  // logical blocks entirely older than the window
+  int32_t arena_for_logical(int32_t j, int64_t length) const;
 
   Desc d_;
   std::vector<int32_t> ref_;

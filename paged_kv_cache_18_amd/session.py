@@ -27,7 +27,8 @@ class PagedKV:
         self.device = device
         self.desc = B.make_desc(wl.n_kv_heads, wl.head_dim, wl.kv_dtype, wl.num_blocks,
                                 group_size=wl.group_size, num_sink_blocks=wl.num_sink_blocks,
-                                sink_blocks_per_seq=wl.sink_blocks_per_seq)
+                                sink_blocks_per_seq=wl.sink_blocks_per_seq,
+                                window_tokens=wl.window_tokens)
         self.pool_bytes = B.pa_pool_bytes(self.desc)
         order = wl.body_free_order if body_free_order is None else body_free_order
         if device is None:
@@ -106,6 +107,8 @@ class PagedKV:
                     r = B.pa_free_block(self.pool, *args)
                 elif kind == "clone":
                     r = B.pa_cow_clone(self.pool, args[0], self.stream())
+                elif kind == "settle":
+                    r = B.pa_seq_settle(self.pool, args[0], self.stream())
                 else:
                     raise ValueError(kind)
             except B.PaError as e:

@@ -65,6 +65,7 @@ class Workload:
     sink_free_order: np.ndarray | None = None
     outlier_channels: np.ndarray | None = None
     outlier_scale: float = 10.0
+    window_tokens: int = 0
     extra: dict = field(default_factory=dict)
 
     @property
@@ -154,24 +155,61 @@ def long_context(seed=3, batch=4, length=65536):
 
 
 def mixed_precision(seed=4, kv="int4", length=65536, steps=64, group=128,
-                    n_kv_heads=8, head_dim=128, n_q_heads=32):
+                    n_kv_heads=8, head_dim=128, n_q_heads=32, window=0):
     """One sequence of ``length`` fp16 tokens, then ``steps`` single-token
     appends.  Logical block 0 (16 sink tokens) lives in a one-block FP16 sink
     arena, the body is INT4 (groups of ``group``) or FP8.  1 % of the
-    (head, dim) channels are scaled x10 in K and V for every token."""
+    (head, dim) channels are scaled x10 in K and V for every token.  With
+    ``window`` > 0 the FP16 arena also holds the blocks of the last
+    ``window`` tokens, and every reserve is followed by a settle."""
     body_blocks = -(-(length + steps - BLOCK) // BLOCK)
     n = _pool_size(body_blocks)
     perm = rng(seed, 0).permutation(n)
     n_out = int(round(0.01 * n_kv_heads * head_dim))
     outl = np.sort(rng(seed, 4).choice(n_kv_heads * head_dim, size=n_out, replace=False))
-    ops = [("create",), ("reserve", 0, length)]
-    ops += [("reserve", 0, 1) for _ in range(steps)]
+    settle = [("settle", 0)] if window else []
+    ops = [("create",), ("reserve", 0, length)] + settle
+    for _ in range(steps):
+        ops += [("reserve", 0, 1)] + settle
     src = [(1, 0, length)] + [(6, s, 1) for s in range(steps)]
-    return Workload(f"mixed-{kv}", seed, n_q_heads, n_kv_heads, head_dim, kv, "f16", "f16",
+    n_sink = 1 + (-(-window // BLOCK) + 2 if window else 0)
+    name = f"mixed-{kv}" + (f"-w{window}-g{group}" if window else "")
+    return Workload(name, seed, n_q_heads, n_kv_heads, head_dim, kv, "f16", "f16",
                     n, perm, ops, [0], {0: src}, group_size=group if kv == "int4" else 0,
-                    num_sink_blocks=1, sink_blocks_per_seq=1,
-                    sink_free_order=np.arange(1), outlier_channels=outl,
+                    num_sink_blocks=n_sink, sink_blocks_per_seq=1,
+                    sink_free_order=rng(seed, 5).permutation(n_sink) if window else np.arange(1),
+                    outlier_channels=outl, window_tokens=window,
                     extra={"lengths": [length + steps], "steps": steps, "prefill": length})
+
+
+def window_batch(lengths, steps=0, window=128, group=64, kv="int4", n_q_heads=32, n_kv_heads=8,
+                 head_dim=128, seed=12):
+    """Sequences of the given lengths with a one-block FP16 sink and a local
+    FP16 window of ``window`` tokens, then ``steps`` decode steps (one token
+    per sequence, each followed by a settle), INT4 groups of ``group`` or
+    FP8 body, 1 % outlier channels x10."""
+    lengths = [int(L) for L in lengths]
+    B = len(lengths)
+    body = sum(max(0, -(-(L + steps) // BLOCK) - 1) for L in lengths)
+    n = max(1, _pool_size(body))
+    n_sink = B * (1 + -(-window // BLOCK) + 2)
+    ops = []
+    src = {}
+    for b, L in enumerate(lengths):
+        ops += [("create",), ("reserve", b, L), ("settle", b)]
+        src[b] = [(1, b, L)]
+    for s in range(steps):
+        for b in range(B):
+            ops += [("reserve", b, 1), ("settle", b)]
+            src[b].append((6, s * 4096 + b, 1))
+    n_o = max(1, int(round(0.01 * n_kv_heads * head_dim)))
+    outl = np.sort(rng(seed, 4).choice(n_kv_heads * head_dim, size=n_o, replace=False))
+    return Workload(f"window-{kv}-w{window}", seed, n_q_heads, n_kv_heads, head_dim, kv, "f16", "f16",
+                    n, rng(seed, 0).permutation(n), ops, list(range(B)), src,
+                    group_size=group if kv == "int4" else 0, num_sink_blocks=n_sink,
+                    sink_blocks_per_seq=1, sink_free_order=rng(seed, 5).permutation(n_sink),
+                    outlier_channels=outl, window_tokens=window,
+                    extra={"lengths": [L + steps for L in lengths], "steps": steps})
 
 
 def shared_prefix(seed=5, prefix=2000, n_children=32, max_suffix=512):
@@ -230,5 +268,7 @@ def by_name(name, **kw):
         "shared-prefix": shared_prefix,
         "shared-prefix-partial": lambda **k: shared_prefix(prefix=1992, **k),
         "spec-verify": llama3_8b,   # the same batch, scored by a verify step
+        # the pages' own scheme: FP16 sink block and last-128-token window, INT4 g = 64
+        "mixed-window": lambda **k: mixed_precision(kv="int4", group=64, window=128, **k),
     }
     return table[name](**kw)

@@ -12,6 +12,7 @@ import torch
 
 from oracle import attention as AT
 from oracle import quant as QT
+from oracle.allocator import Pool, replay
 
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -21,28 +22,48 @@ def cast64(x, dt):
     return torch.from_numpy(np.ascontiguousarray(x)).to(TORCH_DT[dt]).to(torch.float64).numpy()
 
 
-def stored_values(wl, sid):
+def oracle_pool(wl):
+    """The oracle's pool after the workload's op log (tables, arenas)."""
+    pool = Pool(wl.num_blocks, wl.num_sink_blocks, wl.sink_blocks_per_seq,
+                body_free_order=wl.body_free_order, sink_free_order=wl.sink_free_order,
+                window_tokens=wl.window_tokens)
+    replay(pool, wl.ops)
+    return pool
+
+
+def fp16_tokens(wl, pool, sid):
+    """Per token of the sequence: True where its block is in the FP16 arena."""
+    t = pool.seq_table(sid)
+    return np.array([t[p // 16] >= wl.num_blocks for p in range(pool.seq_len(sid))], dtype=bool)
+
+
+def stored_values(wl, sid, fp16=None):
     """Float64 [L][Hkv][D] K and V the pool must hold for sequence sid, plus
-    (for quantized bodies) the oracle's codes/scales/zeros of the body tokens."""
+    (for quantized bodies) the oracle's codes/scales/zeros of every token
+    (the pool holds them for the tokens of body blocks).  ``fp16``: per-token
+    mask of the FP16-arena tokens (default: the sink blocks)."""
     K, V = wl.seq_tokens(sid)
     if wl.kv_dtype in TORCH_DT:
         return cast64(K, wl.kv_dtype), cast64(V, wl.kv_dtype), None
     Kh = cast64(K, "f16").astype(np.float16)
     Vh = cast64(V, "f16").astype(np.float16)
-    sink = 16 * wl.sink_blocks_per_seq
+    L = Kh.shape[0]
+    if fp16 is None:
+        fp16 = np.arange(L) < 16 * wl.sink_blocks_per_seq
     Kq, Vq = Kh.astype(np.float64), Vh.astype(np.float64)
     codes = {}
-    if Kh.shape[0] <= sink:
+    if L == 0 or fp16.all():
         return Kq, Vq, {}
+    body = ~fp16
     if wl.kv_dtype == "int4":
         for name, X, out in (("K", Kh, Kq), ("V", Vh, Vq)):
-            q, s, z = QT.int4_quantize(X[sink:], wl.group_size)
-            out[sink:] = QT.int4_dequant(q, s, z, wl.group_size)
+            q, s, z = QT.int4_quantize(X, wl.group_size)
+            out[body] = QT.int4_dequant(q, s, z, wl.group_size)[body]
             codes[name], codes[name + "S"], codes[name + "Z"] = q, s, z
     else:
         for name, X, out in (("K", Kh, Kq), ("V", Vh, Vq)):
-            c, s = QT.fp8_quantize(X[sink:])
-            out[sink:] = QT.fp8_dequant(c, s)
+            c, s = QT.fp8_quantize(X)
+            out[body] = QT.fp8_dequant(c, s)[body]
             codes[name], codes[name + "S"] = c, s
     return Kq, Vq, codes
 
@@ -61,10 +82,11 @@ def expected(wl, seqs=None, pairs=None):
     if pairs is not None:
         for b, h in pairs:
             want.setdefault(b, []).append(h)
+    pool = oracle_pool(wl) if wl.window_tokens else None
     for b, sid in enumerate(seqs):
         if want is not None and b not in want:
             continue
-        K, V, _ = stored_values(wl, sid)
+        K, V, _ = stored_values(wl, sid, fp16_tokens(wl, pool, sid) if pool else None)
         full = AT.attention_one(q[b], K, V, wl.scale)
         if want is None:
             out[b] = full
@@ -80,10 +102,11 @@ def expected_verify(wl, n_query, seqs=None, rows=None):
     seqs = wl.decode_seqs if seqs is None else seqs
     q = cast64(wl.q_verify(n_query), wl.q_dtype)
     out = np.full((len(seqs), n_query, wl.n_q_heads, wl.head_dim), np.nan)
+    pool = oracle_pool(wl) if wl.window_tokens else None
     for b, sid in enumerate(seqs):
         if rows is not None and b not in rows:
             continue
-        K, V, _ = stored_values(wl, sid)
+        K, V, _ = stored_values(wl, sid, fp16_tokens(wl, pool, sid) if pool else None)
         out[b] = AT.verify_attention_one(q[b], K, V, wl.scale)
     return out
 

@@ -74,34 +74,42 @@ def run(wl, order=None, env=None, canary=True):
 
 def check_stored(kv, wl, t, l):
     """Pool bytes read back through the oracle's layout reader hold exactly the
-    values (raw) or codes/scales/zeros (quantized) the oracle expects."""
+    values (raw, FP16 blocks) or codes/scales/zeros (body blocks of a
+    quantized pool) the oracle expects, block by block."""
+    from _ref import fp16_tokens, oracle_pool
     view = AT.PoolView(kv.pool_host_bytes(), desc_dict(wl))
+    pool = oracle_pool(wl)
     for b, sid in enumerate(wl.decode_seqs):
         L = int(l[b])
-        K, V, codes = stored_values(wl, sid)
+        assert [int(x) for x in t[b, :(L + 15) // 16]] == pool.seq_table(sid), f"table seq {sid}"
+        K, V, codes = stored_values(wl, sid, fp16_tokens(wl, pool, sid))
         if codes is None:
             Kg, Vg = view.logical_kv(t[b], L)
             assert np.array_equal(Kg, K) and np.array_equal(Vg, V), f"stored values, seq {sid}"
             continue
-        sink = 16 * wl.sink_blocks_per_seq
-        nb = (L + 15) // 16
-        for j in range(min(wl.sink_blocks_per_seq, nb)):     # raw fp16 sink blocks
-            for h in range(wl.n_kv_heads):
-                kb, vb = view.block_values(int(t[b, j]), h)
-                n = min(16, L - 16 * j)
-                assert np.array_equal(kb[:n], K[16 * j:16 * j + n, h])
-                assert np.array_equal(vb[:n], V[16 * j:16 * j + n, h])
-        if L <= sink:
-            continue
-        ids = [int(x) for x in t[b, wl.sink_blocks_per_seq:nb]]
+        nbk = (L + 15) // 16
+        body = [j for j in range(nbk) if int(t[b, j]) < wl.num_blocks]
+        # the tokens of the body blocks, and their rows in the gathered arrays
+        toks = np.concatenate([np.arange(16 * j, min(16 * j + 16, L)) for j in body]) if body \
+            else np.zeros(0, int)
+        rows = np.concatenate([np.arange(16 * k, 16 * k + min(16, L - 16 * j))
+                               for k, j in enumerate(body)]) if body else np.zeros(0, int)
         for h in range(wl.n_kv_heads):
-            got = view.body_codes(ids, h)
-            n = L - sink
+            for j in range(nbk):                     # raw fp16 blocks (sink or window)
+                bid, n = int(t[b, j]), min(16, L - 16 * j)
+                if bid >= wl.num_blocks:
+                    kb, vb = view.block_values(bid, h)
+                    assert np.array_equal(kb[:n], K[16 * j:16 * j + n, h]), f"fp16 K seq {sid} blk {j}"
+                    assert np.array_equal(vb[:n], V[16 * j:16 * j + n, h]), f"fp16 V seq {sid} blk {j}"
+            if not body:
+                continue
+            got = view.body_codes([int(t[b, j]) for j in body], h)
             for name in codes:
-                want = codes[name][:, h]
-                g = got[name][:n]
+                want = codes[name][toks, h]
+                g = got[name][rows]
                 if name.endswith("S") or name.endswith("Z"):
-                    assert np.array_equal(g.view(np.uint16), want.view(np.uint16)), f"{name} h{h}"
+                    assert np.array_equal(g.view(np.uint16), want.view(np.uint16)), \
+                        f"{name} seq {sid} h{h}"
                 else:
                     assert np.array_equal(g, want), f"codes {name} seq {sid} head {h}"
 
@@ -428,3 +436,34 @@ def test_verify_full_llama3_8b_sampled():
     rows = list(np.random.default_rng(7).choice(wl.batch, 12, replace=False))
     ref = expected_verify(wl, 6, rows=rows)
     assert_close(out, ref, "bf16", "verify llama3-8b sampled")
+
+
+
+# ---- local FP16 window + INT4 g = 64 body: routing, migration, decode -----------
+WINDOW_LENS = [1, 100, 143, 144, 145, 160, 1000, 3000]
+
+
+@pytest.mark.parametrize("kvdt,group", [("int4", 64), ("fp8", 0), ("int4", 128)])
+def test_window_storage_and_decode(kvdt, group):
+    """Prefill (old blocks quantized on write), 20 decode steps each followed
+    by a settle (blocks leaving the window quantized by the migration kernel):
+    every FP16 block holds its exact fp16 values, every body block the
+    oracle's codes, scales and zeros; decode and a verify step match the
+    oracle on the same stored values."""
+    from _ref import expected_verify
+    wl = W.window_batch(WINDOW_LENS, steps=20, window=128, group=group or 64, kv=kvdt, seed=131)
+    kv, out, t, l = run(wl)
+    check_stored(kv, wl, t, l)
+    assert_close(out, expected(wl), "f16", f"window decode {kvdt} g{group}")
+    _, outv = run_verify(wl, 6)
+    assert_close(outv, expected_verify(wl, 6), "f16", f"window verify {kvdt} g{group}")
+
+
+def test_full_mixed_window():
+    """The pages' scheme on the mixed-precision workload: 65,536 + 64 tokens,
+    FP16 sink block and last-128-token window, INT4 groups of 64."""
+    wl = W.by_name("mixed-window")
+    kv, out, t, l = run(wl)
+    check_stored(kv, wl, t, l)
+    err = assert_close(out, expected(wl), "f16", "mixed window full")
+    log(f"[gpu] mixed window full max err {err:.3g}")

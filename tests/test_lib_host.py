@@ -71,13 +71,15 @@ def assert_same(kv: PagedKV, oracle: Pool, res_lib, res_or):
     ("shared-prefix-partial", {"n_children": 8, "max_suffix": 60}),
     ("mixed-int4", {"length": 300, "steps": 20}),
     ("mixed-fp8", {"length": 33, "steps": 40}),
+    ("mixed-window", {"length": 300, "steps": 40}),
 ])
 def test_workload_op_logs_match_oracle(libpa, name, kw):
     wl = W.by_name(name, **kw)
     kv = PagedKV(wl, device=None)
     res_lib = kv.replay(write=False)
     oracle = Pool(wl.num_blocks, wl.num_sink_blocks, wl.sink_blocks_per_seq,
-                  body_free_order=wl.body_free_order, sink_free_order=wl.sink_free_order)
+                  body_free_order=wl.body_free_order, sink_free_order=wl.sink_free_order,
+                  window_tokens=wl.window_tokens)
     res_or = replay(oracle, wl.ops)
     assert_same(kv, oracle, res_lib, res_or)
     if name == "shared-prefix-partial":     # one clone per child that wrote a suffix
@@ -169,6 +171,37 @@ def test_speculative_rollback_op_logs_match_oracle(libpa, seed):
     res_or = replay(oracle, ops)
     assert_same(kv, oracle, res_lib, res_or)
     assert B.pa_num_free(kv.pool, 0) == oracle.num_free(0)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_window_op_logs_match_oracle(libpa, seed):
+    """Local FP16 window: reserve routing, settle (migrations popped LIFO,
+    FP16 blocks returned), forks, truncation, and the refusals, library vs
+    oracle on random logs."""
+    rnd = random.Random(200 + seed)
+    wl = W.window_batch([rnd.randrange(1, 90) for _ in range(3)], steps=3, window=32)
+    ops = list(wl.ops)
+    nseq = 3
+    for _ in range(60):
+        k = rnd.randrange(5)
+        s_ = rnd.randrange(nseq + 1)
+        if k == 0:
+            ops.append(("reserve", s_, rnd.choice([1, 1, 2, 15, 33])))
+        elif k == 1:
+            ops.append(("settle", s_))
+        elif k == 2:
+            ops.append(("fork", s_))
+            nseq += 1
+        elif k == 3:
+            ops.append(("truncate", s_, rnd.randrange(0, 80)))
+        else:
+            ops.append(("release", s_))
+    kv = PagedKV(wl, device=None)
+    res_lib = kv.replay(ops, write=False)
+    oracle = Pool(wl.num_blocks, wl.num_sink_blocks, 1, body_free_order=wl.body_free_order,
+                  sink_free_order=wl.sink_free_order, window_tokens=32)
+    res_or = replay(oracle, ops)
+    assert_same(kv, oracle, res_lib, res_or)
 
 
 @pytest.mark.parametrize("kv_dtype,D,g,N,S", [
