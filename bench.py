@@ -43,6 +43,9 @@ WORKLOADS = {
                   "32 q / 8 kv heads, head_dim 128, 1% outlier channels x10",
     "mixed-fp8": "mixed precision: 1 x 65,536 (+64 appended) tokens, FP16 sink block, FP8 E4M3 body, "
                  "32 q / 8 kv heads, head_dim 128, 1% outlier channels x10",
+    "mixed-window": "mixed precision with a local window: 1 x 65,536 (+64 appended, each settled) "
+                    "tokens, FP16 sink block and last-128-token FP16 window, INT4 g64 body, 32 q / 8 kv "
+                    "heads, head_dim 128, 1% outlier channels x10",
     "shared-prefix": "shared prefix: 32 forks of a 2,000-token prompt + U[0,512] suffixes, 64 q / 8 kv "
                      "heads, head_dim 128, bf16",
     "shared-prefix-partial": "shared prefix (1,992-token prompt, one CoW clone per writing fork), 64 q / "
@@ -65,15 +68,21 @@ def kv_bytes_per_token(wl):
     return 2 * H * per
 
 
-def algorithmic_bytes(wl, lens):
+def algorithmic_bytes(wl, lens, tables):
     """K/V bytes the decode must read: quantized body tokens at their packed
-    size, sink tokens at fp16."""
+    size, tokens of FP16 blocks (sink and window: table ids >= num_blocks) at
+    fp16."""
     per = kv_bytes_per_token(wl)
-    if wl.sink_blocks_per_seq:
-        sink = 16 * wl.sink_blocks_per_seq
-        raw = 2 * wl.n_kv_heads * wl.head_dim * 2
-        return int(sum(min(L, sink) * raw + max(0, L - sink) * per for L in lens))
-    return int(sum(lens) * per)
+    if not wl.num_sink_blocks:
+        return int(sum(lens) * per)
+    raw = 2 * wl.n_kv_heads * wl.head_dim * 2
+    total = 0
+    for row, L in zip(tables, lens):
+        nb = (L + 15) // 16
+        fp16 = np.asarray(row[:nb]) >= wl.num_blocks
+        tok = np.minimum(16, L - 16 * np.arange(nb))
+        total += int(tok[fp16].sum()) * raw + int(tok[~fp16].sum()) * per
+    return int(total)
 
 
 def cpu_baseline(kv, wl, t, l, budget_s, nq=1):
@@ -103,7 +112,7 @@ def cpu_baseline(kv, wl, t, l, budget_s, nq=1):
             AT.verify_attention_one(q[done], K, V, wl.scale)
         secs += time.perf_counter() - t0
         done += 1
-    byts = algorithmic_bytes(wl, [int(x) for x in l[:done]])
+    byts = algorithmic_bytes(wl, [int(x) for x in l[:done]], t[:done])
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -228,7 +237,7 @@ def main():
     split_ms = [a.elapsed_time(b) for a, b in split_ev]
     split_avg = float(np.mean(split_ms))
 
-    byts = algorithmic_bytes(wl, lens)
+    byts = algorithmic_bytes(wl, lens, t)
     kv_gbs = byts / (ms_step * 1e-3) / 1e9
     achieved = byts / (split_avg * 1e-3) / 1e9
 

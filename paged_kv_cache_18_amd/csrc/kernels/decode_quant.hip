@@ -1,6 +1,6 @@
-// Matrix-core decode split kernel for mixed-precision pools: FP16 sink blocks
-// plus an asymmetric INT4 (one group per token and head) or FP8 E4M3 body,
-// head_dim 128, fp16 queries.
+// Matrix-core decode split kernel for mixed-precision pools: FP16 sink and
+// window blocks plus an asymmetric INT4 (groups of 128 or 64 dims per token
+// and head) or FP8 E4M3 body, head_dim 128, fp16 queries.
 //
 // "The 8GB VRAM Breakthrough ...", section 5 ("On-the-Fly Register
 // Dequantization"): the kernel loads the packed codes and their (scale, zero)
@@ -10,8 +10,8 @@
 //
 // The dequantization is folded out of the dot products so that the
 // matrix-core operands stay exact:
-//   INT4  S[t] = s_t * (sum_d q_d c_td - z_t * sum_d q_d)
-//         O[d] = sum_t c_td (s_t p_t) - sum_t z_t s_t p_t
+//   INT4  S[t] = sum_k s_tk * (sum_{d in k} q_d c_td - z_tk * sum_{d in k} q_d)
+//         O[d] = sum_t c_td (s_tk p_t) - sum_t z_tk s_tk p_t   (k = group of d)
 //   FP8   S[t] = s_t * sum_d q_d e(c_td),  O[d] = sum_t e(c_td) (s_t p_t)
 // The codes enter the fp16 matrix cores exactly: an INT4 nibble n becomes the
 // fp16 value n (0x6400|n is 1024+n, then an exact packed-fp16 subtract); an
@@ -57,33 +57,91 @@ __device__ inline uint32_t fp8pair(uint32_t y) {
 __device__ inline float h_lo(uint32_t w) { return f16_bits_to_f32(uint16_t(w & 0xFFFFu)); }
 __device__ inline float h_hi(uint32_t w) { return f16_bits_to_f32(uint16_t(w >> 16)); }
 
+// NG = scale groups per token and head (head_dim / group size: 1 or 2).
+template <int NG>
 struct BufI4 {
-  u32x4 kc, vc;          // K codes (dims 32kk+8g+0..7 per dword kk), V codes (dword j: tokens 4g+i, dims 8r+2j, +1)
-  u32x2 ks, kz, vs, vz;  // fp16 scale/zero of tokens 4g..4g+3
+  u32x4 kc, vc;  // K codes (dims 32kk+8g+0..7 per dword kk), V codes (dword j: tokens 4g+i, dims 8r+2j, +1)
+  // fp16 (scale, zero) of tokens 4g..4g+3, token-major (token i, group k at half i*NG+k)
+  uint32_t ks[2 * NG], kz[2 * NG], vs[2 * NG], vz[2 * NG];
 };
 
 struct BufF8 {
   u32x4 kc0, kc1, vc0, vc1;  // K units s = 0, 1; V units u = 0, 1
-  u32x2 ks, vs;
+  uint32_t ks[2], vs[2];
 };
 
-template <int KIND>
+// One FP16 block of the sink/window arena for one head: K in the matrix-core
+// operand order, V^T in 4 dwordx4 per lane.
+struct Buf16 {
+  h8 k[4];
+  u32x4 v[4];
+};
+
+template <int KIND, int NG>
 struct Quant;
 
-template <>
-struct Quant<kInt4> {
-  typedef BufI4 Buf;
+template <int NG>
+struct Quant<kInt4, NG> {
+  typedef BufI4<NG> Buf;
 };
 
 template <>
-struct Quant<kFp8> {
+struct Quant<kFp8, 1> {
   typedef BufF8 Buf;
 };
 
+// NW consecutive dwords at p (NW = 2: 8-byte aligned; 4, 8: 16-byte aligned)
+template <int NW>
+__device__ inline void load_words(const uint8_t* p, uint32_t (&d)[NW]) {
+  if constexpr (NW == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    d[0] = v[0];
+    d[1] = v[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[4 * i + e] = v[e];
+    }
+  }
+}
+
+// fp16 number idx of a dword array (idx a compile-time constant after unrolling)
+template <int NW>
+__device__ inline float half_at(const uint32_t (&m)[NW], int idx) {
+  return (idx & 1) ? h_hi(m[idx >> 1]) : h_lo(m[idx >> 1]);
+}
+
+// Scale/zero of token i in group `sel` (a per-lane group index < NG).
+template <int NG>
+__device__ inline float half_sel(const uint32_t (&m)[2 * NG], int i, int sel) {
+  float v = half_at(m, i * NG);
+#pragma unroll
+  for (int k = 1; k < NG; ++k) v = sel == k ? half_at(m, i * NG + k) : v;
+  return v;
+}
+
 // NB = register buffers per wave (NB-1 blocks prefetched ahead).
-template <int KIND, int NB>
+//
+// Groups (NG > 1, INT4 only; the launch guarantees NG * G <= 16): the
+// matrix-core B operand has 16 columns and a KV head serves G query heads, so
+// column c computes head c % G with the V weights scaled by group c / G.
+// Output tile row r holds dim 8r + T, which lies in group (8r) / group_size =
+// g * NG / 4 for the rows 4g..4g+3 a lane holds: lane (g, c) keeps column
+// c - (g * NG / 4) * G.  The scores of the copies are identical, so are their
+// softmax statistics.  On the K side each group has its own accumulator
+// (dims 32kk.. lie in group kk * NG / 4).
+//
+// FP16 blocks (sink and window): a table row reads sink blocks, then body
+// blocks, then the FP16 blocks of the window (ids >= num_blocks).  The body
+// loop runs over every non-sink block of the piece and gives the window's
+// blocks no weight; the window's run at the end of the piece is found by a
+// backward scan of the table (issued before the body loop, read after it) and
+// streamed, with the piece's sink blocks, by a second pipelined loop.
+template <int KIND, int NB, int NG>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 3 : 2))) void decode_split_quant(DecodeArgs a) {
-  typedef typename Quant<KIND>::Buf Buf;
+  typedef typename Quant<KIND, NG>::Buf Buf;
   typedef Mfma<_Float16> MF;
   __shared__ Shared sh;
 
@@ -92,7 +150,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   const int g = lane >> 4, c = lane & 15;
   const PoolDev& p = a.pool;
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H, N = p.num_blocks;
-  const int SP = p.sink_per_seq;
+  const int SP = p.sink_per_seq, NS = p.num_sink_blocks;
+  const int qcol = c < NG * G ? (NG == 1 ? c : c % G) : -1;  // query head (within the group) of column c
+  const int gsel = NG == 1 ? 0 : min(c / G, NG - 1);  // scale group of column c
+  const int keep = c - (NG == 1 ? 0 : (g * NG / 4) * G);  // column this lane writes
   zero_empty_rows<_Float16>(a);
   const Units um = setup_units(a, sh, w, lane);
   int b = 0, fb = 0;
@@ -101,12 +162,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   const uint8_t* base = p.base;
   const int32_t* trow = a.tables;
   int h = 0, L = 0;
-  h8 qp[4];            // Q^T fragments in the code's element order
-  float qsum = 0.f;    // sum of the head's query (INT4 zero-point term)
+  h8 qp[4];         // Q^T fragments in the code's element order
+  float qs[NG];     // per-group sums of the head's query (INT4 zero-point terms)
   f32x4 o[kNT];
   float m_ref = -__builtin_inff(), l_run = 0.f, corr = 0.f;
 
   auto ok = [&](int id) { return id >= 0 && id < N; };
+  auto ok16 = [&](int id) { return id >= N && id < N + NS; };
 
   // softmax update for one block's 4 scores per lane; returns the weights
   auto softmax = [&](const float (&x)[4], int valid, float (&pw)[4]) {
@@ -135,44 +197,47 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     const size_t sid = size_t(ok(id) ? id : 0) * H + h;  // unconditional load
     const uint8_t* kc = base + p.off[kArrK] + sid * p.slab[kArrK];
     const uint8_t* vc = base + p.off[kArrV] + sid * p.slab[kArrV];
-    const uint8_t* ks = base + p.off[kArrKS] + sid * p.slab[kArrKS] + 8 * g;
-    const uint8_t* vs = base + p.off[kArrVS] + sid * p.slab[kArrVS] + 8 * g;
+    const uint8_t* ks = base + p.off[kArrKS] + sid * p.slab[kArrKS] + 8 * NG * g;
+    const uint8_t* vs = base + p.off[kArrVS] + sid * p.slab[kArrVS] + 8 * NG * g;
     if constexpr (KIND == kInt4) {
       bf.kc = *reinterpret_cast<const u32x4*>(kc + lane * 16);
       bf.vc = *reinterpret_cast<const u32x4*>(vc + lane * 16);
-      bf.ks = *reinterpret_cast<const u32x2*>(ks);
-      bf.kz = *reinterpret_cast<const u32x2*>(base + p.off[kArrKZ] + sid * p.slab[kArrKZ] + 8 * g);
-      bf.vs = *reinterpret_cast<const u32x2*>(vs);
-      bf.vz = *reinterpret_cast<const u32x2*>(base + p.off[kArrVZ] + sid * p.slab[kArrVZ] + 8 * g);
+      load_words(ks, bf.ks);
+      load_words(base + p.off[kArrKZ] + sid * p.slab[kArrKZ] + 8 * NG * g, bf.kz);
+      load_words(vs, bf.vs);
+      load_words(base + p.off[kArrVZ] + sid * p.slab[kArrVZ] + 8 * NG * g, bf.vz);
     } else {
       bf.kc0 = *reinterpret_cast<const u32x4*>(kc + lane * 16);
       bf.kc1 = *reinterpret_cast<const u32x4*>(kc + 1024 + lane * 16);
       bf.vc0 = *reinterpret_cast<const u32x4*>(vc + lane * 16);
       bf.vc1 = *reinterpret_cast<const u32x4*>(vc + 1024 + lane * 16);
-      bf.ks = *reinterpret_cast<const u32x2*>(ks);
-      bf.vs = *reinterpret_cast<const u32x2*>(vs);
+      load_words(ks, bf.ks);
+      load_words(vs, bf.vs);
     }
   };
 
   auto consume = [&](int valid, const Buf& bf) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float ksc[4], vsc[4];
-    ksc[0] = h_lo(bf.ks[0]); ksc[1] = h_hi(bf.ks[0]); ksc[2] = h_lo(bf.ks[1]); ksc[3] = h_hi(bf.ks[1]);
-    vsc[0] = h_lo(bf.vs[0]); vsc[1] = h_hi(bf.vs[0]); vsc[2] = h_lo(bf.vs[1]); vsc[3] = h_hi(bf.vs[1]);
     float x[4];
     if constexpr (KIND == kInt4) {
+      f32x4 acc[NG];
+#pragma unroll
+      for (int k = 0; k < NG; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const uint32_t cw = bf.kc[kk];
         const u32x4 av = {nib2h(cw, 0), nib2h(cw, 4), nib2h(cw, 8), nib2h(cw, 12)};
-        acc = MF::qk(__builtin_bit_cast(h8, av), qp[kk], acc);
+        acc[kk * NG / 4] = MF::qk(__builtin_bit_cast(h8, av), qp[kk], acc[kk * NG / 4]);
       }
-      float kzv[4];
-      kzv[0] = h_lo(bf.kz[0]); kzv[1] = h_hi(bf.kz[0]); kzv[2] = h_lo(bf.kz[1]); kzv[3] = h_hi(bf.kz[1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        x[i] = (4 * g + i < valid) ? ksc[i] * (acc[i] - kzv[i] * qsum) * sl2 : -__builtin_inff();
+      for (int i = 0; i < 4; ++i) {
+        float sc = 0.f;
+#pragma unroll
+        for (int k = 0; k < NG; ++k)
+          sc += half_at(bf.ks, i * NG + k) * (acc[k][i] - half_at(bf.kz, i * NG + k) * qs[k]);
+        x[i] = (4 * g + i < valid) ? sc * sl2 : -__builtin_inff();
+      }
     } else {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const u32x4 u = kk < 2 ? bf.kc0 : bf.kc1;
@@ -182,23 +247,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        x[i] = (4 * g + i < valid) ? ksc[i] * acc[i] * sl2 : -__builtin_inff();
+        x[i] = (4 * g + i < valid) ? half_at(bf.ks, i) * acc[i] * sl2 : -__builtin_inff();
     }
     float pw[4];
     softmax(x, valid, pw);
-    // weights times the V scale; tail tokens' metadata may be garbage: select
+    // weights times the V scale of this column's group; tail tokens' metadata
+    // may be garbage: select
     float pv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pv[i] = (4 * g + i < valid) ? vsc[i] * pw[i] : 0.f;
+    for (int i = 0; i < 4; ++i) pv[i] = (4 * g + i < valid) ? half_sel<NG>(bf.vs, i, gsel) * pw[i] : 0.f;
     // FP8: zero the bytes of tail tokens (unwritten slots may hold NaN codes)
     const int t0 = 4 * g;
     const uint32_t vmask = (t0 + 0 < valid ? 0x000000FFu : 0u) | (t0 + 1 < valid ? 0x0000FF00u : 0u) |
                            (t0 + 2 < valid ? 0x00FF0000u : 0u) | (t0 + 3 < valid ? 0xFF000000u : 0u);
     if constexpr (KIND == kInt4) {
-      float vzv[4];
-      vzv[0] = h_lo(bf.vz[0]); vzv[1] = h_hi(bf.vz[0]); vzv[2] = h_lo(bf.vz[1]); vzv[3] = h_hi(bf.vz[1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) corr += (4 * g + i < valid) ? vzv[i] * pv[i] : 0.f;
+      for (int i = 0; i < 4; ++i) corr += (4 * g + i < valid) ? half_sel<NG>(bf.vz, i, gsel) * pv[i] : 0.f;
     }
     // B operand in the token order of the code pairs: INT4 (t0, t2), (t1, t3);
     // FP8 natural
@@ -229,19 +293,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     }
   };
 
-  // ---- FP16 sink blocks (raw layout, natural element order) ----------------------
-  auto consume_sink = [&](int id, int valid) {
-    const size_t sid = size_t(id - N) * H + h;
+  // ---- FP16 blocks of the sink/window arena (raw fp16 in operand order) ----------
+  auto fetch16 = [&](int id, Buf16& bf) {
+    const size_t sid = size_t(ok16(id) ? id - N : 0) * H + h;  // unconditional load
     const _Float16* ks = reinterpret_cast<const _Float16*>(base + p.off[kArrSK] + sid * p.slab[kArrSK]);
     const _Float16* vs = reinterpret_cast<const _Float16*>(base + p.off[kArrSV] + sid * p.slab[kArrSV]);
-    const _Float16* qn = static_cast<const _Float16*>(a.q) + (size_t(b) * Hq + h * G + c) * kD + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) bf.k[kk] = *reinterpret_cast<const h8*>(ks + (kk * 64 + lane) * 8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) bf.v[u] = *reinterpret_cast<const u32x4*>(vs + (u * 64 + lane) * 8);
+  };
+
+  // qf: the query fragments in natural element order
+  auto consume16 = [&](int valid, const Buf16& bf, const h8 (&qf)[4]) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const h8 kf = *reinterpret_cast<const h8*>(ks + (kk * 64 + lane) * 8);
-      const h8 qf = c < G ? *reinterpret_cast<const h8*>(qn + 32 * kk) : h8{};
-      acc = MF::qk(kf, qf, acc);
-    }
+    for (int kk = 0; kk < 4; ++kk) acc = MF::qk(bf.k[kk], qf[kk], acc);
     float x[4], pw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (4 * g + i < valid) ? acc[i] * sl2 : -__builtin_inff();
@@ -258,7 +325,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     const uint32_t m23 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      u32x4 dw = *reinterpret_cast<const u32x4*>(vs + (u * 64 + lane) * 8);
+      u32x4 dw = bf.v[u];
       dw[0] &= m01;  // unwritten tail slots may hold any bits
       dw[1] &= m23;
       dw[2] &= m01;
@@ -287,24 +354,31 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   while (next_piece(a, pos, pos1, b, fb, h, jbeg, jend, nb)) {
     L = seq_len(a, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
+    const int lo = max(jbeg, SP);  // first non-sink block of the piece
+    // the table's last 64 entries of the piece, for the window scan below
+    int tid = trow[max(jend - 1 - lane, 0)];
     {
-      // Q^T fragment of head c (dims 32kk + 8g + 0..7), permuted into the order
-      // in which the code conversion delivers the K elements
-      const _Float16* qn = static_cast<const _Float16*>(a.q) + (size_t(b) * Hq + h * G + c) * kD + 8 * g;
-      float part = 0.f;
+      // Q^T fragment of head qcol (dims 32kk + 8g + 0..7), permuted into the
+      // order in which the code conversion delivers the K elements
+      const _Float16* qn =
+          static_cast<const _Float16*>(a.q) + (size_t(b) * Hq + h * G + max(qcol, 0)) * kD + 8 * g;
+#pragma unroll
+      for (int k = 0; k < NG; ++k) qs[k] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const h8 q = c < G ? *reinterpret_cast<const h8*>(qn + 32 * kk) : h8{};
+        const h8 q = qcol >= 0 ? *reinterpret_cast<const h8*>(qn + 32 * kk) : h8{};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part += float(q[e]);
+        for (int e = 0; e < 8; ++e) qs[kk * NG / 4] += float(q[e]);
         if constexpr (KIND == kInt4)
           qp[kk] = h8{q[0], q[4], q[1], q[5], q[2], q[6], q[3], q[7]};
         else
           qp[kk] = q;
       }
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
-      qsum = part;
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        qs[k] += __shfl_xor(qs[k], 16, 64);
+        qs[k] += __shfl_xor(qs[k], 32, 64);
+      }
     }
 #pragma unroll
     for (int T_ = 0; T_ < kNT; ++T_) o[T_] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -312,17 +386,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     l_run = 0.f;
     corr = 0.f;
 
-    // sink blocks of the piece (logical blocks < SP), one at a time
-    const int send = min(jend, SP);
-    for (int j = jbeg + w; j < send; j += kWaves) {
-      const int id = trow[j];
-      if (id >= N && id < N + p.num_sink_blocks) consume_sink(id, L - 16 * j);
-    }
-
     // body blocks, software-pipelined NB-1 blocks ahead with NB register
     // buffers; loads are unconditional so no branch separates them from
     // their waits (past the end the last block is re-read: an L2 hit)
-    const int jw = max(jbeg, SP) + w;
+    const int jw = lo + w;
     const int n = jw < jend ? (jend - jw + kWaves - 1) / kWaves : 0;
     if (n > 0) {
       auto id_of = [&](int k) { return trow[jw + kWaves * min(k, n - 1)]; };
@@ -350,7 +417,57 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
         if (k + s < n) consume(valid_of(k + s, ids[s]), buf[s]);
     }
 
-    // ---- finish the piece: zero-point correction, FP8 scale, merge ----------------
+    // the window's FP16 run [jt, jend): count FP16 ids backward from jend - 1
+    int jt = jend;
+    if (p.window_tokens > 0 && lo < jend) {
+      for (int top = jend;;) {
+        const int j = top - 1 - lane;
+        const uint64_t fp = __ballot(j >= lo && ok16(tid));
+        const int run = fp == ~uint64_t(0) ? 64 : __builtin_ctzll(~fp);
+        jt = top - run;
+        if (run < 64 || jt <= lo) break;
+        top = jt;
+        tid = trow[max(top - 1 - lane, 0)];
+      }
+    }
+
+    // FP16 blocks: the piece's sink blocks [jbeg, min(jend, SP)) and the
+    // window run [jt, jend), pipelined one block ahead
+    const int ns = max(0, min(jend, SP) - jbeg);
+    const int nf = ns + (jend - jt);
+    const int n16 = w < nf ? (nf - w + kWaves - 1) / kWaves : 0;
+    if (n16 > 0) {
+      h8 qf[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const h8 q = qp[kk];
+        if constexpr (KIND == kInt4)
+          qf[kk] = h8{q[0], q[2], q[4], q[6], q[1], q[3], q[5], q[7]};
+        else
+          qf[kk] = q;
+      }
+      auto j16 = [&](int k) {
+        const int i = w + kWaves * min(k, n16 - 1);
+        return i < ns ? jbeg + i : jt + (i - ns);
+      };
+      auto valid16 = [&](int k, int id) { return ok16(id) ? L - 16 * j16(k) : 0; };
+      Buf16 bb[2];
+      int ids[2];
+      ids[0] = trow[j16(0)];
+      fetch16(ids[0], bb[0]);
+      int k = 0;
+      for (; k + 2 <= n16; k += 2) {
+        ids[1] = trow[j16(k + 1)];
+        fetch16(ids[1], bb[1]);
+        consume16(valid16(k, ids[0]), bb[0], qf);
+        ids[0] = trow[j16(k + 2)];
+        fetch16(ids[0], bb[0]);
+        consume16(valid16(k + 1, ids[1]), bb[1], qf);
+      }
+      if (k < n16) consume16(valid16(k, ids[0]), bb[0], qf);
+    }
+
+    // ---- finish the piece: zero-point correction, merge ------------------------------
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
     if constexpr (KIND == kInt4) {
@@ -359,7 +476,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
 #pragma unroll
       for (int T_ = 0; T_ < kNT; ++T_) o[T_] -= corr;
     }
-    stash_piece(sh, w, g, c, o, m_ref, l_run);
+    if (keep >= 0) stash_piece(sh, w, g, keep, o, m_ref, l_run);
     finish_piece<_Float16>(a, sh, out_map(a), jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, h,
                       fb + h * nb, nb, um);
     pos += jend - jbeg;
@@ -370,59 +487,77 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
 
 }  // namespace
 
-// Prefetch depth: PA_QUANT_NB = 2 (default, 3 waves per SIMD), 3, 4 or 6
-// (2 waves per SIMD).
+// Prefetch depth: PA_QUANT_NB = 2 (3 waves per SIMD), 3, 4 or 6 (2 waves per
+// SIMD).  Default 2 for one scale group per token; with two groups the
+// buffers' extra scale/zero words do not fit three waves, default 3.
+// (Read at every launch, as the other tuning variables are.)
+template <int NG>
 int quant_nb() {
-  static int nb = 0;
-  if (nb == 0) {
-    const char* e = std::getenv("PA_QUANT_NB");
-    const int v = e ? std::atoi(e) : 2;
-    nb = (v == 3 || v == 4 || v == 6) ? v : 2;
-  }
-  return nb;
+  const char* e = std::getenv("PA_QUANT_NB");
+  const int v = e ? std::atoi(e) : 0;
+  return (v == 2 || v == 3 || v == 4 || v == 6) ? v : (NG == 1 ? 2 : 3);
 }
 
-template <int KIND, int NB>
+template <int KIND, int NB, int NG>
 int occ_of() {
   int n = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_quant<KIND, NB>,
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_quant<KIND, NB, NG>,
                                                                      kWaves * 64, 0);
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 
-template <int KIND>
+template <int KIND, int NG>
 int occ_kind() {
-  switch (quant_nb()) {
-    case 3: return occ_of<KIND, 3>();
-    case 4: return occ_of<KIND, 4>();
-    case 6: return occ_of<KIND, 6>();
-    default: return occ_of<KIND, 2>();
+  switch (quant_nb<NG>()) {
+    case 3: return occ_of<KIND, 3, NG>();
+    case 4: return occ_of<KIND, 4, NG>();
+    case 6: return occ_of<KIND, 6, NG>();
+    default: return occ_of<KIND, 2, NG>();
   }
 }
 
-template <int KIND>
+template <int KIND, int NG>
 void launch_kind(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.max_splits)), block(kWaves * 64);
-  switch (quant_nb()) {
-    case 3: hipLaunchKernelGGL((decode_split_quant<KIND, 3>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_quant<KIND, 4>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((decode_split_quant<KIND, 6>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_split_quant<KIND, 2>), grid, block, 0, s, a); break;
+  switch (quant_nb<NG>()) {
+    case 3: hipLaunchKernelGGL((decode_split_quant<KIND, 3, NG>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_quant<KIND, 4, NG>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((decode_split_quant<KIND, 6, NG>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_split_quant<KIND, 2, NG>), grid, block, 0, s, a); break;
   }
 }
 
-int occupancy_quant(int32_t kv_dtype) {
-  static int cache[2] = {0, 0};
-  const int i = kv_dtype == kInt4 ? 0 : 1;
-  if (cache[i] == 0) cache[i] = i == 0 ? occ_kind<kInt4>() : occ_kind<kFp8>();
-  return cache[i];
+// INT4 scale groups per token and head (1 or 2 here); FP8 has one scale per token
+int groups_of(int32_t kv_dtype, int32_t group_size) {
+  return kv_dtype == kInt4 && group_size > 0 ? kD / group_size : 1;
+}
+
+int occupancy_quant(int32_t kv_dtype, int32_t group_size) {
+  static int cache[3][7] = {};  // [INT4 NG = 1, INT4 NG = 2, FP8][prefetch depth]
+  const int ng = groups_of(kv_dtype, group_size);
+  const int i = kv_dtype == kInt4 ? (ng == 1 ? 0 : 1) : 2;
+  const int nb = i == 1 ? quant_nb<2>() : quant_nb<1>();
+  int& c = cache[i][nb];
+  if (c == 0) {
+    switch (i) {
+      case 0: c = occ_kind<kInt4, 1>(); break;
+      case 1: c = occ_kind<kInt4, 2>(); break;
+      default: c = occ_kind<kFp8, 1>(); break;
+    }
+  }
+  return c;
 }
 
 hipError_t launch_decode_split_quant(const DecodeArgs& a, hipStream_t s) {
-  if (a.pool.kv_dtype == kInt4)
-    launch_kind<kInt4>(a, s);
-  else
-    launch_kind<kFp8>(a, s);
+  if (a.pool.kv_dtype == kInt4) {
+    switch (groups_of(kInt4, a.pool.group_size)) {
+      case 1: launch_kind<kInt4, 1>(a, s); break;
+      case 2: launch_kind<kInt4, 2>(a, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    launch_kind<kFp8, 1>(a, s);
+  }
   return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@ struct PoolDev {
   uint8_t* base;
   int32_t n_kv_heads, head_dim, kv_dtype, group_size, num_blocks, num_sink_blocks;
   int32_t sink_per_seq;  // logical blocks 0..sink_per_seq-1 live in the sink arena
+  int32_t window_tokens;  // > 0: the blocks of the last window_tokens tokens may also be FP16
   size_t off[kNumArr];
   size_t slab[kNumArr];
 };
@@ -63,7 +64,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);
 // Resident workgroups per compute unit of the split kernel `kernel` for a pool
 // of kv_dtype (from the runtime's occupancy calculator; cached).
 // nct: 0 for decode, else the verify step's column tiles (1 or 2).
-int decode_split_occupancy(int32_t kernel, int32_t kv_dtype, int nct);
+int decode_split_occupancy(int32_t kernel, int32_t kv_dtype, int nct, int32_t group_size);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 // Merge launch of the matrix-core kernels (defer_merge = 1).
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);

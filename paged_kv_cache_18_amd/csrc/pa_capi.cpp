@@ -75,6 +75,7 @@ pa::PoolDev dev_view(const pa_pool* p) {
   v.num_blocks = d.num_blocks;
   v.num_sink_blocks = d.num_sink_blocks;
   v.sink_per_seq = d.sink_blocks_per_seq;
+  v.window_tokens = d.window_tokens;
   for (int i = 0; i < pa::kNumArr; ++i) {
     v.off[i] = p->layout.offset[i];
     v.slab[i] = p->layout.slab[i];
@@ -170,10 +171,11 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
   const bool mfma_ok = (d.kv_dtype == pa::kBF16 || d.kv_dtype == pa::kF16) &&
                        q_dtype == d.kv_dtype && d.head_dim == 128 &&
                        (n_query == 1 ? G <= 16 : ncol <= 32) && d.num_sink_blocks == 0;
-  const bool quant_ok = ((d.kv_dtype == pa::kInt4 && d.group_size == d.head_dim) ||
-                         d.kv_dtype == pa::kFp8) &&
-                        q_dtype == pa::kF16 && d.head_dim == 128 && G <= 16 && n_query == 1 &&
-                        d.window_tokens == 0;
+  // INT4 groups of 128 or 64 dims: the matrix-core B operand's 16 columns
+  // hold every query head of the KV head once per group
+  const int32_t ngroups = d.kv_dtype == pa::kInt4 ? d.head_dim / d.group_size : 1;
+  const bool quant_ok = (d.kv_dtype == pa::kInt4 || d.kv_dtype == pa::kFp8) && q_dtype == pa::kF16 &&
+                        d.head_dim == 128 && ngroups <= 2 && ngroups * G <= 16 && n_query == 1;
   const char* force = std::getenv("PA_DECODE_KERNEL");  // "generic" forces the VALU kernel
   const bool generic = force && std::strcmp(force, "generic") == 0;
   pl.kernel = generic ? pa::kKernGeneric
@@ -199,7 +201,8 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
       pl.split_blocks = 0;
       int per_cu = env_int("PA_WG_PER_CU", 0);  // tuning knob; default: resident slots
       if (per_cu <= 0)
-        per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype, n_query == 1 ? 0 : ncol <= 16 ? 1 : 2);
+        per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype, n_query == 1 ? 0 : ncol <= 16 ? 1 : 2,
+                                            d.group_size);
       pl.max_splits = int32_t(std::max<int64_t>(
           1, std::min<int64_t>({w, int64_t(cu_count()) * per_cu, int64_t(kCtrCap / 2)})));
       // queued units: the owner streams static_permille/1000 of its region,

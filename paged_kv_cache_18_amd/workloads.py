@@ -183,16 +183,17 @@ def mixed_precision(seed=4, kv="int4", length=65536, steps=64, group=128,
 
 
 def window_batch(lengths, steps=0, window=128, group=64, kv="int4", n_q_heads=32, n_kv_heads=8,
-                 head_dim=128, seed=12):
+                 head_dim=128, seed=12, settle=True):
     """Sequences of the given lengths with a one-block FP16 sink and a local
     FP16 window of ``window`` tokens, then ``steps`` decode steps (one token
-    per sequence, each followed by a settle), INT4 groups of ``group`` or
+    per sequence, each followed by a settle unless ``settle`` is False: then
+    the blocks that leave the window stay FP16), INT4 groups of ``group`` or
     FP8 body, 1 % outlier channels x10."""
     lengths = [int(L) for L in lengths]
     B = len(lengths)
     body = sum(max(0, -(-(L + steps) // BLOCK) - 1) for L in lengths)
     n = max(1, _pool_size(body))
-    n_sink = B * (1 + -(-window // BLOCK) + 2)
+    n_sink = B * (1 + -(-window // BLOCK) + 2 + (0 if settle else -(-steps // BLOCK)))
     ops = []
     src = {}
     for b, L in enumerate(lengths):
@@ -200,11 +201,11 @@ def window_batch(lengths, steps=0, window=128, group=64, kv="int4", n_q_heads=32
         src[b] = [(1, b, L)]
     for s in range(steps):
         for b in range(B):
-            ops += [("reserve", b, 1), ("settle", b)]
+            ops += [("reserve", b, 1)] + ([("settle", b)] if settle else [])
             src[b].append((6, s * 4096 + b, 1))
     n_o = max(1, int(round(0.01 * n_kv_heads * head_dim)))
     outl = np.sort(rng(seed, 4).choice(n_kv_heads * head_dim, size=n_o, replace=False))
-    return Workload(f"window-{kv}-w{window}", seed, n_q_heads, n_kv_heads, head_dim, kv, "f16", "f16",
+    return Workload(f"window-{kv}-w{window}" + ("" if settle else "-lag"), seed, n_q_heads, n_kv_heads, head_dim, kv, "f16", "f16",
                     n, rng(seed, 0).permutation(n), ops, list(range(B)), src,
                     group_size=group if kv == "int4" else 0, num_sink_blocks=n_sink,
                     sink_blocks_per_seq=1, sink_free_order=rng(seed, 5).permutation(n_sink),

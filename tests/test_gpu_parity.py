@@ -245,13 +245,13 @@ def test_full_long_context_sampled():
     log(f"[gpu] long-context full sampled max err {err:.3g}")
 
 
-@pytest.mark.parametrize("kvdt", ["int4", "fp8"])
+@pytest.mark.parametrize("kvdt,group", [("int4", 128), ("int4", 64), ("fp8", 0)])
 @pytest.mark.parametrize("split", ["1", "3", "0"])
-def test_quantized_split_k_and_kernels_agree(kvdt, split):
+def test_quantized_split_k_and_kernels_agree(kvdt, group, split):
     """The matrix-core quantized kernel (many small pieces when the chunk is
     forced small) and the generic kernel both match the oracle."""
     wl = W.from_lengths([700, 16, 17, 1, 260], 32, 8, 128, kvdt, seed=61,
-                        group=128 if kvdt == "int4" else 0, sink=True, outliers=True)
+                        group=group, sink=True, outliers=True)
     env = {"PA_SPLIT_BLOCKS": split} if split != "0" else {}
     _, out_q, _, _ = run(wl, env=env)
     ref = expected(wl)
@@ -457,6 +457,44 @@ def test_window_storage_and_decode(kvdt, group):
     assert_close(out, expected(wl), "f16", f"window decode {kvdt} g{group}")
     _, outv = run_verify(wl, 6)
     assert_close(outv, expected_verify(wl, 6), "f16", f"window verify {kvdt} g{group}")
+
+
+WINDOW_SPLITS = [{}, {"PA_SPLIT_BLOCKS": "3"}, {"PA_SPLIT_BLOCKS": "1"}]
+_window_ref = {}
+
+
+@pytest.mark.parametrize("kvdt,group", [("int4", 64), ("fp8", 0), ("int4", 128)])
+@pytest.mark.parametrize("window,settle", [(128, False), (1100, True)])
+@pytest.mark.parametrize("split", range(len(WINDOW_SPLITS)))
+def test_window_quant_kernel(kvdt, group, window, settle, split):
+    """The matrix-core quantized kernel on window pools finds each table's
+    FP16 run by scanning it backward: also when the pieces cut the run, when
+    the run is longer than one 64-entry scan (1,100-token window) and when
+    settles lag so that the run still holds blocks already out of the
+    window.  Matches the oracle, and the generic kernel does too."""
+    wl = W.window_batch([1, 17, 500, 1300, 2900], steps=24, window=window, group=group or 64,
+                        kv=kvdt, seed=141, settle=settle)
+    key = (kvdt, group, window, settle)
+    if key not in _window_ref:
+        _window_ref[key] = expected(wl)
+    ref = _window_ref[key]
+    env = WINDOW_SPLITS[split]
+    _, out_q, _, _ = run(wl, env=env)
+    assert_close(out_q, ref, "f16", f"window {kvdt} g{group} w{window} settle={settle} {env}")
+    if split == 0:
+        _, out_g, _, _ = run(wl, env={"PA_DECODE_KERNEL": "generic"})
+        assert_close(out_g, ref, "f16", f"window generic {kvdt} g{group} w{window}")
+
+
+@pytest.mark.parametrize("nb", ["2", "3", "4"])
+def test_int4_g64_eight_query_heads_per_kv_head(nb):
+    """INT4 groups of 64 with 8 query heads per KV head: the matrix-core B
+    operand's 16 columns all in use (each head once per group); every
+    prefetch depth of the kernel."""
+    wl = W.from_lengths([900, 33, 1, 410], 64, 8, 128, "int4", seed=71, group=64, sink=True,
+                        outliers=True)
+    _, out, _, _ = run(wl, env={"PA_QUANT_NB": nb})
+    assert_close(out, expected(wl), "f16", f"int4 g64 G=8 nb{nb}")
 
 
 def test_full_mixed_window():
