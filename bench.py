@@ -221,21 +221,19 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
 
-    # the dominant kernel's launch durations: the same steps again, with HIP
-    # events on the launch stream around every split launch
-    split_ev = []
+    # the dominant kernel's average launch duration: as many split launches
+    # again, back to back on the launch stream between two HIP events (an
+    # event pair around every launch would add its own few microseconds to
+    # each; back to back, only the gaps between launches are counted)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     for _ in range(args.steps):
-        B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, n_new, sh)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
         attn_split()
-        e1.record(stream)
-        split_ev.append((e0, e1))
-        attn_rest()
+    e1.record(stream)
     torch.cuda.synchronize()
-    split_ms = [a.elapsed_time(b) for a, b in split_ev]
-    split_avg = float(np.mean(split_ms))
+    split_avg = e0.elapsed_time(e1) / args.steps
+    attn_rest()
 
     byts = algorithmic_bytes(wl, lens, t)
     kv_gbs = byts / (ms_step * 1e-3) / 1e9

@@ -56,6 +56,32 @@ struct Mfma<_Float16> {
   }
 };
 
+// A block-table entry at a wave-uniform index, read through the scalar
+// (constant) cache: the tables are read-only for the whole call.  A plain
+// load becomes a vector load here (the kernels store to other buffers), and
+// its result needs a wait on the vector-memory counter, which also waits for
+// the K/V blocks already in flight.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ inline int table_entry(const int32_t* p) { return *(const_i32*)p; }
+
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+// with the gfx950 row-swap instructions: plain vector ALU, so no LDS round
+// trip (whose counter wait would also wait for pending scalar loads).  Each
+// swap returns the lane's own value and its partner row's, in some order.
+__device__ inline float rows_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float rows_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ inline int seq_len(const DecodeArgs& a, int b) {
   return min(max(a.lens[b], 0), a.max_seq_len);
 }

@@ -131,8 +131,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
         x[i] = vis[i] ? sc[i] * sl2 : -__builtin_inff();
         bm = fmaxf(bm, x[i]);
       }
-      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      bm = rows_max(bm);
       // The reference only moves when a block's max exceeds it by more than 8
       // (weights stay <= 2^8, far inside fp32 and the two-part 16-bit split),
       // so the accumulators are rarely rescaled.  The result is unchanged:
@@ -220,7 +219,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     // re-read it (an L2 hit, never consumed).
     const int jw = jbeg + w;
     const int n = jw < jend ? (jend - jw + kWaves - 1) / kWaves : 0;
-    auto id_of = [&](int k) { return trow[jw + kWaves * min(k, n - 1)]; };
+    auto id_of = [&](int k) { return table_entry(trow + jw + kWaves * min(k, n - 1)); };
     auto valid_of = [&](int k, int id) { return ok(id) ? L - 16 * (jw + kWaves * k) : 0; };
     if (n > 0) {
       v8 kb[NB][4], vb[NB][4];
@@ -230,14 +229,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
         ids[s] = id_of(s);
         fetch(ids[s], kb[s], vb[s]);
       }
+      // table entries are read one block ahead of the fetch that needs them
+      int nid = id_of(NB - 1);
       int k = 0;
       for (; k + NB <= n; k += NB) {
         prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
 #pragma unroll
         for (int s = 0; s < NB; ++s) {
           const int nxt = (s + NB - 1) % NB;
-          ids[nxt] = id_of(k + s + NB - 1);
+          ids[nxt] = nid;
+          nid = id_of(k + s + NB);
           fetch(ids[nxt], kb[nxt], vb[nxt]);
+          // no instruction of the block's product may move above the next
+          // block's loads (it would wait for data still in flight)
+          __builtin_amdgcn_sched_barrier(0);
           consume(valid_of(k + s, ids[s]), jw + kWaves * (k + s), kb[s], vb[s]);
         }
       }

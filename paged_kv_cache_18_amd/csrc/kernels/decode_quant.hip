@@ -173,8 +173,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   // softmax update for one block's 4 scores per lane; returns the weights
   auto softmax = [&](const float (&x)[4], int valid, float (&pw)[4]) {
     float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    bm = rows_max(bm);
     const bool move = bm > m_ref;
     if (__any(move)) {
       const float m_new = move ? bm : m_ref;
@@ -392,7 +391,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     const int jw = lo + w;
     const int n = jw < jend ? (jend - jw + kWaves - 1) / kWaves : 0;
     if (n > 0) {
-      auto id_of = [&](int k) { return trow[jw + kWaves * min(k, n - 1)]; };
+      auto id_of = [&](int k) { return table_entry(trow + jw + kWaves * min(k, n - 1)); };
       auto valid_of = [&](int k, int id) { return ok(id) ? L - 16 * (jw + kWaves * k) : 0; };
       Buf buf[NB];
       int ids[NB];
@@ -401,14 +400,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
         ids[s] = id_of(s);
         fetch(ids[s], buf[s]);
       }
+      // table entries are read one block ahead of the fetch that needs them
+      int nid = id_of(NB - 1);
       int k = 0;
       for (; k + NB <= n; k += NB) {
         prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
 #pragma unroll
         for (int s = 0; s < NB; ++s) {
           const int nxt = (s + NB - 1) % NB;
-          ids[nxt] = id_of(k + s + NB - 1);
+          ids[nxt] = nid;
+          nid = id_of(k + s + NB);
           fetch(ids[nxt], buf[nxt]);
+          // no instruction of the block's product may move above the next
+          // block's loads (it would wait for data still in flight)
+          __builtin_amdgcn_sched_barrier(0);
           consume(valid_of(k + s, ids[s]), buf[s]);
         }
       }
@@ -453,14 +458,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       auto valid16 = [&](int k, int id) { return ok16(id) ? L - 16 * j16(k) : 0; };
       Buf16 bb[2];
       int ids[2];
-      ids[0] = trow[j16(0)];
+      ids[0] = table_entry(trow + j16(0));
       fetch16(ids[0], bb[0]);
       int k = 0;
       for (; k + 2 <= n16; k += 2) {
-        ids[1] = trow[j16(k + 1)];
+        ids[1] = table_entry(trow + j16(k + 1));
         fetch16(ids[1], bb[1]);
         consume16(valid16(k, ids[0]), bb[0], qf);
-        ids[0] = trow[j16(k + 2)];
+        ids[0] = table_entry(trow + j16(k + 2));
         fetch16(ids[0], bb[0]);
         consume16(valid16(k + 1, ids[1]), bb[1], qf);
       }
@@ -468,11 +473,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     }
 
     // ---- finish the piece: zero-point correction, merge ------------------------------
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
+    l_run = rows_sum(l_run);
     if constexpr (KIND == kInt4) {
-      corr += __shfl_xor(corr, 16, 64);
-      corr += __shfl_xor(corr, 32, 64);
+      corr = rows_sum(corr);
 #pragma unroll
       for (int T_ = 0; T_ < kNT; ++T_) o[T_] -= corr;
     }
