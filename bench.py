@@ -53,8 +53,31 @@ WORKLOADS = {
     "spec-verify": "speculative verify step (gamma = 5: 6 causal queries per sequence) on the "
                    "Llama-3-8B-shaped batch: 64 sequences, lengths U[512,4096], 32 q / 8 kv heads, "
                    "head_dim 128, bf16, shuffled tables",
+    "prefill-chunk": "chunked paged prefill: the last 512-token chunk of 4 prompts of 4,096 tokens "
+                     "(causal over the cached prefix and the chunk), 32 q / 8 kv heads, head_dim 128, "
+                     "bf16, prompts reserved chunk by chunk",
 }
-N_QUERY = {"spec-verify": 6}   # queries per sequence of the step (1 = decode)
+N_QUERY = {"spec-verify": 6, "prefill-chunk": 512}   # queries per sequence of the step (1 = decode)
+# configs whose dominant launch is a matrix-core contraction: roofline in
+# TFLOP/s against the dense bf16 peak
+MFMA_BOUND = {"prefill-chunk"}
+MFMA_PEAK_TFLOPS = 2500.0
+
+
+def queries(wl, config, nq):
+    """The step's queries: decode, verify (gamma + 1) or the last prefill chunk."""
+    if nq == 1:
+        return wl.q()
+    if config == "prefill-chunk":
+        return wl.q_chunk(max(wl.extra["lengths"]) // nq - 1, nq)
+    return wl.q_verify(nq)
+
+
+def causal_flops(lens, nq, n_q_heads, head_dim):
+    """Q K^T and P V multiply-adds of a step whose query i (of nq) sees
+    L - nq + i + 1 tokens: 4 * Hq * D flops per (query, visible token)."""
+    vis = sum(sum(max(0, L - nq + i + 1) for i in range(nq)) for L in lens)
+    return 4.0 * n_q_heads * head_dim * vis
 
 
 def kv_bytes_per_token(wl):
@@ -85,7 +108,7 @@ def algorithmic_bytes(wl, lens, tables):
     return int(total)
 
 
-def cpu_baseline(kv, wl, t, l, budget_s, nq=1):
+def cpu_baseline(kv, wl, t, l, budget_s, nq=1, config=""):
     """Time the oracle's decode on the first sequences of the batch: rebuild the
     logical K/V through the table from the copied-back pool bytes, then float64
     attention.  Stops after ~budget_s seconds."""
@@ -99,7 +122,7 @@ def cpu_baseline(kv, wl, t, l, budget_s, nq=1):
                 num_sink_blocks=wl.num_sink_blocks)
     view = AT.PoolView(pool_bytes, desc)
     import torch
-    qsrc = wl.q() if nq == 1 else wl.q_verify(nq)
+    qsrc = queries(wl, config, nq)
     q = torch.from_numpy(qsrc).to({"f32": torch.float32, "f16": torch.float16,
                                    "bf16": torch.bfloat16}[wl.q_dtype]).double().numpy()
     done, secs = 0, 0.0
@@ -166,7 +189,7 @@ def main():
         q = torch.from_numpy(wl.q()).to(torch_dtype(wl.q_dtype)).to(dev)
         ws_bytes = B.pa_decode_workspace_bytes(kv.pool, wl.batch, wl.n_q_heads, max_len)
     else:
-        q = torch.from_numpy(wl.q_verify(nq)).to(torch_dtype(wl.q_dtype)).to(dev)
+        q = torch.from_numpy(queries(wl, args.config, nq)).to(torch_dtype(wl.q_dtype)).to(dev)
         ws_bytes = B.pa_verify_workspace_bytes(kv.pool, wl.batch, wl.n_q_heads, nq, max_len)
     out = torch.empty_like(q)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
@@ -194,9 +217,11 @@ def main():
     vargs = (q, kv.pool, tdev, ldev, wl.batch, wl.n_q_heads, nq, wl.q_dtype, tdev.shape[1],
              max_len, wl.scale, out, ws, ws.numel(), sh)
 
-    def attn_split():   # the dominant launch (the verify call is one launch at these shapes)
+    def attn_split():   # the dominant launch (verify / prefill: one launch at these shapes)
         if nq == 1:
             B.pa_decode_split(*dargs)
+        elif args.config == "prefill-chunk":
+            B.pa_prefill_attention(*vargs)
         else:
             B.pa_verify_attention(*vargs)
 
@@ -286,7 +311,7 @@ def main():
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(kv, wl, t, l, args.cpu_budget, nq)
+        cpu = cpu_baseline(kv, wl, t, l, args.cpu_budget, nq, args.config)
 
     split_blocks = B.pa_decode_split_blocks(kv.pool, wl.batch, wl.n_q_heads, max_len)
     # HBM bytes per split launch from the committed rocprofv3 counters, while
@@ -294,6 +319,20 @@ def main():
     from paged_kv_cache_18_amd.profiling import traffic_bytes
     tb = None if args.identity_tables else traffic_bytes(args.config)
     traffic = round(tb / (split_avg * 1e-3) / 1e9, 1) if tb else None
+    if args.config in MFMA_BOUND:
+        # algorithmic flops of the causal chunk (masked tokens not counted)
+        flops = causal_flops(lens, nq, wl.n_q_heads, wl.head_dim)
+        tfl = flops / (split_avg * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tfl / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+                    "traffic_unit": "GB/s", "traffic_bytes_per_launch": tb,
+                    "flops_per_launch": flops, "kernel": "decode_split (prefill chunk)",
+                    "avg_launch_ms": round(split_avg, 5)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "traffic_bytes_per_launch": tb, "kernel": "decode_split",
+                    "avg_launch_ms": round(split_avg, 5)}
     res = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) and queries/s, 1 MI355X",
         "value": round(kv_gbs, 2),
@@ -317,10 +356,7 @@ def main():
         "queries_per_s": round(wl.batch * nq / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": byts,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_bytes_per_launch": tb, "kernel": "decode_split",
-                     "avg_launch_ms": round(split_avg, 5)},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     res.update(extra)

@@ -297,7 +297,7 @@ pa_status pa_verify_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t 
  * exactly the decode of the whole sequence.  A query whose position falls
  * before the start of the cache (L_b < n_query) has no token: zero output.
  *  q, out: device [batch][n_query][n_q_heads][head_dim] of q_dtype.
- *  n_query: 1..64 (gamma + 1).  Other arguments and the workspace contract
+ *  n_query: 1..4096 (gamma + 1).  Other arguments and the workspace contract
  *  are those of pa_decode_attention.  Rollback of rejected tokens is
  *  pa_seq_truncate (their blocks return to the free stack last-first). */
 pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
@@ -305,6 +305,30 @@ pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t*
                               int32_t n_query, int32_t q_dtype, int32_t max_blocks_per_seq,
                               int32_t max_seq_len, float scale, void* out, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* ---- chunked paged prefill ---------------------------------------------------- */
+
+/* Workspace bytes pa_prefill_attention needs for these shapes. */
+pa_status pa_prefill_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
+                                     int32_t chunk, int32_t max_seq_len, size_t* bytes);
+
+/* Attention of one prefill chunk ([8GB] section 6: a long prompt is
+ * prefilled in slices of 512 tokens, so the Q K^T tile never spans the whole
+ * prompt; the slice's K/V go into the paged cache through the tables first).
+ * The chunk's tokens are already reserved and appended, so they are the last
+ * `chunk` cached tokens of every sequence; query i of the chunk attends to
+ * tokens 0 .. L_b - chunk + i (the cached prefix and the chunk up to
+ * itself).  Prefilling a prompt chunk by chunk gives exactly the causal
+ * attention of the whole prompt.  The same operation as the verify step,
+ * for chunks up to 4096 tokens:
+ *  q, out: device [batch][chunk][n_q_heads][head_dim] of q_dtype.
+ *  chunk: 1..4096.  Other arguments and the workspace contract are those of
+ *  pa_decode_attention. */
+pa_status pa_prefill_attention(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
+                               const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
+                               int32_t chunk, int32_t q_dtype, int32_t max_blocks_per_seq,
+                               int32_t max_seq_len, float scale, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* How the decode splits its work for these shapes (informational): > 0 is a
  * fixed number of blocks per chunk; < 0 is minus the number of workgroups of

@@ -77,6 +77,45 @@ def verify_attention_one(q, K, V, scale):
     return out
 
 
+def causal_attention(q, K, V, scale):
+    """Causal self-attention of a whole prompt in one pass: token i's query
+    sees tokens 0..i.  Written as one masked score matrix (the form that
+    chunked prefill avoids materializing: 8GB page, section 6, "Chunked
+    Prefill"), independently of the per-query loops above.
+
+    q: [P][Hq][D]; K, V: [P][Hkv][D].  Returns [P][Hq][D] float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    P, hq, _ = q.shape
+    hkv = K.shape[1]
+    group = hq // hkv
+    out = np.zeros(q.shape, dtype=np.float64)
+    future = np.triu(np.ones((P, P), dtype=bool), k=1)  # key t > query i
+    for h in range(hq):
+        g = h // group
+        s = scale * (q[:, h, :] @ K[:, g, :].T)          # [P][P]
+        s[future] = -np.inf
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ V[:, g, :]
+    return out
+
+
+def prefill_chunks(q, K, V, scale, chunk):
+    """A prompt prefilled in chunks of `chunk` tokens (8GB page, section 6):
+    chunk c's K/V join the cache, then its queries attend over the cache so
+    far, causally among themselves -- the verify step's operation with
+    n_query = the chunk's length.  Returns [P][Hq][D] float64."""
+    P = np.asarray(q).shape[0]
+    parts = []
+    for s0 in range(0, P, chunk):
+        e = min(P, s0 + chunk)
+        parts.append(verify_attention_one(np.asarray(q)[s0:e], np.asarray(K)[:e], np.asarray(V)[:e], scale))
+    return np.concatenate(parts) if parts else np.zeros(np.asarray(q).shape)
+
+
 def decode_attention(q, kv, scale):
     """q: [B][Hq][D]; kv: list of (K, V) per sequence, each [L_b][Hkv][D]."""
     return np.stack([attention_one(q[b], K, V, scale) for b, (K, V) in enumerate(kv)])

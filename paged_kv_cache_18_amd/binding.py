@@ -81,6 +81,8 @@ _PROTOS = {
     "pa_decode_attention": _DECODE_ARGS,
     "pa_verify_workspace_bytes": [vp, i32, i32, i32, i32, C.POINTER(sz)],
     "pa_verify_attention": [vp, vp, P32, P32, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz, vp],
+    "pa_prefill_workspace_bytes": [vp, i32, i32, i32, i32, C.POINTER(sz)],
+    "pa_prefill_attention": [vp, vp, P32, P32, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz, vp],
     "pa_decode_split": _DECODE_ARGS,
     "pa_decode_combine": _DECODE_ARGS,
 }
@@ -328,6 +330,22 @@ def pa_verify_attention(q, pool, tables_dev, lens_dev, batch, n_q_heads, n_query
     _check(lib().pa_verify_attention(_ptr(q), pool, _i32ptr(tables_dev), _i32ptr(lens_dev), batch,
                                      n_q_heads, n_query, dt, max_blocks, max_seq_len, scale,
                                      _ptr(out), _ptr(workspace), workspace_bytes, _ptr(stream)))
+
+
+def pa_prefill_workspace_bytes(pool, batch, n_q_heads, chunk, max_seq_len):
+    out = sz()
+    _check(lib().pa_prefill_workspace_bytes(pool, batch, n_q_heads, chunk, max_seq_len,
+                                            C.byref(out)))
+    return out.value
+
+
+def pa_prefill_attention(q, pool, tables_dev, lens_dev, batch, n_q_heads, chunk, q_dtype,
+                         max_blocks, max_seq_len, scale, out, workspace, workspace_bytes,
+                         stream=None):
+    dt = DTYPES[q_dtype] if isinstance(q_dtype, str) else int(q_dtype)
+    _check(lib().pa_prefill_attention(_ptr(q), pool, _i32ptr(tables_dev), _i32ptr(lens_dev), batch,
+                                      n_q_heads, chunk, dt, max_blocks, max_seq_len, scale,
+                                      _ptr(out), _ptr(workspace), workspace_bytes, _ptr(stream)))
 
 
 def pa_stream_read(src, nbytes, sink, stream=None):

@@ -88,21 +88,24 @@ __device__ inline int seq_len(const DecodeArgs& a, int b) {
 
 __device__ inline int seq_blocks(const DecodeArgs& a, int b) { return (seq_len(a, b) + 15) >> 4; }
 
-// Start of sequence b's segments in the flattened list: Hkv * sum_{b'<b} nb_b'.
+// Segments per sequence: one per KV head and column slice.
+__device__ inline int seg_heads(const DecodeArgs& a) { return a.pool.n_kv_heads * max(a.col_slices, 1); }
+
+// Start of sequence b's segments in the flattened list: seg_heads * sum_{b'<b} nb_b'.
 __device__ inline int seq_start(const DecodeArgs& a, int b, int lane) {
   int acc = 0;
   for (int base = 0; base < b; base += 64) {
     const int bb = base + lane;
     acc += bb < b ? seq_blocks(a, bb) : 0;
   }
-  return wave_sum_int(acc) * a.pool.n_kv_heads;
+  return wave_sum_int(acc) * seg_heads(a);
 }
 
 // Total blocks of the flattened list (one wavefront, result in every lane).
 __device__ inline int total_work(const DecodeArgs& a, int lane) {
   int tot = 0;
   for (int base = 0; base < a.batch; base += 64)
-    tot += base + lane < a.batch ? seq_blocks(a, base + lane) * a.pool.n_kv_heads : 0;
+    tot += base + lane < a.batch ? seq_blocks(a, base + lane) * seg_heads(a) : 0;
   return wave_sum_int(tot);
 }
 
@@ -120,20 +123,25 @@ struct SharedT {
 };
 using Shared = SharedT<16>;
 
-// Output columns of a segment (b, h): column col = qi*G + gi is query qi of
-// the sequence's n_query (1 for decode) and query head h*G + gi, stored at
-// row (b*n_query + qi)*Hq + h*G + gi of out ([batch][n_query][Hq][D]).
+// Output columns of a segment (b, hv), hv = h*nsl + s (KV head h, column
+// slice s of SW columns): its column col is the (query, head) column
+// gc = s*SW + col = qi*G + gi, query qi of the sequence's n_query (1 for
+// decode) and query head h*G + gi, stored at row (b*n_query + qi)*Hq + h*G + gi
+// of out ([batch][n_query][Hq][D]).  The last slice may hold fewer columns.
 struct OutMap {
-  int G, Hq, nq;
-  __device__ int ncol() const { return nq * G; }
-  __device__ size_t row(int b, int h, int col) const {
-    return (size_t(b) * nq + col / G) * Hq + h * G + col % G;
+  int G, Hq, nq, nsl, SW;
+  __device__ int ncol() const { return SW; }
+  __device__ int cols(int hv) const { return min(SW, nq * G - (hv % nsl) * SW); }
+  __device__ int gcol(int hv, int col) const { return (hv % nsl) * SW + col; }
+  __device__ size_t row(int b, int hv, int col) const {
+    const int gc = gcol(hv, col);
+    return (size_t(b) * nq + gc / G) * Hq + (hv / nsl) * G + gc % G;
   }
 };
 
 __device__ inline OutMap out_map(const DecodeArgs& a) {
-  const int G = a.n_q_heads / a.pool.n_kv_heads;
-  return OutMap{G, a.n_q_heads, max(a.n_query, 1)};
+  const int G = a.n_q_heads / a.pool.n_kv_heads, nq = max(a.n_query, 1), nsl = max(a.col_slices, 1);
+  return OutMap{G, a.n_q_heads, nq, nsl, nsl > 1 ? 32 : nq * G};
 }
 
 // The cut of the work list (see the top of this file).  Unit ids grow with
@@ -200,7 +208,7 @@ __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane
 template <class SH>
 __device__ inline void locate(const DecodeArgs& a, SH& sh, int w, int lane, int p0, int& b,
                               int& fb) {
-  const int H = a.pool.n_kv_heads, B = a.batch;
+  const int H = seg_heads(a), B = a.batch;
   if (w == 0) {
     int run = 0, f = 0, fbi = B;
     for (int base = 0; base < B; base += 64) {
@@ -282,7 +290,7 @@ __device__ inline void zero_empty_rows(const DecodeArgs& a) {
 // advances (b, fb) past finished or empty sequences.  False when done.
 __device__ inline bool next_piece(const DecodeArgs& a, int pos, int pos1, int& b, int& fb, int& h,
                                   int& jbeg, int& jend, int& nb) {
-  const int H = a.pool.n_kv_heads;
+  const int H = seg_heads(a);
   while (pos < pos1 && b < a.batch) {
     nb = seq_blocks(a, b);
     if (pos >= fb + nb * H) {
@@ -448,7 +456,7 @@ __device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& 
       }
       __syncthreads();  // red is rewritten by the next trip
     }
-    if (pg == 0) {
+    if (pg == 0 && hc < om.cols(h)) {  // the last column slice may be short
       const float inv = r.l > 0.f ? 1.f / r.l : 0.f;
       TO* o = out + om.row(b, h, hc) * kD + (cc % kCols) * 4;
 #pragma unroll
@@ -500,7 +508,7 @@ __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& o
       osum += sh.o[v][hc][d] * wt;
     }
     if (complete) {
-      out[om.row(b, h, hc) * kD + d] = TO(lsum > 0.f ? osum / lsum : 0.f);
+      if (hc < om.cols(h)) out[om.row(b, h, hc) * kD + d] = TO(lsum > 0.f ? osum / lsum : 0.f);
     } else {
       const size_t row = (size_t(unit) * 2 + slot) * NC + hc;
       st_agent(&a.ws_o[row * kD + d], osum);

@@ -20,10 +20,11 @@ using namespace dec;
 template <typename TO>
 __global__ __launch_bounds__(kWaves * 64) void decode_merge_kernel(DecodeArgs a) {
   __shared__ Shared sh;
-  const int H = a.pool.n_kv_heads;
+  const int H = seg_heads(a);
   const OutMap om = out_map(a);
   const int hc = int(blockIdx.x) % om.ncol(), bh = int(blockIdx.x) / om.ncol();
   const int b = bh / H, h = bh % H;
+  if (hc >= om.cols(h)) return;  // past the last column of a short slice
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = seq_blocks(a, b);
@@ -38,8 +39,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_merge_kernel(DecodeArgs a)
 }  // namespace
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
-  const int ncol = max(a.n_query, 1) * (a.n_q_heads / a.pool.n_kv_heads);
-  const dim3 grid(unsigned(a.batch) * unsigned(a.pool.n_kv_heads) * unsigned(ncol));
+  const int nsl = max(a.col_slices, 1);
+  const int ncol = nsl > 1 ? 32 : max(a.n_query, 1) * (a.n_q_heads / a.pool.n_kv_heads);
+  const dim3 grid(unsigned(a.batch) * unsigned(a.pool.n_kv_heads * nsl) * unsigned(ncol));
   if (a.q_dtype == kBF16)
     hipLaunchKernelGGL(decode_merge_kernel<__bf16>, grid, dim3(kWaves * 64), 0, s, a);
   else

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   const PoolDev& p = a.pool;
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H;
   const OutMap om = out_map(a);
-  const int nq = om.nq, ncol = om.ncol();
+  const int nq = om.nq, nsl = om.nsl;
   zero_empty_rows<T>(a);
   const Units um = setup_units(a, sh, w, lane);
   int b = 0, fb = 0;
@@ -85,8 +85,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   const float sl2 = a.scale_log2;
   const int nbk = p.num_blocks;
 
-  // per-piece state, captured by the lambdas below
-  int h = 0, L = 0;
+  // per-piece state, captured by the lambdas below: segment hv = h*nsl + s
+  // (KV head h, column slice s)
+  int hv = 0, h = 0, L = 0;
   const int32_t* trow = a.tables;
   v8 qf[NCT][4];
   f32x4 o[NCT][kNT];
@@ -192,16 +193,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   int pos = pos0;
   bool first = true;
   int jbeg = 0, jend = 0, nb = 0;
-  while (next_piece(a, pos, pos1, b, fb, h, jbeg, jend, nb)) {
+  while (next_piece(a, pos, pos1, b, fb, hv, jbeg, jend, nb)) {
     L = seq_len(a, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
+    h = hv / nsl;
+    const int ncol = om.cols(hv);
 #pragma unroll
     for (int t = 0; t < NCT; ++t) {
-      // Q^T fragment: lane (g, c) of tile t holds column col = 16t + c, i.e.
-      // Q[query col / G][head h*G + col % G][32kk + 8g .. +7]; zero past the
-      // last column
-      const int col = 16 * t + c, qi = col / G;
-      const T* qp = static_cast<const T*>(a.q) + om.row(b, h, col) * kD + 8 * g;
+      // Q^T fragment: lane (g, c) of tile t holds the segment's column
+      // col = 16t + c, i.e. Q[query gc / G][head h*G + gc % G][32kk + 8g .. +7]
+      // for gc = s*32 + col in column slice s; zero past the last column
+      const int col = 16 * t + c, qi = om.gcol(hv, col) / G;
+      const T* qp = static_cast<const T*>(a.q) + om.row(b, hv, min(col, ncol - 1)) * kD + 8 * g;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         qf[t][kk] = col < ncol ? *reinterpret_cast<const v8*>(qp + 32 * kk) : v8{};
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       l_run[t] += __shfl_xor(l_run[t], 32, 64);
       stash_piece(sh, w, g, 16 * t + c, o[t], m_ref[t], l_run[t]);
     }
-    finish_piece<T>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, h, fb + h * nb,
+    finish_piece<T>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, hv, fb + hv * nb,
                     nb, um);
     pos += jend - jbeg;
     first = false;
@@ -280,8 +283,8 @@ int mfma_nb() {
 template <typename T>
 hipError_t launch_nb(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.max_splits)), block(kWaves * 64);
-  if (a.n_query > 1) {  // the verify step: one or two column tiles, causal
-    const int ncol = a.n_query * (a.n_q_heads / a.pool.n_kv_heads);
+  if (a.n_query > 1) {  // verify / prefill chunk: one or two column tiles, causal
+    const int ncol = a.n_query * (a.n_q_heads / a.pool.n_kv_heads);  // > 32: slices of 32
     if (ncol <= 16)
       hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, true>), grid, block, 0, s, a);
     else

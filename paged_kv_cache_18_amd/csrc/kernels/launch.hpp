@@ -41,7 +41,11 @@ struct DecodeArgs {
   const int32_t* tables;
   const int32_t* lens;
   int32_t batch, n_q_heads, q_dtype, max_blocks_per_seq, max_seq_len;
-  int32_t n_query;        // queries per sequence: 1 (decode) or the verify step's gamma + 1
+  int32_t n_query;        // queries per sequence: 1 (decode), gamma + 1 (verify) or a prefill chunk
+  // matrix-core kernels: column slices per (sequence, KV head) -- segments
+  // (b, h * col_slices + s) of 32 (query, head) columns each; 1 = one
+  // segment of all n_query * G columns
+  int32_t col_slices;
   float scale_log2;      // softmax scale * log2(e): scores live in the log2 domain
   void* out;
   float* ws_o;           // [batch][n_q_heads][max_splits][head_dim] partial sums

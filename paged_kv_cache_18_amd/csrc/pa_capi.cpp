@@ -130,6 +130,7 @@ struct Plan {
   int32_t split_blocks, max_splits, kernel;
   int32_t unit_blocks, static_permille;  // the cut of the matrix-core kernels
   int32_t defer_merge;                   // split segments merged by a second launch
+  int32_t col_slices;                    // matrix-core kernels: 32-column slices per (seq, kv head)
   size_t ws_bytes;      // bytes the call needs
   size_t ws_o_offset;   // byte offset of the partial sums
   size_t ws_ml_offset;  // float index (from ws_o) of the (max, sum) pairs
@@ -168,9 +169,12 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
   Plan pl{};
   const int32_t G = n_q_heads / d.n_kv_heads;
   const int32_t ncol = n_query * G;  // output columns per (sequence, kv head)
+  // more than 32 (query, head) columns (a long verify step, a prefill chunk):
+  // slices of 32 columns, each its own segment of the work list
+  const int32_t nsl = n_query > 1 && ncol > 32 ? (ncol + 31) / 32 : 1;
+  const int32_t seg_cols = nsl > 1 ? 32 : ncol;
   const bool mfma_ok = (d.kv_dtype == pa::kBF16 || d.kv_dtype == pa::kF16) &&
-                       q_dtype == d.kv_dtype && d.head_dim == 128 &&
-                       (n_query == 1 ? G <= 16 : ncol <= 32) && d.num_sink_blocks == 0;
+                       q_dtype == d.kv_dtype && d.head_dim == 128 && G <= 16 && d.num_sink_blocks == 0;
   // INT4 groups of 128 or 64 dims: the matrix-core B operand's 16 columns
   // hold every query head of the KV head once per group
   const int32_t ngroups = d.kv_dtype == pa::kInt4 ? d.head_dim / d.group_size : 1;
@@ -185,7 +189,8 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
   const int64_t nb = (int64_t(max_seq_len) + 15) / 16;
   if (pl.kernel != pa::kKernGeneric) {
     // Fixed chunks of the flattened list; two partial slots per workgroup.
-    const int64_t w = flat_upper(batch, d.n_kv_heads, max_seq_len);
+    pl.col_slices = pl.kernel == pa::kKernMfma16 ? nsl : 1;
+    const int64_t w = flat_upper(batch, d.n_kv_heads, max_seq_len) * pl.col_slices;
     if (w >= (int64_t(1) << 31) - 4096) fail(pa::kInvalidArg, "batch * n_kv_heads * blocks too large");
     int32_t c = env_int("PA_SPLIT_BLOCKS", 0);  // fixed chunk size (tuning/tests)
     int64_t units = 0;                          // units of the cut, at most
@@ -201,8 +206,8 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
       pl.split_blocks = 0;
       int per_cu = env_int("PA_WG_PER_CU", 0);  // tuning knob; default: resident slots
       if (per_cu <= 0)
-        per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype, n_query == 1 ? 0 : ncol <= 16 ? 1 : 2,
-                                            d.group_size);
+        per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype,
+                                            n_query == 1 ? 0 : seg_cols <= 16 ? 1 : 2, d.group_size);
       pl.max_splits = int32_t(std::max<int64_t>(
           1, std::min<int64_t>({w, int64_t(cu_count()) * per_cu, int64_t(kCtrCap / 2)})));
       // queued units: the owner streams static_permille/1000 of its region,
@@ -224,10 +229,10 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
     // thread, done by the workgroup that completes it; when segments span
     // many workgroups on average those rounds form a serial tail, and a
     // second launch with one workgroup per (segment, query head) is shorter.
-    const int64_t segs = std::max<int64_t>(1, int64_t(batch) * d.n_kv_heads);
+    const int64_t segs = std::max<int64_t>(1, int64_t(batch) * d.n_kv_heads * pl.col_slices);
     const int fuse_max = env_int("PA_FUSE_MAX_PIECES", kFuseMaxPieces);
     pl.defer_merge = units / segs + 1 > fuse_max ? 1 : 0;
-    const size_t rows = size_t(units) * 2 * size_t(ncol);
+    const size_t rows = size_t(units) * 2 * size_t(pl.col_slices > 1 ? seg_cols : ncol);
     pl.ws_o_offset = kCtrBytes;
     pl.ws_ml_offset = rows * size_t(d.head_dim);
     pl.ws_bytes = kCtrBytes + rows * (size_t(d.head_dim) + 2) * sizeof(float);
@@ -253,7 +258,7 @@ void check_shapes(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t ma
 
 enum Phase { kBoth = 3, kSplit = 1, kCombine = 2 };
 
-constexpr int32_t kMaxQueries = 64;  // verify step: queries per sequence, at most
+constexpr int32_t kMaxQueries = 4096;  // verify step / prefill chunk: queries per sequence, at most
 
 pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* tables,
                  const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t q_dtype,
@@ -262,7 +267,7 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
   return guard([&] {
     need_device(pool);
     check_shapes(pool, batch, n_q_heads, max_seq_len);
-    if (n_query < 1 || n_query > kMaxQueries) fail(pa::kInvalidArg, "n_query must be in [1, 64]");
+    if (n_query < 1 || n_query > kMaxQueries) fail(pa::kInvalidArg, "n_query must be in [1, 4096]");
     const pa::Desc& d = pool->core.desc();
     if (pa::is_raw(d.kv_dtype)) {
       if (q_dtype != d.kv_dtype) fail(pa::kInvalidArg, "q_dtype must equal the pool's kv_dtype");
@@ -310,6 +315,7 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     a.unit_blocks = pl.unit_blocks;
     a.static_permille = pl.static_permille;
     a.defer_merge = pl.defer_merge;
+    a.col_slices = std::max(pl.col_slices, 1);
     a.split_blocks = pl.split_blocks;
     a.max_splits = pl.max_splits;
     a.kernel = pl.kernel;
@@ -601,7 +607,7 @@ pa_status pa_verify_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t 
   return guard([&] {
     check_shapes(pool, batch, n_q_heads, max_seq_len);
     need(bytes, "bytes");
-    if (n_query < 1 || n_query > kMaxQueries) fail(pa::kInvalidArg, "n_query must be in [1, 64]");
+    if (n_query < 1 || n_query > kMaxQueries) fail(pa::kInvalidArg, "n_query must be in [1, 4096]");
     const pa::Desc& d = pool->core.desc();
     const int32_t qdt = pa::is_raw(d.kv_dtype) ? d.kv_dtype : int32_t(pa::kF16);
     *bytes = make_plan(pool, batch, n_q_heads, max_seq_len, qdt, n_query).ws_bytes;
@@ -615,6 +621,20 @@ pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t*
                               size_t ws_bytes, void* stream) {
   return decode(kBoth, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
                 scale, out, ws, ws_bytes, stream, n_query);
+}
+
+pa_status pa_prefill_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
+                                     int32_t chunk, int32_t max_seq_len, size_t* bytes) {
+  return pa_verify_workspace_bytes(pool, batch, n_q_heads, chunk, max_seq_len, bytes);
+}
+
+pa_status pa_prefill_attention(const void* q, const pa_pool* pool, const int32_t* tables,
+                               const int32_t* lens, int32_t batch, int32_t n_q_heads,
+                               int32_t chunk, int32_t q_dtype, int32_t max_blocks,
+                               int32_t max_seq_len, float scale, void* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return decode(kBoth, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
+                scale, out, ws, ws_bytes, stream, chunk);
 }
 
 pa_status pa_stream_read(const void* src, size_t bytes, void* sink, void* stream) {

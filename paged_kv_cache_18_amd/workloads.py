@@ -85,6 +85,11 @@ class Workload:
         return rng(self.seed, 7, n_query).standard_normal(
             (self.batch, n_query, self.n_q_heads, self.head_dim), dtype=np.float32)
 
+    def q_chunk(self, k, n):
+        """Queries of prefill chunk k (n tokens per sequence)."""
+        return rng(self.seed, 8, k).standard_normal(
+            (self.batch, n, self.n_q_heads, self.head_dim), dtype=np.float32)
+
     def kv_chunk(self, tag, index, count):
         """K and V (float32 [count][Hkv][D]) of one source chunk."""
         shape = (count, self.n_kv_heads, self.head_dim)
@@ -213,6 +218,26 @@ def window_batch(lengths, steps=0, window=128, group=64, kv="int4", n_q_heads=32
                     extra={"lengths": [L + steps for L in lengths], "steps": steps})
 
 
+def chunked_prefill(seed=9, lengths=(4096, 4096, 4096, 4096), chunk=512, n_q_heads=32, n_kv_heads=8,
+                    head_dim=128, dt="bf16"):
+    """Prompts prefilled in chunks of `chunk` tokens (8GB page, section 6):
+    round k reserves (and writes) every unfinished prompt's next chunk, so
+    the sequences' blocks interleave in the pool as a chunk scheduler would
+    leave them.  Chunk k's queries: q_chunk(k, n)."""
+    lengths = [int(L) for L in lengths]
+    B = len(lengths)
+    n = _pool_size(sum(-(-L // BLOCK) for L in lengths))
+    ops = [("create",) for _ in range(B)]
+    for s0 in range(0, max(lengths + [0]), chunk):
+        for b, L in enumerate(lengths):
+            if s0 < L:
+                ops.append(("reserve", b, min(chunk, L - s0)))
+    return Workload("prefill-chunk", seed, n_q_heads, n_kv_heads, head_dim, dt, dt, dt, n,
+                    rng(seed, 0).permutation(n), ops, list(range(B)),
+                    {b: [(1, b, L)] for b, L in enumerate(lengths)},
+                    extra={"lengths": lengths, "chunk": chunk})
+
+
 def shared_prefix(seed=5, prefix=2000, n_children=32, max_suffix=512):
     """An owner sequence holds a ``prefix``-token prompt; ``n_children`` forks
     each add a suffix of uniform length in [0, max_suffix].  64 q / 8 kv
@@ -271,5 +296,7 @@ def by_name(name, **kw):
         "spec-verify": llama3_8b,   # the same batch, scored by a verify step
         # the pages' own scheme: FP16 sink block and last-128-token window, INT4 g = 64
         "mixed-window": lambda **k: mixed_precision(kv="int4", group=64, window=128, **k),
+        # 4 prompts of 4,096 tokens in 512-token chunks; the bench times the last chunk
+        "prefill-chunk": chunked_prefill,
     }
     return table[name](**kw)

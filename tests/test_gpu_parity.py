@@ -505,3 +505,103 @@ def test_full_mixed_window():
     check_stored(kv, wl, t, l)
     err = assert_close(out, expected(wl), "f16", "mixed window full")
     log(f"[gpu] mixed window full max err {err:.3g}")
+
+
+# ---- chunked paged prefill --------------------------------------------------------
+def prefill_chunk_gpu(kv, wl, k, n, seqs, env=None):
+    """Attention of prefill chunk k (its n queries) for the sequences `seqs`,
+    with each one's cache cut at the chunk's end: the state right after the
+    chunk was appended.  Returns out float64 [len(seqs)][n][Hq][D]."""
+    old = {}
+    for key, v in (env or {}).items():
+        old[key] = os.environ.get(key)
+        os.environ[key] = v
+    try:
+        tdev, _, t, l = kv.device_tables(seqs)
+        ends = np.array([k * wl.extra["chunk"] + n] * len(seqs), dtype=np.int32)
+        assert np.all(ends <= l), "chunk past the prompt"
+        ldev = torch.from_numpy(ends).to(DEV)
+        qall = wl.q_chunk(k, n)
+        q = torch.from_numpy(qall[seqs]).to(TORCH_DT[wl.q_dtype]).to(DEV)
+        bq = len(seqs)
+        max_len = int(ends.max())
+        out_full = torch.full((bq + 1, n, wl.n_q_heads, wl.head_dim), 7.0, dtype=q.dtype, device=DEV)
+        need = B.pa_prefill_workspace_bytes(kv.pool, bq, wl.n_q_heads, n, max_len)
+        ws = torch.full((need + 4096,), 0xAB, dtype=torch.uint8, device=DEV)
+        ws[:need] = 0
+        B.pa_prefill_attention(q, kv.pool, tdev, ldev, bq, wl.n_q_heads, n, wl.q_dtype, tdev.shape[1],
+                               max_len, wl.scale, out_full[:bq], ws, ws.numel(), kv.stream())
+        torch.cuda.synchronize()
+        assert torch.all(out_full[bq] == 7.0), "write past out"
+        assert torch.all(ws[need:] == 0xAB), "write past workspace"
+        return out_full[:bq].to(torch.float64).cpu().numpy()
+    finally:
+        for key, v in old.items():
+            if v is None:
+                os.environ.pop(key, None)
+            else:
+                os.environ[key] = v
+
+
+def expected_prefill_chunk(wl, k, n, seqs):
+    from _ref import cast64
+    q = cast64(wl.q_chunk(k, n), wl.q_dtype)
+    e = k * wl.extra["chunk"] + n
+    out = []
+    for b in seqs:
+        K, V, _ = stored_values(wl, b)
+        out.append(AT.verify_attention_one(q[b], K[:e], V[:e], wl.scale))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("hq,chunk", [(32, 256), (64, 128), (8, 512)])
+def test_prefill_chunks_match_oracle(hq, chunk):
+    """A batch of prompts prefilled chunk by chunk (blocks interleaved across
+    sequences by the chunk rounds): every chunk's attention -- (query, head)
+    columns cut into 32-column slices once there are more than 32, causal
+    inside the chunk -- matches the oracle; the ragged last chunk of a prompt
+    runs as its own call."""
+    lengths = [3 * chunk, 2 * chunk + 37, chunk]
+    wl = W.chunked_prefill(seed=151, lengths=lengths, chunk=chunk, n_q_heads=hq)
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    for k in range(3):
+        seqs = [b for b, L in enumerate(lengths) if L >= (k + 1) * chunk]
+        out = prefill_chunk_gpu(kv, wl, k, chunk, seqs)
+        assert_close(out, expected_prefill_chunk(wl, k, chunk, seqs), "bf16", f"chunk {k} hq {hq}")
+    out = prefill_chunk_gpu(kv, wl, 2, 37, [1])
+    assert_close(out, expected_prefill_chunk(wl, 2, 37, [1]), "bf16", "ragged last chunk")
+
+
+@pytest.mark.parametrize("env", [{"PA_SPLIT_BLOCKS": "3"}, {"PA_FUSE_MAX_PIECES": "1"},
+                                 {"PA_DECODE_KERNEL": "generic"}])
+def test_prefill_chunk_split_merge_and_generic(env):
+    """One 300-token chunk over a 700-token cache: short last column slice
+    (300 x 4 = 1,200 columns = 37.5 slices), fixed small chunks of the work
+    list, the merge as a second launch, and the generic kernel."""
+    wl = W.chunked_prefill(seed=152, lengths=[700, 700], chunk=400)
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    out = prefill_chunk_gpu(kv, wl, 1, 300, [0, 1], env=env)
+    assert_close(out, expected_prefill_chunk(wl, 1, 300, [0, 1]), "bf16", f"prefill {env}")
+
+
+def test_prefill_full_workload_last_chunk_sampled():
+    """The bench's prefill workload (4 x 4,096 tokens, 512-token chunks): the
+    last chunk's attention, 64 slices of 32 columns per KV head, checked on
+    sampled (sequence, query) rows."""
+    wl = W.by_name("prefill-chunk")
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    k = 4096 // 512 - 1
+    out = prefill_chunk_gpu(kv, wl, k, 512, [0, 1, 2, 3])
+    assert np.all(np.isfinite(out))
+    from _ref import cast64
+    q = cast64(wl.q_chunk(k, 512), wl.q_dtype)
+    r = np.random.default_rng(7)
+    for b in range(4):
+        K, V, _ = stored_values(wl, b)
+        for i in r.choice(512, 6, replace=False):
+            e = 4096 - 512 + int(i) + 1
+            ref = AT.attention_one(q[b, i], K[:e], V[:e], wl.scale)
+            assert_close(out[b, i][None], ref[None], "bf16", f"prefill b{b} i{i}")
