@@ -218,6 +218,40 @@ pa_status pa_seq_info(const pa_pool* pool, int32_t seq, int32_t* len, int32_t* n
 pa_status pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n,
                           int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
 
+/* ---- block-hash prefix cache -------------------------------------------------------- */
+/* [PR8] section 8.3: the prompt is hashed in block-sized pieces; a
+ * block already in the cache is mapped into the new request's table and its
+ * prefill skipped, a missing one is prefilled and then registered.  Keys are
+ * chained over the token ids: h_j = FNV-1a-64 of (h_{j-1} as 8 little-endian
+ * bytes, then the 16 ids of block j as int32 little-endian), h_{-1} = the
+ * FNV-1a offset basis, so a block's key names its whole prefix.  Only full
+ * blocks are cached; each entry also records its 16 ids and its parent block
+ * and is used only when both match.  The cache holds one reference per
+ * entry.  Pools with a local window are refused (PA_ERR_UNSUPPORTED): their
+ * blocks move.  token_ids: host int32 [n_tokens]. */
+
+/* New sequence mapped onto the longest cached prefix of whole blocks of
+ * token_ids (one reference per mapped block); *n_cached_tokens = 16 * blocks
+ * mapped (the caller reserves and appends the rest, then registers). */
+pa_status pa_prefix_lookup(pa_pool* pool, const int32_t* token_ids, int32_t n_tokens,
+                           int32_t* out_seq, int32_t* n_cached_tokens);
+/* Enter the full blocks of `seq` (its first min(n_tokens, len)/16 blocks,
+ * keyed by token_ids) that are not cached yet, in order, stopping at the
+ * first position cached under another block.  *n_added may be NULL. */
+pa_status pa_prefix_register(pa_pool* pool, int32_t seq, const int32_t* token_ids,
+                             int32_t n_tokens, int32_t* n_added);
+/* Drop up to max_blocks entries, least recently used (looked up or
+ * registered) first, among entries with no cached child whose block is held
+ * by the cache alone; their blocks return to the free stack.  *n_evicted
+ * may be NULL. */
+pa_status pa_prefix_evict(pa_pool* pool, int32_t max_blocks, int32_t* n_evicted);
+/* Entries, and blocks found / asked for by every lookup so far. */
+pa_status pa_prefix_stats(const pa_pool* pool, int32_t* n_entries, int64_t* hit_blocks,
+                          int64_t* asked_blocks);
+/* The chained keys of the n_tokens/16 full blocks of token_ids into host
+ * hashes_out (checking aid; needs no pool). */
+pa_status pa_prefix_block_hashes(const int32_t* token_ids, int32_t n_tokens, uint64_t* hashes_out);
+
 /* ---- device work ------------------------------------------------------------------ */
 
 /* Write n_tokens tokens into their slots, quantizing on write for an INT4 or

@@ -70,6 +70,11 @@ _PROTOS = {
     "pa_seq_fork": [vp, i32, P32],
     "pa_seq_reserve": [vp, i32, i32, P32, vp],
     "pa_seq_truncate": [vp, i32, i32],
+    "pa_prefix_lookup": [vp, P32, i32, C.POINTER(i32), C.POINTER(i32)],
+    "pa_prefix_register": [vp, i32, P32, i32, C.POINTER(i32)],
+    "pa_prefix_evict": [vp, i32, C.POINTER(i32)],
+    "pa_prefix_stats": [vp, C.POINTER(i32), C.POINTER(i64), C.POINTER(i64)],
+    "pa_prefix_block_hashes": [P32, i32, C.POINTER(C.c_uint64)],
     "pa_seq_release": [vp, i32],
     "pa_seq_info": [vp, i32, P32, P32],
     "pa_block_tables": [vp, P32, i32, i32, P32, P32],
@@ -242,6 +247,46 @@ def pa_seq_reserve(pool, seq, n_tokens, stream=None):
 
 def pa_seq_truncate(pool, seq, new_len):
     _check(lib().pa_seq_truncate(pool, seq, new_len))
+
+
+# ---- block-hash prefix cache --------------------------------------------------------
+def _ids(token_ids):
+    a = np.ascontiguousarray(np.asarray(token_ids, dtype=np.int32))
+    return a, a.ctypes.data_as(P32)
+
+
+def pa_prefix_lookup(pool, token_ids):
+    """New sequence on the longest cached prefix; returns (seq, cached tokens)."""
+    a, p = _ids(token_ids)
+    sid, n = i32(), i32()
+    _check(lib().pa_prefix_lookup(pool, p, a.size, C.byref(sid), C.byref(n)))
+    return sid.value, n.value
+
+
+def pa_prefix_register(pool, seq, token_ids):
+    a, p = _ids(token_ids)
+    n = i32()
+    _check(lib().pa_prefix_register(pool, seq, p, a.size, C.byref(n)))
+    return n.value
+
+
+def pa_prefix_evict(pool, max_blocks):
+    n = i32()
+    _check(lib().pa_prefix_evict(pool, max_blocks, C.byref(n)))
+    return n.value
+
+
+def pa_prefix_stats(pool):
+    e, h, a = i32(), i64(), i64()
+    _check(lib().pa_prefix_stats(pool, C.byref(e), C.byref(h), C.byref(a)))
+    return e.value, h.value, a.value
+
+
+def pa_prefix_block_hashes(token_ids):
+    a, p = _ids(token_ids)
+    out = np.zeros(max(a.size // 16, 1), dtype=np.uint64)
+    _check(lib().pa_prefix_block_hashes(p, a.size, out.ctypes.data_as(C.POINTER(C.c_uint64))))
+    return out[:a.size // 16]
 
 
 def pa_seq_release(pool, seq):

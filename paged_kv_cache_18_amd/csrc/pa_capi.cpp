@@ -493,6 +493,60 @@ pa_status pa_seq_settle(pa_pool* pool, int32_t seq, void* stream, int32_t* n_mov
   });
 }
 
+pa_status pa_prefix_lookup(pa_pool* pool, const int32_t* ids, int32_t n, int32_t* out_seq,
+                           int32_t* n_cached) {
+  return guard([&] {
+    need(pool, "pool");
+    need(out_seq, "out_seq");
+    need(n_cached, "n_cached_tokens");
+    int32_t sid = -1;
+    *n_cached = pool->core.prefix_lookup(ids, n, &sid);
+    *out_seq = sid;
+  });
+}
+
+pa_status pa_prefix_register(pa_pool* pool, int32_t seq, const int32_t* ids, int32_t n,
+                             int32_t* n_added) {
+  return guard([&] {
+    need(pool, "pool");
+    const int32_t k = pool->core.prefix_register(seq, ids, n);
+    if (n_added) *n_added = k;
+  });
+}
+
+pa_status pa_prefix_evict(pa_pool* pool, int32_t max_blocks, int32_t* n_evicted) {
+  return guard([&] {
+    need(pool, "pool");
+    const int32_t k = pool->core.prefix_evict(max_blocks);
+    if (n_evicted) *n_evicted = k;
+  });
+}
+
+pa_status pa_prefix_stats(const pa_pool* pool, int32_t* n_entries, int64_t* hit_blocks,
+                          int64_t* asked_blocks) {
+  return guard([&] {
+    need(pool, "pool");
+    if (n_entries) *n_entries = pool->core.prefix_entries();
+    if (hit_blocks) *hit_blocks = pool->core.prefix_hit_blocks();
+    if (asked_blocks) *asked_blocks = pool->core.prefix_asked_blocks();
+  });
+}
+
+pa_status pa_prefix_block_hashes(const int32_t* ids, int32_t n, uint64_t* out) {
+  return guard([&] {
+    if (n < 0) fail(pa::kInvalidArg, "negative token count");
+    if (n >= pa::kBlock) {
+      need(ids, "token_ids");
+      need(out, "hashes_out");
+    }
+    uint64_t h = 0xcbf29ce484222325ull;
+    for (int32_t j = 0; j < n / pa::kBlock; ++j) {
+      h = pa::PoolCore::block_hash(h, ids + size_t(j) * pa::kBlock);
+      out[j] = h;
+    }
+  });
+}
+
 pa_status pa_seq_truncate(pa_pool* pool, int32_t seq, int32_t new_len) {
   return guard([&] {
     need(pool, "pool");

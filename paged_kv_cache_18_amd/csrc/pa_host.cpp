@@ -285,4 +285,119 @@ void PoolCore::seq_release(int32_t sid) {
   s.live = false;
 }
 
+// ---- block-hash prefix cache (Primer chapter 8, section 8.3: hash the prompt
+// in block-sized pieces; a hit points the new request's table at the cached
+// block and skips its prefill; a miss is prefilled and its block registered.
+// The 3-minute page, "Compartilhamento e compromissos": shared prefixes map to
+// the same physical blocks) -----------------------------------------------------
+
+uint64_t PoolCore::block_hash(uint64_t prev, const int32_t* ids16) {
+  constexpr uint64_t kPrime = 0x100000001b3ull;
+  uint64_t h = 0xcbf29ce484222325ull;
+  for (int i = 0; i < 8; ++i) {
+    h ^= (prev >> (8 * i)) & 0xFFu;
+    h *= kPrime;
+  }
+  for (int t = 0; t < kBlock; ++t) {
+    const uint32_t v = uint32_t(ids16[t]);
+    for (int i = 0; i < 4; ++i) {
+      h ^= (v >> (8 * i)) & 0xFFu;
+      h *= kPrime;
+    }
+  }
+  return h;
+}
+
+namespace {
+void need_prefix_pool(const Desc& d) {
+  if (d.window_tokens > 0)
+    fail(kUnsupported, "the prefix cache needs a pool without a local window (blocks would move)");
+}
+}  // namespace
+
+int32_t PoolCore::prefix_lookup(const int32_t* ids, int32_t n, int32_t* out_seq) {
+  need_prefix_pool(d_);
+  if (n < 0) fail(kInvalidArg, "negative token count");
+  if (n > 0 && !ids) fail(kInvalidArg, "null token ids");
+  const int32_t sid = seq_create();
+  Seq& s = seqs_[size_t(sid)];
+  uint64_t h = 0xcbf29ce484222325ull;
+  int32_t parent = -1;
+  const int32_t nb = n / kBlock;
+  for (int32_t j = 0; j < nb; ++j) {
+    h = block_hash(h, ids + size_t(j) * kBlock);
+    auto it = pcache_.find(h);
+    if (it == pcache_.end()) break;
+    PEntry& e = it->second;
+    if (e.parent != parent || !std::equal(e.ids, e.ids + kBlock, ids + size_t(j) * kBlock)) break;
+    incref(e.block);
+    s.table.push_back(e.block);
+    e.stamp = ++pclock_;
+    parent = e.block;
+  }
+  const int32_t hits = int32_t(s.table.size());
+  s.length = hits * kBlock;
+  p_asked_ += nb;
+  p_hits_ += hits;
+  if (out_seq) *out_seq = sid;
+  return hits * kBlock;
+}
+
+int32_t PoolCore::prefix_register(int32_t sid, const int32_t* ids, int32_t n) {
+  need_prefix_pool(d_);
+  const Seq& s = seq(sid);
+  if (n < 0) fail(kInvalidArg, "negative token count");
+  if (n > 0 && !ids) fail(kInvalidArg, "null token ids");
+  const int32_t nb = std::min(n, s.length) / kBlock;
+  uint64_t h = 0xcbf29ce484222325ull, ph = 0;
+  int32_t parent = -1, added = 0;
+  for (int32_t j = 0; j < nb; ++j) {
+    h = block_hash(h, ids + size_t(j) * kBlock);
+    const int32_t blk = s.table[size_t(j)];
+    auto it = pcache_.find(h);
+    if (it != pcache_.end()) {
+      PEntry& e = it->second;
+      // the position is cached under another block (or another chain): stop
+      if (e.block != blk || e.parent != parent) break;
+      e.stamp = ++pclock_;
+    } else {
+      incref(blk);
+      PEntry e{};
+      e.block = blk;
+      e.parent = parent;
+      e.parent_hash = ph;
+      std::copy(ids + size_t(j) * kBlock, ids + size_t(j + 1) * kBlock, e.ids);
+      e.stamp = ++pclock_;
+      e.children = 0;
+      pcache_.emplace(h, e);
+      if (j > 0) ++pcache_.at(ph).children;
+      ++added;
+    }
+    parent = blk;
+    ph = h;
+  }
+  return added;
+}
+
+int32_t PoolCore::prefix_evict(int32_t max_blocks) {
+  if (max_blocks < 0) fail(kInvalidArg, "negative max_blocks");
+  int32_t done = 0;
+  while (done < max_blocks) {
+    // the least recently used leaf whose block only the cache holds
+    auto best = pcache_.end();
+    for (auto it = pcache_.begin(); it != pcache_.end(); ++it) {
+      const PEntry& e = it->second;
+      if (e.children == 0 && ref_[size_t(e.block)] == 1 && (best == pcache_.end() || e.stamp < best->second.stamp))
+        best = it;
+    }
+    if (best == pcache_.end()) break;
+    const PEntry e = best->second;
+    pcache_.erase(best);
+    if (e.parent >= 0) --pcache_.at(e.parent_hash).children;
+    free_block(e.block);
+    ++done;
+  }
+  return done;
+}
+
 }  // namespace pa

@@ -13,6 +13,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <string>
+#include <unordered_map>
 #include <utility>
 #include <vector>
 
@@ -93,12 +94,43 @@ class PoolCore {
   void seq_release(int32_t seq);
   const Seq& seq(int32_t id) const;
 
+  // ---- block-hash prefix cache ----------------------------------------------
+  // A full block of a prompt is keyed by the chained hash of the prompt's
+  // token ids up to and including it: h_j = FNV-1a-64(h_{j-1} as 8 bytes LE,
+  // then the block's 16 ids as int32 LE), h_{-1} = the FNV-1a offset basis.
+  static uint64_t block_hash(uint64_t prev, const int32_t* ids16);
+  // New sequence mapped onto the cached blocks of the longest cached prefix
+  // of whole blocks (each entry checked on its ids and on its parent block);
+  // returns the cached tokens (a multiple of 16).
+  int32_t prefix_lookup(const int32_t* ids, int32_t n, int32_t* out_seq);
+  // Enters the sequence's full blocks (up to n ids) not yet cached; the cache
+  // holds one reference per entry.  Stops at the first block whose chain
+  // position is cached under another block.  Returns the entries added.
+  int32_t prefix_register(int32_t seq, const int32_t* ids, int32_t n);
+  // Drops up to max_blocks entries, least recently used first, among those
+  // with no cached child whose block only the cache holds; returns how many.
+  int32_t prefix_evict(int32_t max_blocks);
+  int32_t prefix_entries() const { return int32_t(pcache_.size()); }
+  int64_t prefix_hit_blocks() const { return p_hits_; }
+  int64_t prefix_asked_blocks() const { return p_asked_; }
+
  private:
   Seq& seq_mut(int32_t id);
   void check_id(int32_t id) const;
   void check_drop(const std::vector<int32_t>& blocks, size_t from) const;
   int64_t n_out(int64_t length) const;  // logical blocks entirely older than the window
   int32_t arena_for_logical(int32_t j, int64_t length) const;
+
+  struct PEntry {
+    int32_t block, parent;  // parent: the cached block of position j - 1, -1 at j = 0
+    uint64_t parent_hash;
+    int32_t ids[kBlock];
+    uint64_t stamp;   // last use (lookup hit or register)
+    int32_t children; // cached entries whose parent this is
+  };
+  std::unordered_map<uint64_t, PEntry> pcache_;
+  uint64_t pclock_ = 0;
+  int64_t p_hits_ = 0, p_asked_ = 0;
 
   Desc d_;
   std::vector<int32_t> ref_;

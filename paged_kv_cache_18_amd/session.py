@@ -109,6 +109,12 @@ class PagedKV:
                     r = B.pa_cow_clone(self.pool, args[0], self.stream())
                 elif kind == "settle":
                     r = B.pa_seq_settle(self.pool, args[0], self.stream())
+                elif kind == "prefix_lookup":
+                    r = B.pa_prefix_lookup(self.pool, args[0])
+                elif kind == "prefix_register":
+                    r = B.pa_prefix_register(self.pool, args[0], args[1])
+                elif kind == "prefix_evict":
+                    r = B.pa_prefix_evict(self.pool, args[0])
                 else:
                     raise ValueError(kind)
             except B.PaError as e:

@@ -605,3 +605,38 @@ def test_prefill_full_workload_last_chunk_sampled():
             e = 4096 - 512 + int(i) + 1
             ref = AT.attention_one(q[b, i], K[:e], V[:e], wl.scale)
             assert_close(out[b, i][None], ref[None], "bf16", f"prefill b{b} i{i}")
+
+
+# ---- block-hash prefix cache --------------------------------------------------------
+@pytest.mark.parametrize("dt", ["bf16", "int4"])
+def test_prefix_cache_hit_skips_prefill_and_decodes(dt):
+    """Request A is prefilled and registered; request B shares its first 150
+    token ids: the lookup maps A's 9 full blocks (144 tokens) into B's table,
+    only B's remaining tokens are appended, and both decode to the oracle's
+    attention over their logical caches (B's first 144 tokens are A's)."""
+    ids_a = list(range(1000, 1200))
+    ids_b = ids_a[:150] + [7] * 60
+    base = W.from_lengths([200, 210], 32, 8, 128, dt, seed=171, group=64 if dt == "int4" else 0,
+                          sink=dt == "int4")
+    wl = W.Workload("prefix-cache", base.seed, 32, 8, 128, base.kv_dtype, base.q_dtype, base.in_dtype,
+                    base.num_blocks, base.body_free_order,
+                    [("create",), ("reserve", 0, 200), ("prefix_register", 0, ids_a),
+                     ("prefix_lookup", ids_b), ("reserve", 1, 210 - 144)],
+                    [0, 1], {0: [(1, 0, 200)], 1: [(1, 0, 144), (1, 1, 66)]},
+                    group_size=base.group_size, num_sink_blocks=base.num_sink_blocks,
+                    sink_blocks_per_seq=base.sink_blocks_per_seq,
+                    sink_free_order=base.sink_free_order, outlier_channels=base.outlier_channels,
+                    extra={"lengths": [200, 210]})
+    kv = PagedKV(wl, DEV)
+    res = kv.replay()
+    assert res[2] == 12 and res[3] == (1, 144)
+    t, l = kv.tables()
+    assert list(t[1, :9]) == list(t[0, :9]) and not set(t[1, 9:14]) & set(t[0, :13])
+    assert [B.pa_refcount(kv.pool, int(x)) for x in t[0, :9]] == [3] * 9  # A, the cache, B
+    assert B.pa_prefix_stats(kv.pool) == (12, 9, 13)
+    tdev, ldev, t, l = kv.device_tables()
+    q = torch.from_numpy(wl.q()).to(TORCH_DT[wl.q_dtype]).to(DEV)
+    out = kv.decode(q, tdev, ldev, int(l.max()))
+    torch.cuda.synchronize()
+    assert_close(out.double().cpu().numpy(), expected(wl), "f16" if dt == "int4" else "bf16",
+                 f"prefix cache {dt}")

@@ -263,3 +263,66 @@ def test_error_paths(libpa):
         B.pa_decode_workspace_bytes(pool, 1, 3, 16)  # 3 q heads over 2 kv heads
     assert e.value.code == "INVALID_ARG"
     B.pa_pool_destroy(pool)
+
+
+# ---- block-hash prefix cache ------------------------------------------------------
+def test_prefix_block_hashes_match_oracle(libpa):
+    from oracle.prefix_cache import block_keys
+    rnd = np.random.default_rng(3)
+    for n in (0, 15, 16, 17, 100, 1000):
+        ids = rnd.integers(-2**31, 2**31 - 1, size=n, dtype=np.int64).astype(np.int32)
+        assert [int(x) for x in B.pa_prefix_block_hashes(ids)] == block_keys(ids)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_prefix_cache_op_logs_match_oracle(libpa, seed):
+    """Requests drawn from a few prompt families (shared system prompts with
+    different continuations): look up, prefill what was not cached, register,
+    release, evict -- in random order, the same ops through the library and
+    the oracle, compared after every op (results, tables, refcounts, free
+    stacks, cache statistics)."""
+    from oracle.prefix_cache import PrefixCache, replay_with_cache
+    rnd = random.Random(100 + seed)
+    nb = 48
+    wl = W.tiny()
+    wl.num_blocks = nb
+    wl.body_free_order = np.array(rnd.sample(range(nb), nb))
+    kv = PagedKV(wl, device=None)
+    oracle = Pool(nb, body_free_order=wl.body_free_order)
+    cache = PrefixCache(oracle)
+    bases = [[rnd.randrange(50) for _ in range(rnd.randrange(16, 90))] for _ in range(3)]
+    live, hits = {}, 0
+    for _ in range(150):
+        k = rnd.randrange(6)
+        if k <= 1 or not live:
+            ids = rnd.choice(bases)[:rnd.randrange(0, 90)] + [rnd.randrange(50) for _ in range(rnd.randrange(0, 30))]
+            op = ("prefix_lookup", ids)
+        elif k == 2:    # prefill what the lookup did not map
+            sid = rnd.choice(list(live))
+            op = ("reserve", sid, len(live[sid]) - oracle.seq_len(sid))
+        elif k == 3:
+            sid = rnd.choice(list(live))
+            op = ("prefix_register", sid, live[sid])
+        elif k == 4:
+            sid = rnd.choice(list(live))
+            op = ("release", sid)
+        else:
+            op = ("prefix_evict", rnd.randrange(0, 6))
+        res_lib = kv.replay([op], write=False)
+        res_or = replay_with_cache(oracle, cache, [op])
+        assert_same(kv, oracle, res_lib, res_or)
+        assert B.pa_prefix_stats(kv.pool) == cache.stats()
+        r = res_or[0]
+        if op[0] == "prefix_lookup":
+            live[r[0]] = op[1]
+            hits += r[1] > 0
+        elif op[0] == "release" and not (isinstance(r, tuple) and r[0] == "error"):
+            del live[op[1]]
+    assert hits > 0
+
+
+def test_prefix_cache_refuses_window_pools(libpa):
+    wl = W.window_batch([40], window=32)
+    kv = PagedKV(wl, device=None)
+    res = kv.replay([("prefix_lookup", list(range(32)))], write=False)
+    assert res == [("error", "UNSUPPORTED")]
