@@ -53,6 +53,8 @@ WORKLOADS = {
     "spec-verify": "speculative verify step (gamma = 5: 6 causal queries per sequence) on the "
                    "Llama-3-8B-shaped batch: 64 sequences, lengths U[512,4096], 32 q / 8 kv heads, "
                    "head_dim 128, bf16, shuffled tables",
+    "llama3-8b-bs8": "the Llama-3-8B-shaped decode batch in a pool of 8-token blocks",
+    "llama3-8b-bs32": "the Llama-3-8B-shaped decode batch in a pool of 32-token blocks",
     "prefill-chunk": "chunked paged prefill: the last 512-token chunk of 4 prompts of 4,096 tokens "
                      "(causal over the cached prefix and the chunk), 32 q / 8 kv heads, head_dim 128, "
                      "bf16, prompts reserved chunk by chunk",
@@ -119,7 +121,7 @@ def cpu_baseline(kv, wl, t, l, budget_s, nq=1, config=""):
     pool_bytes = kv.pool_host_bytes()
     desc = dict(kv_dtype=DTYPES[wl.kv_dtype], n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
                 group_size=wl.group_size or wl.head_dim, num_blocks=wl.num_blocks,
-                num_sink_blocks=wl.num_sink_blocks)
+                num_sink_blocks=wl.num_sink_blocks, block_size=wl.block_size)
     view = AT.PoolView(pool_bytes, desc)
     import torch
     qsrc = queries(wl, config, nq)
@@ -202,7 +204,7 @@ def main():
         for p in range(max(L - nq, 0), L):
             k_new.append(K[p])
             v_new.append(V[p])
-            slots.append(t[b, p // 16] * 16 + p % 16)
+            slots.append(t[b, p // wl.block_size] * wl.block_size + p % wl.block_size)
         del K, V
     k_new, v_new = np.stack(k_new), np.stack(v_new)
     n_new = len(slots)
@@ -349,13 +351,16 @@ def main():
         "config": {"workload": WORKLOADS[args.config]
                    + (", identity block order" if args.identity_tables else ""), "batch": wl.batch,
                    "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
-                   "head_dim": wl.head_dim, "block_size": 16, "kv_dtype": wl.kv_dtype,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
                    "total_tokens": int(sum(lens)), "max_seq_len": max_len, "n_query": nq,
                    **({} if nq > 1 else {"split_blocks": split_blocks} if split_blocks > 0
                       else {"persistent_workgroups": -split_blocks})},
         "queries_per_s": round(wl.batch * nq / (ms_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": byts,
+        # the block-size trade: slots held per cached token (last-block padding)
+        "block_size": wl.block_size,
+        "slots_per_token": round(sum(-(-L // wl.block_size) * wl.block_size for L in lens) / max(sum(lens), 1), 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

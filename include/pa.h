@@ -30,19 +30,23 @@
  * Pool memory layout (one caller buffer, byte offsets from pa_pool_layout)
  *  Arrays are placed in the order listed, each starting at a multiple of 256
  *  bytes.  Each array is [blocks][n_kv_heads][slab], one slab per (block,
- *  head) for the 16 tokens of the block (the outer order of [8GB] section 7:
+ *  head) for the BS tokens of the block (the outer order of [8GB] section 7:
  *  block, head, then tokens).  Body arrays have num_blocks slabs per head,
- *  sink arrays num_sink_blocks.
- *    raw body (F32/F16/BF16): K, V             slab = 16*D elements
+ *  sink arrays num_sink_blocks.  BS = block_size: 16, or 8 or 32 for a raw
+ *  F16/BF16 pool with D = 128 (no sink arena); every rule below with BS = 16
+ *  where it is not written out.
+ *    raw body (F32/F16/BF16): K, V             slab = BS*D elements
  *    INT4 body:  KC, VC (codes)                slab = 16*D/2 bytes
  *                KS, KZ, VS, VZ (fp16)         slab = 16*(D/group) values
  *    FP8 body:   KC, VC (codes)                slab = 16*D bytes
  *                KS, VS (fp16)                 slab = 16 values
  *    sink arena (if any): SK, SV (fp16 raw)    slab = 16*D elements
- *  Inside a slab, with t the token (0..15) and d the dimension (0..D-1):
- *    raw K       element ((d/8)*16 + t)*8 + d%8
+ *  Inside a slab, with t the token (0..S-1) and d the dimension (0..D-1),
+ *  S = 16 (or 8 for BS = 8; a BS = 32 slab is two 16-token slabs, tokens
+ *  0..15 then 16..31, each laid out by the S = 16 rules):
+ *    raw K       element ((d/8)*S + t)*8 + d%8
  *    raw V       NT = D/16, r = d/NT, T = d%NT, g = t/4, i = t%4,
- *                element ((T/2*64 + g*16 + r)*2 + T%2)*4 + i
+ *                element ((T/2*(S/4)*16 + g*16 + r)*2 + T%2)*4 + i
  *    INT4 K      k = d/2: byte ((k%16/4*16 + t)*(D/32) + k/16)*4 + k%4
  *    INT4 V      byte ((g*16 + r)*(NT/2) + T/2)*4 + i
  *                (INT4: even d in the low nibble, odd d in the high nibble,
@@ -60,7 +64,7 @@
  * Block ids and slots
  *  Body ids are 0..num_blocks-1, sink ids num_blocks..num_blocks+num_sink-1.
  *  The id range is the block's precision metadata ([8GB] section 4: every
- *  physical block carries precision metadata).  A slot is id*16 + offset.
+ *  physical block carries precision metadata).  A slot is id*BS + offset.
  *
  * Numerics
  *  Decode accumulates in fp32 and writes out in q's dtype (rounded once).
@@ -117,9 +121,14 @@ typedef int32_t pa_status;
 typedef struct pa_pool pa_pool;
 
 /* Pool descriptor.  [8GB] section 3: a flat pool of fixed-size blocks,
- * 16 tokens each; section 4: FP16 sink blocks beside an INT4/FP8 body. */
+ * 16 tokens each; section 4: FP16 sink blocks beside an INT4/FP8 body.
+ * [3MIN] "Compartilhamento e compromissos": smaller blocks waste less of
+ * their last block, larger ones take fewer table entries -- 8 and 32 are
+ * offered for raw F16/BF16 pools with D = 128 to measure that trade. */
 typedef struct {
-  int32_t block_size;          /* tokens per block; must be 16                    */
+  int32_t block_size;          /* tokens per block: 16; 8 or 32 for a raw F16/BF16
+                                  pool with head_dim 128, no sink arena, no window,
+                                  no prefix cache                                 */
   int32_t n_kv_heads;          /* >= 1                                            */
   int32_t head_dim;            /* D: multiple of 32 (of 64 for FP8), 32..256      */
   int32_t kv_dtype;            /* body storage: PA_F32/F16/BF16/INT4_ASYM/FP8_E4M3 */

@@ -131,10 +131,11 @@ class PoolView:
     def __init__(self, pool_bytes, desc):
         self.b = np.asarray(pool_bytes, dtype=np.uint8)
         self.desc = desc
+        self.bs = desc.get("block_size", LY.BLOCK)
         self.arrays, self.total = LY.pool_arrays(
             desc["kv_dtype"], desc["n_kv_heads"], desc["head_dim"],
             desc.get("group_size", desc["head_dim"]), desc["num_blocks"],
-            desc.get("num_sink_blocks", 0))
+            desc.get("num_sink_blocks", 0), self.bs)
 
     def _view(self, name, dtype):
         return LY.array_view(self.b, self.arrays, name, self.desc["n_kv_heads"], dtype)
@@ -167,7 +168,7 @@ class PoolView:
         raise ValueError("body_codes is for quantized pools")
 
     def block_values(self, bid, head):
-        """K, V of one physical block and head as float64 [16][D] each."""
+        """K, V of one physical block and head as float64 [bs][D] each."""
         desc = self.desc
         D, N = desc["head_dim"], desc["num_blocks"]
         kd = desc["kv_dtype"]
@@ -178,8 +179,8 @@ class PoolView:
                     LY.gather_raw(sv, [bid - N], head, D, "V").astype(np.float64))
         if kd in LY.ELEM:
             dt = self._raw_dtype()
-            k = LY.gather_raw(self._view("K", dt), [bid], head, D, "K")
-            v = LY.gather_raw(self._view("V", dt), [bid], head, D, "V")
+            k = LY.gather_raw(self._view("K", dt), [bid], head, D, "K", self.bs)
+            v = LY.gather_raw(self._view("V", dt), [bid], head, D, "V", self.bs)
             return self._to64(k, kd), self._to64(v, kd)
         c = self.body_codes([bid], head)
         if kd == LY.DT_INT4:
@@ -190,13 +191,13 @@ class PoolView:
 
     def logical_kv(self, table_row, seq_len):
         """Rebuild [L][Hkv][D] float64 K and V of one sequence."""
-        H, D = self.desc["n_kv_heads"], self.desc["head_dim"]
-        nblk = (seq_len + LY.BLOCK - 1) // LY.BLOCK
-        K = np.zeros((nblk * LY.BLOCK, H, D))
-        V = np.zeros((nblk * LY.BLOCK, H, D))
+        H, D, bs = self.desc["n_kv_heads"], self.desc["head_dim"], self.bs
+        nblk = (seq_len + bs - 1) // bs
+        K = np.zeros((nblk * bs, H, D))
+        V = np.zeros((nblk * bs, H, D))
         for j in range(nblk):
             for h in range(H):
                 k, v = self.block_values(int(table_row[j]), h)
-                K[j * LY.BLOCK:(j + 1) * LY.BLOCK, h] = k
-                V[j * LY.BLOCK:(j + 1) * LY.BLOCK, h] = v
+                K[j * bs:(j + 1) * bs, h] = k
+                V[j * bs:(j + 1) * bs, h] = v
         return K[:seq_len], V[:seq_len]

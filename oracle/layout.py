@@ -24,31 +24,43 @@ DT_F32, DT_F16, DT_BF16, DT_INT4, DT_FP8 = 0, 1, 2, 3, 4
 ELEM = {DT_F32: 4, DT_F16: 2, DT_BF16: 2}
 
 
-def _td(D):
-    t = np.arange(BLOCK)[:, None]
+def _td(D, bs=BLOCK):
+    t = np.arange(bs)[:, None]
     d = np.arange(D)[None, :]
-    return np.broadcast_to(t, (BLOCK, D)), np.broadcast_to(d, (BLOCK, D))
+    return np.broadcast_to(t, (bs, D)), np.broadcast_to(d, (bs, D))
 
 
-def raw_k_index(D):
-    """Element index of K[t][d] inside a raw slab: [d/8][t][d%8]."""
-    t, d = _td(D)
-    return ((d // 8) * BLOCK + t) * 8 + d % 8
+def _sub_slabs(bs):
+    """Tokens per sub-slab (S) and sub-slabs per block: a 32-token block is
+    two 16-token slabs back to back, an 8-token block one slab of S = 8."""
+    S = 8 if bs == 8 else 16
+    return S, bs // S
 
 
-def raw_v_index(D):
-    """Element index of V[t][d] inside a raw slab.
+def raw_k_index(D, bs=BLOCK):
+    """Element index of K[t][d] inside a raw block of bs tokens: sub-slab
+    t // S, then [d/8][t % S][d%8] inside it."""
+    S, _ = _sub_slabs(bs)
+    t, d = _td(D, bs)
+    return (t // S) * S * D + ((d // 8) * S + t % S) * 8 + d % 8
 
-    With NT = D/16: row r = d / NT, tile T = d % NT, token group g = t / 4,
+
+def raw_v_index(D, bs=BLOCK):
+    """Element index of V[t][d] inside a raw block of bs tokens (sub-slab
+    t // S of S tokens, then the rule inside it).
+
+    With NT = D/16: row r = d / NT, tile T = d % NT, token group g = (t%S)/4,
     i = t % 4, unit u = T / 2, parity p = T % 2:
-    index = ((u*64 + g*16 + r)*2 + p)*4 + i.
+    index = ((u*(S/4)*16 + g*16 + r)*2 + p)*4 + i  (u*64 at S = 16).
     """
-    t, d = _td(D)
+    S, _ = _sub_slabs(bs)
+    t, d = _td(D, bs)
     nt = D // 16
     r, T = d // nt, d % nt
-    g, i = t // 4, t % 4
+    ts = t % S
+    g, i = ts // 4, ts % 4
     u, p = T // 2, T % 2
-    return ((u * 64 + g * 16 + r) * 2 + p) * 4 + i
+    return (t // S) * S * D + ((u * (S // 4) * 16 + g * 16 + r) * 2 + p) * 4 + i
 
 
 def int4_k_byte(D):
@@ -107,14 +119,16 @@ def _align(x, a=256):
     return (x + a - 1) // a * a
 
 
-def pool_arrays(kv_dtype, n_kv_heads, head_dim, group_size, num_blocks, num_sink_blocks):
+def pool_arrays(kv_dtype, n_kv_heads, head_dim, group_size, num_blocks, num_sink_blocks,
+                block_size=BLOCK):
     """Ordered list of (name, byte offset, bytes per (block, head) slab, arena
-    block count) for every array in the pool, and the total byte size."""
+    block count) for every array in the pool, and the total byte size.
+    block_size other than 16 only for raw pools (the others are fixed at 16)."""
     H, D, N, S = n_kv_heads, head_dim, num_blocks, num_sink_blocks
     items = []
     if kv_dtype in ELEM:
         e = ELEM[kv_dtype]
-        items += [("K", BLOCK * D * e, N), ("V", BLOCK * D * e, N)]
+        items += [("K", block_size * D * e, N), ("V", block_size * D * e, N)]
     elif kv_dtype == DT_INT4:
         ng = D // group_size
         items += [("KC", BLOCK * D // 2, N), ("VC", BLOCK * D // 2, N),
@@ -145,9 +159,9 @@ def array_view(pool_bytes, arrays, name, n_kv_heads, dtype):
 
 
 # ---- logical rebuild (one sequence, one kv head) -------------------------------
-def gather_raw(slabs, ids, head, D, which):
-    """Logical [len(ids)*16][D] values of K or V from raw slabs."""
-    idx = raw_k_index(D) if which == "K" else raw_v_index(D)
+def gather_raw(slabs, ids, head, D, which, bs=BLOCK):
+    """Logical [len(ids)*bs][D] values of K or V from raw slabs of bs tokens."""
+    idx = raw_k_index(D, bs) if which == "K" else raw_v_index(D, bs)
     return np.concatenate([slabs[b, head][idx] for b in ids], axis=0)
 
 

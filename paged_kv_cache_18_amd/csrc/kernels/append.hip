@@ -134,7 +134,8 @@ __global__ __launch_bounds__(kWaves * 64) void append_kv_kernel(PoolDev p, const
   if (tok >= n) return;
   const int slot = slots[tok];
   if (slot < 0) return;
-  const int id = slot >> 4, t = slot & 15;
+  const int bs = p.block_size;  // 16; 8 or 32 for raw 16-bit pools
+  const int id = slot / bs, t = slot % bs;
   if (id >= N + p.num_sink_blocks) return;
 
   const void* src = kind ? vin : kin;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kWaves * 64) void append_kv_kernel(PoolDev p, const
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int d = 2 * (lane + 64 * m) + e;
-        const int idx = kind ? raw_v_elem(t, d, D) : raw_k_elem(t, d);
+        const int idx = kind ? raw_v_elem(t, d, D, bs) : raw_k_elem(t, d, bs);
         if (dt == kF32)
           reinterpret_cast<float*>(slab)[idx] = x[m][e];
         else if (dt == kF16)

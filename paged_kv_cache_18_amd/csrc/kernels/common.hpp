@@ -14,14 +14,20 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
 __host__ __device__ inline bool is_raw_dev(int dt) { return dt == kF32 || dt == kF16 || dt == kBF16; }
 
-// ---- slab index functions (t = token 0..15, d = dimension) ------------------
-// raw K: [d/8][t][d%8]
-__host__ __device__ inline int raw_k_elem(int t, int d) { return ((d >> 3) * 16 + t) * 8 + (d & 7); }
+// ---- slab index functions (t = token of the block, d = dimension) -------------
+// A 32-token block is two 16-token slabs back to back; an 8-token block one
+// slab of S = 8.
+// raw K: [d/8][t][d%8] within a slab of S tokens
+__host__ __device__ inline int raw_k_elem(int t, int d, int BS = 16) {
+  const int S = BS == 8 ? 8 : 16, half = t / S;
+  return half * 16 * 128 + ((d >> 3) * S + t % S) * 8 + (d & 7);  // halves only with D = 128
+}
 
 // raw V: NT = D/16, r = d/NT, T = d%NT, g = t/4, i = t%4
-__host__ __device__ inline int raw_v_elem(int t, int d, int D) {
+__host__ __device__ inline int raw_v_elem(int t, int d, int D, int BS = 16) {
+  const int S = BS == 8 ? 8 : 16, half = t / S, ts = t % S;
   const int nt = D >> 4, r = d / nt, T = d % nt;
-  return (((T >> 1) * 64 + (t >> 2) * 16 + r) * 2 + (T & 1)) * 4 + (t & 3);
+  return half * 16 * D + (((T >> 1) * (S >> 2) * 16 + (ts >> 2) * 16 + r) * 2 + (T & 1)) * 4 + (ts & 3);
 }
 
 // INT4 K code byte of dimension pair k = d/2

@@ -46,6 +46,7 @@
 // (max, sum, acc) through LDS; segments split across chunks are merged by the
 // workgroup that completes them (decode_common.hpp).
 #include <cstdlib>
+#include <type_traits>
 
 #include "decode_common.hpp"
 
@@ -63,7 +64,15 @@ using namespace dec;
 // head into one tile; the verify step packs n_query x G (query, head) columns
 // into one or two tiles and masks, per column, the tokens after its own
 // query's position (causal among the step's new tokens).
-template <typename T, int NB, int NCT, bool CAUSAL>
+// BS: tokens per pool block (16; 8 or 32).  The kernel always works on
+// 16-token tiles: tile jt is block jt (16), 16-token slab jt % 2 of block
+// jt / 2 (32: tile id 2 * block + slab), or blocks 2jt and 2jt + 1 (8: lanes
+// of tokens 8..15 read the second).
+struct TileId {
+  int a, b;  // 8-token blocks: the two block ids
+};
+
+template <typename T, int NB, int NCT, bool CAUSAL, int BS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 && !CAUSAL ? 3 : 2))) void decode_split_mfma16(DecodeArgs a) {
   typedef typename Mfma<T>::v8 v8;
   typedef typename Mfma<T>::v4 v4;
@@ -100,15 +109,40 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   // load across the wave).  The loads are issued unconditionally -- an
   // out-of-range table entry reads block 0 and is never consumed -- so no
   // branch separates a load from its use and the wait counters stay exact.
-  auto fetch = [&](int id, v8(&kf)[4], v8(&vf)[4]) {
-    const int safe = (id < 0 || id >= nbk) ? 0 : id;
-    const size_t slab = (size_t(safe) * H + h) * (16 * kD);
-    const T* ks = kbase + slab;
-    const T* vs = vbase + slab;
+  // a tile's table entries: the block id (16), 2 * block id + slab (32), or
+  // the two block ids (8)
+  typedef typename std::conditional<BS == 8, TileId, int>::type Tid;
+  auto fetch = [&](Tid tid, v8(&kf)[4], v8(&vf)[4]) {
+    TileId ti;
+    if constexpr (BS == 16) ti = TileId{tid, 0};
+    else if constexpr (BS == 32) ti = TileId{tid >> 1, tid & 1};
+    else ti = tid;
+    const int safe = (ti.a < 0 || ti.a >= nbk) ? 0 : ti.a;
+    const size_t slab = (size_t(safe) * H + h) * (BS * kD);
+    if constexpr (BS == 16) {
+      const T* ks = kbase + slab;
+      const T* vs = vbase + slab;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kf[u] = *reinterpret_cast<const v8*>(ks + (u * 64 + lane) * 8);
+      for (int u = 0; u < 4; ++u) kf[u] = *reinterpret_cast<const v8*>(ks + (u * 64 + lane) * 8);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) vf[u] = *reinterpret_cast<const v8*>(vs + (u * 64 + lane) * 8);
+      for (int u = 0; u < 4; ++u) vf[u] = *reinterpret_cast<const v8*>(vs + (u * 64 + lane) * 8);
+    } else if constexpr (BS == 32) {  // half ti.b: a 16-token slab at 16*b tokens into the block
+      const T* ks = kbase + slab + ti.b * (16 * kD);
+      const T* vs = vbase + slab + ti.b * (16 * kD);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kf[u] = *reinterpret_cast<const v8*>(ks + (u * 64 + lane) * 8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vf[u] = *reinterpret_cast<const v8*>(vs + (u * 64 + lane) * 8);
+    } else {  // BS 8: tokens 0..7 from block a, 8..15 from block b
+      const int sb = (ti.b < 0 || ti.b >= nbk) ? safe : ti.b;
+      const size_t slab_b = (size_t(sb) * H + h) * (BS * kD);
+      const T* ks = kbase + (c < 8 ? slab : slab_b) + ((g * BS + (c & 7)) * 8);
+      const T* vs = vbase + (g < 2 ? slab : slab_b) + (((g & 1) * 16 + c) * 8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kf[u] = *reinterpret_cast<const v8*>(ks + u * 4 * BS * 8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vf[u] = *reinterpret_cast<const v8*>(vs + u * 2 * 16 * 8);
+    }
   };
   auto ok = [&](int id) { return id >= 0 && id < nbk; };
 
@@ -222,18 +256,39 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     // re-read it (an L2 hit, never consumed).
     const int jw = jbeg + w;
     const int n = jw < jend ? (jend - jw + kWaves - 1) / kWaves : 0;
-    auto id_of = [&](int k) { return table_entry(trow + jw + kWaves * min(k, n - 1)); };
-    auto valid_of = [&](int k, int id) { return ok(id) ? L - 16 * (jw + kWaves * k) : 0; };
+    auto id_of = [&](int k) -> Tid {
+      const int jt = jw + kWaves * min(k, n - 1);
+      if constexpr (BS == 16) {
+        return table_entry(trow + jt);
+      } else if constexpr (BS == 32) {
+        return 2 * table_entry(trow + (jt >> 1)) + (jt & 1);
+      } else {  // BS 8: the second block exists only if the sequence reaches it
+        const int last = (L + BS - 1) / BS - 1;
+        return TileId{table_entry(trow + 2 * jt), table_entry(trow + min(2 * jt + 1, last))};
+      }
+    };
+    auto valid_of = [&](int k, Tid tid) {
+      if constexpr (BS == 16) {
+        return ok(tid) ? L - 16 * (jw + kWaves * k) : 0;
+      } else if constexpr (BS == 32) {
+        return ok(tid >> 1) ? L - 16 * (jw + kWaves * k) : 0;
+      } else {
+        const int v = L - 16 * (jw + kWaves * k);
+        if (!ok(tid.a)) return 0;
+        if constexpr (BS == 8) return ok(tid.b) ? v : min(v, 8);
+        return v;
+      }
+    };
     if (n > 0) {
       v8 kb[NB][4], vb[NB][4];
-      int ids[NB];
+      Tid ids[NB];
 #pragma unroll
       for (int s = 0; s < NB - 1; ++s) {
         ids[s] = id_of(s);
         fetch(ids[s], kb[s], vb[s]);
       }
       // table entries are read one block ahead of the fetch that needs them
-      int nid = id_of(NB - 1);
+      Tid nid = id_of(NB - 1);
       int k = 0;
       for (; k + NB <= n; k += NB) {
         prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
@@ -280,23 +335,36 @@ int mfma_nb() {
   return nb;
 }
 
-template <typename T>
-hipError_t launch_nb(const DecodeArgs& a, hipStream_t s) {
+template <typename T, int BS>
+hipError_t launch_bs(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.max_splits)), block(kWaves * 64);
   if (a.n_query > 1) {  // verify / prefill chunk: one or two column tiles, causal
     const int ncol = a.n_query * (a.n_q_heads / a.pool.n_kv_heads);  // > 32: slices of 32
     if (ncol <= 16)
-      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, true, BS>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 2, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 2, true, BS>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  switch (mfma_nb()) {
-    case 3: hipLaunchKernelGGL((decode_split_mfma16<T, 3, 1, false>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_mfma16<T, 4, 1, false>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, false>), grid, block, 0, s, a); break;
+  if constexpr (BS == 16) {
+    switch (mfma_nb()) {
+      case 3: hipLaunchKernelGGL((decode_split_mfma16<T, 3, 1, false, 16>), grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL((decode_split_mfma16<T, 4, 1, false, 16>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, false, 16>), grid, block, 0, s, a); break;
+    }
+  } else {
+    hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, false, BS>), grid, block, 0, s, a);
   }
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_nb(const DecodeArgs& a, hipStream_t s) {
+  switch (a.pool.block_size) {
+    case 8: return launch_bs<T, 8>(a, s);
+    case 32: return launch_bs<T, 32>(a, s);
+    default: return launch_bs<T, 16>(a, s);
+  }
 }
 
 template <typename T>
@@ -304,14 +372,14 @@ int occupancy_nb(int nct) {
   int n = 0;
   hipError_t e;
   if (nct == 2)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 2, true>, kWaves * 64, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 2, true, 16>, kWaves * 64, 0);
   else if (nct == 1)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 1, true>, kWaves * 64, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 1, true, 16>, kWaves * 64, 0);
   else
     switch (mfma_nb()) {
-      case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 3, 1, false>, kWaves * 64, 0); break;
-      case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 4, 1, false>, kWaves * 64, 0); break;
-      default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 1, false>, kWaves * 64, 0); break;
+      case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 3, 1, false, 16>, kWaves * 64, 0); break;
+      case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 4, 1, false, 16>, kWaves * 64, 0); break;
+      default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 1, false, 16>, kWaves * 64, 0); break;
     }
   return (e == hipSuccess && n > 0) ? n : 2;
 }

@@ -15,6 +15,7 @@ struct PoolDev {
   int32_t n_kv_heads, head_dim, kv_dtype, group_size, num_blocks, num_sink_blocks;
   int32_t sink_per_seq;  // logical blocks 0..sink_per_seq-1 live in the sink arena
   int32_t window_tokens;  // > 0: the blocks of the last window_tokens tokens may also be FP16
+  int32_t block_size;     // tokens per block: 16; 8 or 32 (raw 16-bit, D 128)
   size_t off[kNumArr];
   size_t slab[kNumArr];
 };

@@ -76,6 +76,7 @@ pa::PoolDev dev_view(const pa_pool* p) {
   v.num_sink_blocks = d.num_sink_blocks;
   v.sink_per_seq = d.sink_blocks_per_seq;
   v.window_tokens = d.window_tokens;
+  v.block_size = d.block_size;
   for (int i = 0; i < pa::kNumArr; ++i) {
     v.off[i] = p->layout.offset[i];
     v.slab[i] = p->layout.slab[i];
@@ -186,6 +187,8 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
               : mfma_ok ? pa::kKernMfma16
               : quant_ok ? pa::kKernQuant
                          : pa::kKernGeneric;
+  if (d.block_size != 16 && pl.kernel != pa::kKernMfma16)
+    fail(pa::kUnsupported, "block sizes 8 and 32 are decoded by the matrix-core kernel only");
   const int64_t nb = (int64_t(max_seq_len) + 15) / 16;
   if (pl.kernel != pa::kKernGeneric) {
     // Fixed chunks of the flattened list; two partial slots per workgroup.
@@ -275,8 +278,8 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
       fail(pa::kInvalidArg, "INT4/FP8 pools take fp16 queries");
     }
     if (max_blocks < 1) fail(pa::kInvalidArg, "max_blocks_per_seq must be >= 1");
-    if (int64_t(max_seq_len) > int64_t(max_blocks) * 16)
-      fail(pa::kInvalidArg, "max_seq_len exceeds 16 * max_blocks_per_seq");
+    if (int64_t(max_seq_len) > int64_t(max_blocks) * d.block_size)
+      fail(pa::kInvalidArg, "max_seq_len exceeds block_size * max_blocks_per_seq");
     if (!std::isfinite(scale)) fail(pa::kInvalidArg, "scale must be finite");
     if (batch == 0) return;
     need(q, "q");

@@ -17,7 +17,12 @@ bool is_raw(int32_t dt) { return dt == kF32 || dt == kF16 || dt == kBF16; }
 int32_t elem_bytes(int32_t dt) { return dt == kF32 ? 4 : 2; }
 
 void validate_desc(const Desc& d) {
-  if (d.block_size != kBlock) fail(kUnsupported, "block_size must be 16");
+  if (d.block_size != kBlock) {
+    if (d.block_size != 8 && d.block_size != 32) fail(kUnsupported, "block_size must be 8, 16 or 32");
+    if ((d.kv_dtype != kF16 && d.kv_dtype != kBF16) || d.head_dim != 128 || d.num_sink_blocks > 0 ||
+        d.window_tokens > 0)
+      fail(kUnsupported, "block sizes 8 and 32 need a raw F16/BF16 pool with head_dim 128, no sink arena");
+  }
   if (d.n_kv_heads < 1 || d.n_kv_heads > 1024) fail(kInvalidArg, "n_kv_heads out of range");
   if (d.head_dim < 32 || d.head_dim > 256 || d.head_dim % 32)
     fail(kInvalidArg, "head_dim must be a multiple of 32 in [32, 256]");
@@ -49,7 +54,7 @@ Layout compute_layout(const Desc& d) {
     L.slab[i] = 0;
     L.nblocks[i] = 0;
   }
-  const size_t D = size_t(d.head_dim), B = kBlock;
+  const size_t D = size_t(d.head_dim), B = size_t(d.block_size);
   struct Item { int id; size_t slab; int32_t n; };
   std::vector<Item> items;
   if (is_raw(d.kv_dtype)) {
@@ -217,10 +222,11 @@ std::vector<int32_t> PoolCore::seq_reserve(int32_t sid, int32_t n,
   std::vector<int32_t> slots;
   if (n == 0) return slots;
   int32_t need[2] = {0, 0};
-  const bool clone = (s.length % kBlock != 0) && ref_[size_t(s.table.back())] > 1;
+  const int32_t bs = d_.block_size;
+  const bool clone = (s.length % bs != 0) && ref_[size_t(s.table.back())] > 1;
   if (clone) ++need[arena_of(s.table.back())];
   const int32_t first_new = int32_t(s.table.size());
-  const int32_t last = int32_t((int64_t(s.length) + n + kBlock - 1) / kBlock);
+  const int32_t last = int32_t((int64_t(s.length) + n + bs - 1) / bs);
   const int64_t final_len = int64_t(s.length) + n;
   for (int32_t j = first_new; j < last; ++j) ++need[arena_for_logical(j, final_len)];
   for (int a = 0; a < 2; ++a)
@@ -238,7 +244,7 @@ std::vector<int32_t> PoolCore::seq_reserve(int32_t sid, int32_t n,
   slots.resize(size_t(n));
   for (int32_t i = 0; i < n; ++i) {
     int32_t p = s.length + i;
-    slots[size_t(i)] = s.table[size_t(p / kBlock)] * kBlock + p % kBlock;
+    slots[size_t(i)] = s.table[size_t(p / bs)] * bs + p % bs;
   }
   s.length += n;
   return slots;
@@ -266,7 +272,7 @@ int32_t PoolCore::seq_settle(int32_t sid, std::vector<std::pair<int32_t, int32_t
 void PoolCore::seq_truncate(int32_t sid, int32_t new_len) {
   Seq& s = seq_mut(sid);
   if (new_len < 0 || new_len > s.length) fail(kInvalidArg, "truncate beyond length");
-  size_t keep = size_t((new_len + kBlock - 1) / kBlock);
+  size_t keep = size_t((new_len + d_.block_size - 1) / d_.block_size);
   check_drop(s.table, keep);
   while (s.table.size() > keep) {
     free_block(s.table.back());
@@ -312,6 +318,7 @@ namespace {
 void need_prefix_pool(const Desc& d) {
   if (d.window_tokens > 0)
     fail(kUnsupported, "the prefix cache needs a pool without a local window (blocks would move)");
+  if (d.block_size != kBlock) fail(kUnsupported, "the prefix cache keys 16-token blocks");
 }
 }  // namespace
 

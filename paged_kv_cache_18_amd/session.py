@@ -28,7 +28,7 @@ class PagedKV:
         self.desc = B.make_desc(wl.n_kv_heads, wl.head_dim, wl.kv_dtype, wl.num_blocks,
                                 group_size=wl.group_size, num_sink_blocks=wl.num_sink_blocks,
                                 sink_blocks_per_seq=wl.sink_blocks_per_seq,
-                                window_tokens=wl.window_tokens)
+                                window_tokens=wl.window_tokens, block_size=wl.block_size)
         self.pool_bytes = B.pa_pool_bytes(self.desc)
         order = wl.body_free_order if body_free_order is None else body_free_order
         if device is None:

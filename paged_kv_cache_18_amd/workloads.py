@@ -66,6 +66,7 @@ class Workload:
     outlier_channels: np.ndarray | None = None
     outlier_scale: float = 10.0
     window_tokens: int = 0
+    block_size: int = BLOCK       # tokens per pool block (8 and 32: raw 16-bit, D 128)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -135,17 +136,20 @@ def tiny(seed=1):
                     extra={"lengths": lengths})
 
 
-def llama3_8b(seed=2, batch=64, min_len=512, max_len=4096):
+def llama3_8b(seed=2, batch=64, min_len=512, max_len=4096, block_size=BLOCK):
     """Llama-3-8B-shaped decode layer: 32 q / 8 kv heads, head_dim 128, bf16,
-    lengths uniform in [min_len, max_len], pool = blocks needed + 10 %."""
+    lengths uniform in [min_len, max_len], pool = blocks needed + 10 %.
+    block_size 8 or 32: the same batch in a pool of that block size (the
+    block-size trade of the 3-minute page, "Compartilhamento e compromissos")."""
     r = rng(seed, 0)
     lengths = [int(x) for x in r.integers(min_len, max_len + 1, size=batch)]
-    n = _pool_size(sum(-(-L // BLOCK) for L in lengths))
+    n = _pool_size(sum(-(-L // block_size) for L in lengths))
     perm = r.permutation(n)
-    return Workload("llama3-8b", seed, 32, 8, 128, "bf16", "bf16", "bf16", n, perm,
+    name = "llama3-8b" + ("" if block_size == BLOCK else f"-bs{block_size}")
+    return Workload(name, seed, 32, 8, 128, "bf16", "bf16", "bf16", n, perm,
                     _prefill_ops(lengths), list(range(batch)),
                     {b: [(1, b, L)] for b, L in enumerate(lengths)},
-                    extra={"lengths": lengths})
+                    block_size=block_size, extra={"lengths": lengths})
 
 
 def long_context(seed=3, batch=4, length=65536):
@@ -261,14 +265,14 @@ def shared_prefix(seed=5, prefix=2000, n_children=32, max_suffix=512):
 
 
 def from_lengths(lengths, n_q_heads=32, n_kv_heads=8, head_dim=128, kv_dtype="bf16", seed=11,
-                 name="custom", group=0, sink=False, outliers=False):
+                 name="custom", group=0, sink=False, outliers=False, block_size=BLOCK):
     """Sequences of the given lengths (prefilled sequence-major), pool of the
     blocks needed + 10 % in a seeded random order.  For a quantized body,
     ``sink=True`` puts logical block 0 in a FP16 sink arena."""
     lengths = [int(L) for L in lengths]
     qdt = kv_dtype if kv_dtype in ("f32", "f16", "bf16") else "f16"
     n_sink = len(lengths) if sink else 0
-    body = sum(max(0, -(-L // BLOCK) - (1 if sink else 0)) for L in lengths)
+    body = sum(max(0, -(-L // block_size) - (1 if sink else 0)) for L in lengths)
     n = max(1, _pool_size(body))
     perm = rng(seed, 0).permutation(n)
     outl = None
@@ -281,7 +285,7 @@ def from_lengths(lengths, n_q_heads=32, n_kv_heads=8, head_dim=128, kv_dtype="bf
                     group_size=group, num_sink_blocks=n_sink,
                     sink_blocks_per_seq=1 if sink else 0,
                     sink_free_order=rng(seed, 5).permutation(n_sink) if sink else None,
-                    outlier_channels=outl, extra={"lengths": lengths})
+                    outlier_channels=outl, block_size=block_size, extra={"lengths": lengths})
 
 
 def by_name(name, **kw):
@@ -294,6 +298,8 @@ def by_name(name, **kw):
         "shared-prefix": shared_prefix,
         "shared-prefix-partial": lambda **k: shared_prefix(prefix=1992, **k),
         "spec-verify": llama3_8b,   # the same batch, scored by a verify step
+        "llama3-8b-bs8": lambda **k: llama3_8b(block_size=8, **k),
+        "llama3-8b-bs32": lambda **k: llama3_8b(block_size=32, **k),
         # the pages' own scheme: FP16 sink block and last-128-token window, INT4 g = 64
         "mixed-window": lambda **k: mixed_precision(kv="int4", group=64, window=128, **k),
         # 4 prompts of 4,096 tokens in 512-token chunks; the bench times the last chunk

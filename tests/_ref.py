@@ -26,7 +26,7 @@ def oracle_pool(wl):
     """The oracle's pool after the workload's op log (tables, arenas)."""
     pool = Pool(wl.num_blocks, wl.num_sink_blocks, wl.sink_blocks_per_seq,
                 body_free_order=wl.body_free_order, sink_free_order=wl.sink_free_order,
-                window_tokens=wl.window_tokens)
+                window_tokens=wl.window_tokens, block_size=wl.block_size)
     replay(pool, wl.ops)
     return pool
 
@@ -34,7 +34,8 @@ def oracle_pool(wl):
 def fp16_tokens(wl, pool, sid):
     """Per token of the sequence: True where its block is in the FP16 arena."""
     t = pool.seq_table(sid)
-    return np.array([t[p // 16] >= wl.num_blocks for p in range(pool.seq_len(sid))], dtype=bool)
+    return np.array([t[p // wl.block_size] >= wl.num_blocks for p in range(pool.seq_len(sid))],
+                    dtype=bool)
 
 
 def stored_values(wl, sid, fp16=None):

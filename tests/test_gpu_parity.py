@@ -36,7 +36,7 @@ def log(msg):
 def desc_dict(wl):
     return dict(kv_dtype=B.DTYPES[wl.kv_dtype], n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
                 group_size=wl.group_size or wl.head_dim, num_blocks=wl.num_blocks,
-                num_sink_blocks=wl.num_sink_blocks)
+                num_sink_blocks=wl.num_sink_blocks, block_size=wl.block_size)
 
 
 def run(wl, order=None, env=None, canary=True):
@@ -81,7 +81,8 @@ def check_stored(kv, wl, t, l):
     pool = oracle_pool(wl)
     for b, sid in enumerate(wl.decode_seqs):
         L = int(l[b])
-        assert [int(x) for x in t[b, :(L + 15) // 16]] == pool.seq_table(sid), f"table seq {sid}"
+        bs = wl.block_size
+        assert [int(x) for x in t[b, :(L + bs - 1) // bs]] == pool.seq_table(sid), f"table seq {sid}"
         K, V, codes = stored_values(wl, sid, fp16_tokens(wl, pool, sid))
         if codes is None:
             Kg, Vg = view.logical_kv(t[b], L)
@@ -640,3 +641,35 @@ def test_prefix_cache_hit_skips_prefill_and_decodes(dt):
     torch.cuda.synchronize()
     assert_close(out.double().cpu().numpy(), expected(wl), "f16" if dt == "int4" else "bf16",
                  f"prefix cache {dt}")
+
+
+# ---- block sizes 8 and 32 (raw 16-bit pools) ----------------------------------------
+BS_LENS = [1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 100, 1000, 2049]
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_block_sizes_storage_decode_verify(bs, dt):
+    """Pools of 8- and 32-token blocks: appended tokens land where the
+    layout rules for that block size put them; decode (default cut, small
+    fixed chunks, merge launch) and a verify step match the oracle, with
+    lengths around every block and tile edge."""
+    from _ref import expected_verify
+    wl = W.from_lengths(BS_LENS, 32, 8, 128, dt, seed=181 + bs, block_size=bs)
+    kv, out, t, l = run(wl)
+    check_stored(kv, wl, t, l)
+    ref = expected(wl)
+    assert_close(out, ref, dt, f"bs{bs} {dt}")
+    for env in ({"PA_SPLIT_BLOCKS": "3"}, {"PA_FUSE_MAX_PIECES": "1"}):
+        _, o2, _, _ = run(wl, env=env)
+        assert_close(o2, ref, dt, f"bs{bs} {dt} {env}")
+    _, outv = run_verify(wl, 6)
+    assert_close(outv, expected_verify(wl, 6), dt, f"bs{bs} {dt} verify")
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_block_sizes_full_llama3_8b_sampled(bs):
+    wl = W.by_name(f"llama3-8b-bs{bs}")
+    kv, out, t, l = run(wl)
+    pairs = _sample_pairs(wl, 16, 3)
+    assert_close(out, expected(wl, pairs=pairs), "bf16", f"llama3-8b bs{bs}")

@@ -72,6 +72,8 @@ def assert_same(kv: PagedKV, oracle: Pool, res_lib, res_or):
     ("mixed-int4", {"length": 300, "steps": 20}),
     ("mixed-fp8", {"length": 33, "steps": 40}),
     ("mixed-window", {"length": 300, "steps": 40}),
+    ("llama3-8b-bs8", {"batch": 16, "min_len": 1, "max_len": 700}),
+    ("llama3-8b-bs32", {"batch": 16, "min_len": 1, "max_len": 700}),
 ])
 def test_workload_op_logs_match_oracle(libpa, name, kw):
     wl = W.by_name(name, **kw)
@@ -79,7 +81,7 @@ def test_workload_op_logs_match_oracle(libpa, name, kw):
     res_lib = kv.replay(write=False)
     oracle = Pool(wl.num_blocks, wl.num_sink_blocks, wl.sink_blocks_per_seq,
                   body_free_order=wl.body_free_order, sink_free_order=wl.sink_free_order,
-                  window_tokens=wl.window_tokens)
+                  window_tokens=wl.window_tokens, block_size=wl.block_size)
     res_or = replay(oracle, wl.ops)
     assert_same(kv, oracle, res_lib, res_or)
     if name == "shared-prefix-partial":     # one clone per child that wrote a suffix
@@ -204,17 +206,18 @@ def test_window_op_logs_match_oracle(libpa, seed):
     assert_same(kv, oracle, res_lib, res_or)
 
 
-@pytest.mark.parametrize("kv_dtype,D,g,N,S", [
-    ("f32", 64, 0, 64, 0), ("bf16", 128, 0, 10171, 0), ("f16", 32, 0, 5, 0),
-    ("int4", 128, 128, 4509, 1), ("int4", 128, 64, 100, 3), ("int4", 256, 32, 7, 0),
-    ("fp8", 128, 0, 4509, 1), ("fp8", 64, 0, 9, 0)])
-def test_layout_matches_oracle(libpa, kv_dtype, D, g, N, S):
+@pytest.mark.parametrize("kv_dtype,D,g,N,S,bs", [
+    ("f32", 64, 0, 64, 0, 16), ("bf16", 128, 0, 10171, 0, 16), ("f16", 32, 0, 5, 0, 16),
+    ("int4", 128, 128, 4509, 1, 16), ("int4", 128, 64, 100, 3, 16), ("int4", 256, 32, 7, 0, 16),
+    ("fp8", 128, 0, 4509, 1, 16), ("fp8", 64, 0, 9, 0, 16), ("bf16", 128, 0, 777, 0, 8),
+    ("f16", 128, 0, 33, 0, 32)])
+def test_layout_matches_oracle(libpa, kv_dtype, D, g, N, S, bs):
     desc = B.make_desc(8, D, kv_dtype, N, group_size=g, num_sink_blocks=S,
-                       sink_blocks_per_seq=1 if S else 0)
+                       sink_blocks_per_seq=1 if S else 0, block_size=bs)
     pool = B.pa_pool_create(desc, None, 0)
     lay = B.pa_pool_layout(pool)
     B.pa_pool_destroy(pool)
-    arrays, total = LY.pool_arrays(B.DTYPES[kv_dtype], 8, D, g or D, N, S)
+    arrays, total = LY.pool_arrays(B.DTYPES[kv_dtype], 8, D, g or D, N, S, bs)
     rename = {"KC": "K", "VC": "V"}
     assert lay["total_bytes"] == total == B.pa_pool_bytes(desc)
     assert {rename.get(n, n): (o, s) for n, o, s, _ in arrays} == \
@@ -222,7 +225,9 @@ def test_layout_matches_oracle(libpa, kv_dtype, D, g, N, S):
 
 
 def test_error_paths(libpa):
-    bad = [B.make_desc(8, 100, "bf16", 10), B.make_desc(8, 128, "bf16", 10, block_size=8),
+    bad = [B.make_desc(8, 100, "bf16", 10), B.make_desc(8, 128, "int4", 10, group_size=64, block_size=8),
+           B.make_desc(8, 128, "bf16", 10, block_size=64), B.make_desc(8, 64, "bf16", 10, block_size=32),
+           B.make_desc(8, 128, "f32", 10, block_size=8),
            B.make_desc(8, 128, "int4", 10, group_size=48), B.make_desc(8, 96, "fp8", 10),
            B.make_desc(0, 128, "bf16", 10), B.make_desc(8, 128, "bf16", 10, num_sink_blocks=1,
                                                           sink_blocks_per_seq=1),

@@ -120,6 +120,36 @@ def test_layout_bijections(D):
             assert sorted(byte.ravel().tolist()) == list(range(n))
 
 
+@pytest.mark.parametrize("bs", [8, 32])
+def test_raw_layout_other_block_sizes(bs):
+    """Block sizes 8 and 32 (raw 16-bit pools, D = 128): the index functions
+    are bijections onto the slab, reduce to the 16-token rules' shape, and
+    keep 8 consecutive dims of one token (K) or 4 consecutive tokens of one
+    dim pair (V) in each 16-byte chunk, which a 16-token matrix-core tile
+    gathers from one block half (32) or from two blocks (8)."""
+    D = 128
+    k, v = LY.raw_k_index(D, bs), LY.raw_v_index(D, bs)
+    for idx in (k, v):
+        assert sorted(idx.ravel().tolist()) == list(range(bs * D))
+    for t in range(bs):                     # K chunk: token t, dims 8c..8c+7
+        for c in range(16):
+            row = k[t, 8 * c:8 * c + 8]
+            assert row.tolist() == list(range(row[0], row[0] + 8)) and row[0] % 8 == 0
+    nt = D // 16                            # V chunk: dims 8r + 2u, +1 of tokens 4q..4q+3
+    for q in range(bs // 4):
+        for r in range(16):
+            for u in range(nt // 2):
+                got = [v[4 * q + i, 8 * r + 2 * u + p] for p in range(2) for i in range(4)]
+                assert got == list(range(got[0], got[0] + 8)) and got[0] % 8 == 0
+    # the 16-token rules are the bs = 16 case of the same formulas, and a
+    # 32-token block is two 16-token slabs back to back
+    assert np.array_equal(LY.raw_k_index(D, 16), LY.raw_k_index(D))
+    assert np.array_equal(LY.raw_v_index(D, 16), LY.raw_v_index(D))
+    if bs == 32:
+        for idx, one in ((k, LY.raw_k_index(D)), (v, LY.raw_v_index(D))):
+            assert np.array_equal(idx[:16], one) and np.array_equal(idx[16:], one + 16 * D)
+
+
 def test_layout_load_units_D128():
     """The properties the header states for D = 128: every 16-byte unit read by
     lane l = 16*g + r (or 16*g + t) holds what the matrix-core tiles expect."""
