@@ -94,7 +94,8 @@ def split_and_copy(d, counter):
     return statistics.median(split[1:]), max(copies)   # drop the warm-up dispatch
 
 
-def summarize(cfg, trace_dir, fetch_dir, write_dir, bench_json, commands, src_hash=None):
+def summarize(cfg, trace_dir, fetch_dir, write_dir, bench_json, commands, src_hash=None,
+              plain_json=None):
     stats, split_ns, names = trace_summary(trace_dir)
     fetch_kib, fetch_copy = split_and_copy(fetch_dir, "FETCH_SIZE")
     write_kib, write_copy = split_and_copy(write_dir, "WRITE_SIZE")
@@ -155,6 +156,26 @@ def summarize(cfg, trace_dir, fetch_dir, write_dir, bench_json, commands, src_ha
         f"Bench line of the trace run: ms_per_step {bench['ms_per_step']}, value "
         f"{bench['value']} GB/s, roofline achieved {bench['roofline']['achieved']} GB/s.",
         "",
+    ]
+    if plain_json:
+        # the profiler adds host time to every launch; where a launch is
+        # shorter than that, the back-to-back launches starve and the events
+        # count the gaps, so the same command is also run without it
+        with open(plain_json) as f:
+            plain = json.loads(f.read().strip().splitlines()[-1])
+        entry["bench_split_avg_us_events_unprofiled"] = round(plain["roofline"]["avg_launch_ms"] * 1e3, 3)
+        lines += [
+            f"The same bench command without the profiler (`python3 bench.py --config {cfg} "
+            f"--steps 50 --warmup 10 --cpu-budget 0`): HIP-event average "
+            f"{entry['bench_split_avg_us_events_unprofiled']} µs per split launch, ms_per_step "
+            f"{plain['ms_per_step']}, value {plain['value']} GB/s, roofline achieved "
+            f"{plain['roofline']['achieved']} {plain['roofline']['unit']}. Under the profiler "
+            f"every launch also pays the tracer's host-side cost; where that exceeds the "
+            f"kernel's duration the back-to-back launches leave the GPU idle between them "
+            f"and the profiled run's event average counts those gaps.",
+            "",
+        ]
+    lines += [
         "## HBM bytes per split dispatch (rocprofv3 --pmc, one counter per run)",
         "",
         "| Counter | KiB per dispatch (median) | 1 GiB copy reads (KiB) | scale | bytes |",
@@ -204,12 +225,14 @@ def main():
     ap.add_argument("--write", required=True)
     ap.add_argument("--bench-json", required=True, help="bench.py output of the trace run")
     ap.add_argument("--commands", default="", help="file with the three commands, one per line")
+    ap.add_argument("--plain-bench-json", default=None,
+                    help="bench.py output of the same command run without the profiler")
     ap.add_argument("--source-hash", default=None,
                     help="source_hash() of the tree the runs were made from (default: this tree)")
     args = ap.parse_args()
     cmds = open(args.commands).read().strip().splitlines() if args.commands else []
     print(json.dumps(summarize(args.config, args.trace, args.fetch, args.write, args.bench_json, cmds,
-                               args.source_hash), indent=1))
+                               args.source_hash, args.plain_bench_json), indent=1))
 
 
 if __name__ == "__main__":
