@@ -25,6 +25,7 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config llama3-8b
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -236,6 +237,12 @@ def main():
         attn_split()
         attn_rest()
 
+    # the workload generator leaves millions of small Python objects; a full
+    # collection over them takes tens of milliseconds and, landing inside a
+    # timed loop, would be counted as GPU time: move them out of the
+    # collector's reach before timing
+    gc.collect()
+    gc.freeze()
     print(f"[bench] warmup {args.warmup} ...", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()

@@ -91,28 +91,15 @@ __device__ inline int seq_blocks(const DecodeArgs& a, int b) { return (seq_len(a
 // Segments per sequence: one per KV head and column slice.
 __device__ inline int seg_heads(const DecodeArgs& a) { return a.pool.n_kv_heads * max(a.col_slices, 1); }
 
-// Start of sequence b's segments in the flattened list: seg_heads * sum_{b'<b} nb_b'.
-__device__ inline int seq_start(const DecodeArgs& a, int b, int lane) {
-  int acc = 0;
-  for (int base = 0; base < b; base += 64) {
-    const int bb = base + lane;
-    acc += bb < b ? seq_blocks(a, bb) : 0;
-  }
-  return wave_sum_int(acc) * seg_heads(a);
-}
-
-// Total blocks of the flattened list (one wavefront, result in every lane).
-__device__ inline int total_work(const DecodeArgs& a, int lane) {
-  int tot = 0;
-  for (int base = 0; base < a.batch; base += 64)
-    tot += base + lane < a.batch ? seq_blocks(a, base + lane) * seg_heads(a) : 0;
-  return wave_sum_int(tot);
-}
-
 // LDS of a workgroup: per wave and output column (max, sum, acc) of the
 // current piece, reused as scratch by the segment merge.
+// Sequence lengths kept in LDS by setup_units for the first kLenCap
+// sequences (later ones are read from memory where needed).
+constexpr int kLenCap = 512;
+
 template <int CAP>
 struct SharedT {
+  int len[kLenCap];
   float m[kWaves][CAP];
   float l[kWaves][CAP];
   alignas(16) float o[kWaves][CAP][kD + 1];
@@ -122,6 +109,27 @@ struct SharedT {
   int last;
 };
 using Shared = SharedT<16>;
+
+// Length (tokens) and blocks of sequence b, from the LDS copy where it has one.
+template <class SH>
+__device__ inline int len_of(const DecodeArgs& a, const SH& sh, int b) {
+  return b < kLenCap ? sh.len[b] : seq_len(a, b);
+}
+template <class SH>
+__device__ inline int blocks_of(const DecodeArgs& a, const SH& sh, int b) {
+  return (len_of(a, sh, b) + 15) >> 4;
+}
+
+// Start of sequence b's segments in the flattened list: seg_heads * sum_{b'<b} nb_b'.
+template <class SH>
+__device__ inline int seq_start(const DecodeArgs& a, const SH& sh, int b, int lane) {
+  int acc = 0;
+  for (int base = 0; base < b; base += 64) {
+    const int bb = base + lane;
+    acc += bb < b ? blocks_of(a, sh, bb) : 0;
+  }
+  return wave_sum_int(acc) * seg_heads(a);
+}
 
 // Output columns of a segment (b, hv), hv = h*nsl + s (KV head h, column
 // slice s of SW columns): its column col is the (query, head) column
@@ -172,11 +180,19 @@ struct Units {
   __device__ int queued(int q) const { return (q % R) * per() + 1 + q / R; }
 };
 
-// Wave 0 sizes the cut from the lengths; every thread gets it.
+// Wave 0 reads the lengths (one load per sequence, kept in LDS for the
+// first kLenCap) and sizes the cut from them; every thread gets both.
 template <class SH>
 __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane) {
   if (w == 0) {
-    const int W = total_work(a, lane);
+    int tot = 0;
+    for (int base = 0; base < a.batch; base += 64) {
+      const int bb = base + lane;
+      const int L = bb < a.batch ? seq_len(a, bb) : 0;
+      if (bb < min(a.batch, kLenCap)) sh.len[bb] = L;
+      tot += ((L + 15) >> 4) * seg_heads(a);
+    }
+    const int W = wave_sum_int(tot);
     const int R = a.max_splits;  // the split kernel's grid
     int C, Cs, U = 1, m = 0;
     if (a.split_blocks > 0) {
@@ -213,7 +229,7 @@ __device__ inline void locate(const DecodeArgs& a, SH& sh, int w, int lane, int 
     int run = 0, f = 0, fbi = B;
     for (int base = 0; base < B; base += 64) {
       const int bb = base + lane;
-      const int sz = bb < B ? seq_blocks(a, bb) * H : 0;
+      const int sz = bb < B ? blocks_of(a, sh, bb) * H : 0;
       int incl = sz;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -276,23 +292,24 @@ __device__ inline int next_unit(const DecodeArgs& a, SH& sh, const Units& um) {
 
 // Zero the output rows of empty sequences (no piece covers them); workgroup
 // c takes sequences c, c + grid, ...
-template <typename TO>
-__device__ inline void zero_empty_rows(const DecodeArgs& a) {
+template <typename TO, class SH>
+__device__ inline void zero_empty_rows(const DecodeArgs& a, const SH& sh) {
   const int Hq = a.n_q_heads, nq = max(a.n_query, 1);
   TO* out = static_cast<TO*>(a.out);
   for (int b = blockIdx.x; b < a.batch; b += gridDim.x)
-    if (seq_blocks(a, b) == 0)
+    if (blocks_of(a, sh, b) == 0)
       for (int i = threadIdx.x; i < nq * Hq * kD; i += kWaves * 64)
         out[size_t(b) * nq * Hq * kD + i] = TO(0.f);
 }
 
 // The next piece [jbeg, jend) of segment (b, h) starting at position pos;
 // advances (b, fb) past finished or empty sequences.  False when done.
-__device__ inline bool next_piece(const DecodeArgs& a, int pos, int pos1, int& b, int& fb, int& h,
-                                  int& jbeg, int& jend, int& nb) {
+template <class SH>
+__device__ inline bool next_piece(const DecodeArgs& a, const SH& sh, int pos, int pos1, int& b,
+                                  int& fb, int& h, int& jbeg, int& jend, int& nb) {
   const int H = seg_heads(a);
   while (pos < pos1 && b < a.batch) {
-    nb = seq_blocks(a, b);
+    nb = blocks_of(a, sh, b);
     if (pos >= fb + nb * H) {
       fb += nb * H;
       ++b;

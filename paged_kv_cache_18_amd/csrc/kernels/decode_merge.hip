@@ -27,10 +27,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_merge_kernel(DecodeArgs a)
   if (hc >= om.cols(h)) return;  // past the last column of a short slice
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nb = seq_blocks(a, b);
-  if (nb == 0) return;  // workgroup-uniform
   const Units um = setup_units(a, sh, w, lane);
-  const int S = seq_start(a, b, lane) + h * nb;  // every wave computes it
+  const int nb = blocks_of(a, sh, b);
+  if (nb == 0) return;  // workgroup-uniform
+  const int S = seq_start(a, sh, b, lane) + h * nb;  // every wave computes it
   const int np = um.unit_of(S + nb - 1) - um.unit_of(S) + 1;
   if (np <= 1) return;
   merge_segment<TO>(a, sh, om, b, h, S, np, um, hc, 1);

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H;
   const OutMap om = out_map(a);
   const int nq = om.nq, nsl = om.nsl;
-  zero_empty_rows<T>(a);
   const Units um = setup_units(a, sh, w, lane);
+  zero_empty_rows<T>(a, sh);
   int b = 0, fb = 0;
 
   const T* kbase = reinterpret_cast<const T*>(p.base + p.off[kArrK]);
@@ -227,8 +227,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   int pos = pos0;
   bool first = true;
   int jbeg = 0, jend = 0, nb = 0;
-  while (next_piece(a, pos, pos1, b, fb, hv, jbeg, jend, nb)) {
-    L = seq_len(a, b);
+  while (next_piece(a, sh, pos, pos1, b, fb, hv, jbeg, jend, nb)) {
+    L = len_of(a, sh, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
     h = hv / nsl;
     const int ncol = om.cols(hv);

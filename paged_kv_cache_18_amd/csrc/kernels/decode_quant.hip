@@ -39,11 +39,36 @@ typedef _Float16 h8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef _Float16 h4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
 typedef _Float16 h2 __attribute__((__vector_size__(2 * sizeof(_Float16))));
 
-// Nibbles at bits shift..shift+3 and shift+16..shift+19 of x -> fp16 pair.
-__device__ inline uint32_t nib2h(uint32_t x, int shift) {
-  const uint32_t t = ((x >> shift) & 0x000F000Fu) | 0x64006400u;  // 1024 + n
-  h2 v = __builtin_bit_cast(h2, t) - h2{_Float16(1024.f), _Float16(1024.f)};
-  return __builtin_bit_cast(uint32_t, v);
+// INT4 codes to exact fp16 values.  A nibble n placed in the low mantissa
+// bits under 0x6400 reads as 1024 + n; one bit-select and one packed
+// subtract give n.  A nibble at mantissa bits 4..7 reads as 1024 + 16n, and
+// one packed fma, x/16 - 64, gives n (both steps exact in fp16).
+// nib4(x): the fp16 pairs of the nibbles at bits (s, s + 16), s = 0, 4, 8, 12.
+__device__ inline uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
+__device__ inline uint32_t nib_lo(uint32_t x) {  // bits 0..3 and 16..19
+  const h2 v = __builtin_bit_cast(h2, and_or(x, 0x000F000Fu, 0x64006400u));
+  return __builtin_bit_cast(uint32_t, v - h2{_Float16(1024.f), _Float16(1024.f)});
+}
+__device__ inline uint32_t nib_hi(uint32_t x) {  // bits 4..7 and 20..23
+  const h2 v = __builtin_bit_cast(h2, and_or(x, 0x00F000F0u, 0x64006400u));
+  return __builtin_bit_cast(
+      uint32_t, __builtin_elementwise_fma(v, h2{_Float16(0.0625f), _Float16(0.0625f)},
+                                          h2{_Float16(-64.f), _Float16(-64.f)}));
+}
+__device__ inline u32x4 nib4(uint32_t x) {
+  const uint32_t y = x >> 8;
+  return u32x4{nib_lo(x), nib_hi(x), nib_lo(y), nib_hi(y)};
+}
+
+// Keep v in a register where it is computed: a select of it then stays a
+// select instead of becoming a branch around its computation.
+__device__ inline float pin(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // E4M3 codes in bytes 0,1 (HI = false) or 2,3 (HI = true) of y -> fp16 pair,
@@ -154,8 +179,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   const int qcol = c < NG * G ? (NG == 1 ? c : c % G) : -1;  // query head (within the group) of column c
   const int gsel = NG == 1 ? 0 : min(c / G, NG - 1);  // scale group of column c
   const int keep = c - (NG == 1 ? 0 : (g * NG / 4) * G);  // column this lane writes
-  zero_empty_rows<_Float16>(a);
   const Units um = setup_units(a, sh, w, lane);
+  zero_empty_rows<_Float16>(a, sh);
   int b = 0, fb = 0;
 
   const float sl2 = a.scale_log2;
@@ -224,7 +249,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const uint32_t cw = bf.kc[kk];
-        const u32x4 av = {nib2h(cw, 0), nib2h(cw, 4), nib2h(cw, 8), nib2h(cw, 12)};
+        const u32x4 av = nib4(cw);
         acc[kk * NG / 4] = MF::qk(__builtin_bit_cast(h8, av), qp[kk], acc[kk * NG / 4]);
       }
 #pragma unroll
@@ -233,7 +258,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
 #pragma unroll
         for (int k = 0; k < NG; ++k)
           sc += half_at(bf.ks, i * NG + k) * (acc[k][i] - half_at(bf.kz, i * NG + k) * qs[k]);
-        x[i] = (4 * g + i < valid) ? sc * sl2 : -__builtin_inff();
+        const float xs = pin(sc * sl2);
+        x[i] = (4 * g + i < valid) ? xs : -__builtin_inff();
       }
     } else {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -245,8 +271,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
         acc = MF::qk(__builtin_bit_cast(h8, av), qp[kk], acc);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        x[i] = (4 * g + i < valid) ? half_at(bf.ks, i) * acc[i] * sl2 : -__builtin_inff();
+      for (int i = 0; i < 4; ++i) {
+        const float xs = pin(half_at(bf.ks, i) * acc[i] * sl2);
+        x[i] = (4 * g + i < valid) ? xs : -__builtin_inff();
+      }
     }
     float pw[4];
     softmax(x, valid, pw);
@@ -254,14 +282,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     // may be garbage: select
     float pv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pv[i] = (4 * g + i < valid) ? half_sel<NG>(bf.vs, i, gsel) * pw[i] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const float w_ = pin(half_sel<NG>(bf.vs, i, gsel) * pw[i]);
+      pv[i] = (4 * g + i < valid) ? w_ : 0.f;
+    }
     // FP8: zero the bytes of tail tokens (unwritten slots may hold NaN codes)
     const int t0 = 4 * g;
     const uint32_t vmask = (t0 + 0 < valid ? 0x000000FFu : 0u) | (t0 + 1 < valid ? 0x0000FF00u : 0u) |
                            (t0 + 2 < valid ? 0x00FF0000u : 0u) | (t0 + 3 < valid ? 0xFF000000u : 0u);
     if constexpr (KIND == kInt4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) corr += (4 * g + i < valid) ? half_sel<NG>(bf.vz, i, gsel) * pv[i] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const float z_ = pin(half_sel<NG>(bf.vz, i, gsel) * pv[i]);
+        corr += (4 * g + i < valid) ? z_ : 0.f;
+      }
     }
     // B operand in the token order of the code pairs: INT4 (t0, t2), (t1, t3);
     // FP8 natural
@@ -276,10 +310,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     for (int T_ = 0; T_ < kNT; ++T_) {
       uint32_t lo, hi;
       if constexpr (KIND == kInt4) {
-        const uint32_t cw = bf.vc[T_ >> 1];
+        const u32x4 nv = nib4(bf.vc[T_ >> 1]);
         const int par = T_ & 1;
-        lo = nib2h(cw, 4 * par);      // tokens (t0, t2)
-        hi = nib2h(cw, 8 + 4 * par);  // tokens (t1, t3)
+        lo = nv[par];      // bits 4par: tokens (t0, t2)
+        hi = nv[2 + par];  // bits 8 + 4par: tokens (t1, t3)
       } else {
         const uint32_t cw = (T_ < 4 ? bf.vc0[T_] : bf.vc1[T_ - 4]) & vmask;
         lo = fp8pair<false>(cw);  // tokens (t0, t1)
@@ -350,22 +384,30 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   int pos = pos0;
   bool first = true;
   int jbeg = 0, jend = 0, nb = 0;
-  while (next_piece(a, pos, pos1, b, fb, h, jbeg, jend, nb)) {
-    L = seq_len(a, b);
+  while (next_piece(a, sh, pos, pos1, b, fb, h, jbeg, jend, nb)) {
+    L = len_of(a, sh, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
     const int lo = max(jbeg, SP);  // first non-sink block of the piece
     // the table's last 64 entries of the piece, for the window scan below
-    int tid = trow[max(jend - 1 - lane, 0)];
+    int tid = p.window_tokens > 0 ? trow[max(jend - 1 - lane, 0)] : 0;
+    // Q^T fragment of head qcol (dims 32kk + 8g + 0..7): loaded here, and
+    // permuted into the order in which the code conversion delivers the K
+    // elements (and summed per group) once the body's first blocks are in
+    // flight
+    h8 qraw[4];
     {
-      // Q^T fragment of head qcol (dims 32kk + 8g + 0..7), permuted into the
-      // order in which the code conversion delivers the K elements
       const _Float16* qn =
           static_cast<const _Float16*>(a.q) + (size_t(b) * Hq + h * G + max(qcol, 0)) * kD + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qraw[kk] = qcol >= 0 ? *reinterpret_cast<const h8*>(qn + 32 * kk) : h8{};
+    }
+    auto prep_q = [&]() {
 #pragma unroll
       for (int k = 0; k < NG; ++k) qs[k] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const h8 q = qcol >= 0 ? *reinterpret_cast<const h8*>(qn + 32 * kk) : h8{};
+        const h8 q = qraw[kk];
 #pragma unroll
         for (int e = 0; e < 8; ++e) qs[kk * NG / 4] += float(q[e]);
         if constexpr (KIND == kInt4)
@@ -374,11 +416,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
           qp[kk] = q;
       }
 #pragma unroll
-      for (int k = 0; k < NG; ++k) {
-        qs[k] += __shfl_xor(qs[k], 16, 64);
-        qs[k] += __shfl_xor(qs[k], 32, 64);
-      }
-    }
+      for (int k = 0; k < NG; ++k) qs[k] = rows_sum(qs[k]);
+    };
 #pragma unroll
     for (int T_ = 0; T_ < kNT; ++T_) o[T_] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_ref = -__builtin_inff();
@@ -402,6 +441,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       }
       // table entries are read one block ahead of the fetch that needs them
       int nid = id_of(NB - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      prep_q();
       int k = 0;
       for (; k + NB <= n; k += NB) {
         prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
@@ -420,6 +461,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
 #pragma unroll
       for (int s = 0; s < NB - 1; ++s)
         if (k + s < n) consume(valid_of(k + s, ids[s]), buf[s]);
+    } else {
+      prep_q();
     }
 
     // the window's FP16 run [jt, jend): count FP16 ids backward from jend - 1
@@ -491,14 +534,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
 }  // namespace
 
 // Prefetch depth: PA_QUANT_NB = 2 (3 waves per SIMD), 3, 4 or 6 (2 waves per
-// SIMD).  Default 2 for one scale group per token; with two groups the
-// buffers' extra scale/zero words do not fit three waves, default 3.
+// SIMD).  Default 3: two blocks in flight per wave at two waves per SIMD
+// measured faster than one at three for INT4 (both group sizes) and FP8.
 // (Read at every launch, as the other tuning variables are.)
 template <int NG>
 int quant_nb() {
   const char* e = std::getenv("PA_QUANT_NB");
   const int v = e ? std::atoi(e) : 0;
-  return (v == 2 || v == 3 || v == 4 || v == 6) ? v : (NG == 1 ? 2 : 3);
+  return (v == 2 || v == 3 || v == 4 || v == 6) ? v : 3;
 }
 
 template <int KIND, int NB, int NG>
