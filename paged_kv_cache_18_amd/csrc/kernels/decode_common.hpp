@@ -93,13 +93,15 @@ __device__ inline int seg_heads(const DecodeArgs& a) { return a.pool.n_kv_heads 
 
 // LDS of a workgroup: per wave and output column (max, sum, acc) of the
 // current piece, reused as scratch by the segment merge.
-// Sequence lengths kept in LDS by setup_units for the first kLenCap
-// sequences (later ones are read from memory where needed).
+// Sequence lengths, and the running sums of their list positions, kept in
+// LDS by setup_units for the first kLenCap sequences (later ones are read
+// from memory where needed).
 constexpr int kLenCap = 512;
 
 template <int CAP>
 struct SharedT {
   int len[kLenCap];
+  int pre[kLenCap];  // list positions of sequences 0..b (blocks times segments per sequence)
   float m[kWaves][CAP];
   float l[kWaves][CAP];
   alignas(16) float o[kWaves][CAP][kD + 1];
@@ -123,6 +125,8 @@ __device__ inline int blocks_of(const DecodeArgs& a, const SH& sh, int b) {
 // Start of sequence b's segments in the flattened list: seg_heads * sum_{b'<b} nb_b'.
 template <class SH>
 __device__ inline int seq_start(const DecodeArgs& a, const SH& sh, int b, int lane) {
+  if (b == 0) return 0;
+  if (b <= kLenCap) return sh.pre[b - 1];
   int acc = 0;
   for (int base = 0; base < b; base += 64) {
     const int bb = base + lane;
@@ -185,14 +189,23 @@ struct Units {
 template <class SH>
 __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane) {
   if (w == 0) {
-    int tot = 0;
+    int W = 0;
     for (int base = 0; base < a.batch; base += 64) {
       const int bb = base + lane;
       const int L = bb < a.batch ? seq_len(a, bb) : 0;
-      if (bb < min(a.batch, kLenCap)) sh.len[bb] = L;
-      tot += ((L + 15) >> 4) * seg_heads(a);
+      const int sz = ((L + 15) >> 4) * seg_heads(a);
+      int incl = sz;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      if (bb < min(a.batch, kLenCap)) {
+        sh.len[bb] = L;
+        sh.pre[bb] = W + incl;
+      }
+      W += __shfl(incl, 63, 64);
     }
-    const int W = wave_sum_int(tot);
     const int R = a.max_splits;  // the split kernel's grid
     int C, Cs, U = 1, m = 0;
     if (a.split_blocks > 0) {
@@ -219,12 +232,27 @@ __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane
   return Units{sh.units[0], sh.units[1], sh.units[2], sh.units[3], sh.units[4], sh.units[5]};
 }
 
-// Wave 0 finds the sequence b holding position p0 and the position fb of its
-// first block; every thread gets them.
+// The sequence b holding position p0 and the position fb of its first block.
+// Every wave reads them from the running sums in LDS where the batch fits
+// there; otherwise wave 0 scans the lengths and every thread gets them.
 template <class SH>
 __device__ inline void locate(const DecodeArgs& a, SH& sh, int w, int lane, int p0, int& b,
                               int& fb) {
   const int H = seg_heads(a), B = a.batch;
+  if (B <= kLenCap) {
+    b = B;
+    fb = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int bb = base + lane;
+      const unsigned long long hit = __ballot(bb < B && sh.pre[bb] > p0);
+      if (hit) {
+        b = base + __builtin_ctzll(hit);
+        fb = b > 0 ? __builtin_amdgcn_readfirstlane(sh.pre[b - 1]) : 0;
+        break;
+      }
+    }
+    return;
+  }
   if (w == 0) {
     int run = 0, f = 0, fbi = B;
     for (int base = 0; base < B; base += 64) {
