@@ -324,15 +324,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   }
 }
 
-// Prefetch depth (PA_MFMA_NB = 2, 3 or 4; default 2).
+// Prefetch depth (PA_MFMA_NB = 2, 3 or 4; default 2).  Read at every launch,
+// as the other tuning variables are.
 int mfma_nb() {
-  static int nb = 0;
-  if (nb == 0) {
-    const char* e = std::getenv("PA_MFMA_NB");
-    const int v = e ? std::atoi(e) : 2;
-    nb = (v == 3 || v == 4) ? v : 2;
-  }
-  return nb;
+  const char* e = std::getenv("PA_MFMA_NB");
+  const int v = e ? std::atoi(e) : 2;
+  return (v == 3 || v == 4) ? v : 2;
 }
 
 template <typename T, int BS>
@@ -392,10 +389,11 @@ hipError_t launch_decode_split_mfma16(const DecodeArgs& a, hipStream_t s) {
 
 // nct: 0 = decode, 1 or 2 = verify step with that many column tiles.
 int occupancy_mfma16(int32_t kv_dtype, int nct) {
-  static int cache[2][3] = {{0, 0, 0}, {0, 0, 0}};
+  static int cache[2][3][5] = {};  // [dtype][column tiles][prefetch depth]
   const int i = kv_dtype == kBF16 ? 0 : 1;
-  if (cache[i][nct] == 0) cache[i][nct] = i == 0 ? occupancy_nb<__bf16>(nct) : occupancy_nb<_Float16>(nct);
-  return cache[i][nct];
+  int& c = cache[i][nct][nct == 0 ? mfma_nb() : 2];
+  if (c == 0) c = i == 0 ? occupancy_nb<__bf16>(nct) : occupancy_nb<_Float16>(nct);
+  return c;
 }
 
 }  // namespace pa
