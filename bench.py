@@ -335,7 +335,7 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(tfl / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
                     "traffic_unit": "GB/s", "traffic_bytes_per_launch": tb,
-                    "flops_per_launch": flops, "kernel": "decode_split (prefill chunk)",
+                    "flops_per_launch": flops, "kernel": "prefill_tile",
                     "avg_launch_ms": round(split_avg, 5)}
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -74,6 +74,11 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t s);
 // Merge launch of the matrix-core kernels (defer_merge = 1).
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
 
+// Chunked-prefill attention of 16-bit pools of 16-token blocks (n_query
+// queries per sequence, causal): one workgroup per (sequence, KV head, group
+// of 128 (query, head) columns), no workspace.
+hipError_t launch_prefill_tile(const DecodeArgs& a, hipStream_t s);
+
 // Streaming read of `bytes` (a multiple of 16) at src with `grid` workgroups.
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, int grid, hipStream_t s);
 

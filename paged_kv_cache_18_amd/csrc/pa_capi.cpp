@@ -269,10 +269,17 @@ enum Phase { kBoth = 3, kSplit = 1, kCombine = 2 };
 
 constexpr int32_t kMaxQueries = 4096;  // verify step / prefill chunk: queries per sequence, at most
 
+// Prefill chunks of 16-bit pools of 16-token blocks go to the tile kernel
+// (PA_PREFILL_TILE=0 keeps them on the split kernel, for comparison).
+bool prefill_tile(const pa_pool* pool, const Plan& pl) {
+  return pl.kernel == pa::kKernMfma16 && pool->core.desc().block_size == 16 &&
+         env_int("PA_PREFILL_TILE", 1) != 0;
+}
+
 pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* tables,
                  const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t q_dtype,
                  int32_t max_blocks, int32_t max_seq_len, float scale, void* out, void* ws,
-                 size_t ws_bytes, void* stream, int32_t n_query = 1) {
+                 size_t ws_bytes, void* stream, int32_t n_query = 1, bool prefill = false) {
   return guard([&] {
     need_device(pool);
     check_shapes(pool, batch, n_q_heads, max_seq_len);
@@ -293,9 +300,10 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     need(lens, "seq_lens_dev");
     need(out, "out");
     const Plan pl = make_plan(pool, batch, n_q_heads, max_seq_len, q_dtype, n_query);
+    const bool tile = prefill && prefill_tile(pool, pl);
     if (pl.kernel == pa::kKernGeneric && int64_t(batch) * n_query > 65535)
       fail(pa::kUnsupported, "batch * n_query above 65535 on the generic kernel");
-    if (pl.ws_bytes > 0) {
+    if (!tile && pl.ws_bytes > 0) {
       need(ws, "workspace");
       if (ws_bytes < pl.ws_bytes)
         fail(pa::kInvalidArg, "workspace too small: need " + std::to_string(pl.ws_bytes) + " bytes");
@@ -314,6 +322,11 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     a.n_query = n_query;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out = out;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (tile) {
+      if (phase & kSplit) check_hip(pa::launch_prefill_tile(a, s), "prefill launch");
+      return;
+    }
     if (pl.ws_bytes) {
       a.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.ws_o_offset);
       a.ws_ml = a.ws_o + pl.ws_ml_offset;
@@ -328,7 +341,6 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     a.split_blocks = pl.split_blocks;
     a.max_splits = pl.max_splits;
     a.kernel = pl.kernel;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     if (phase & kSplit) check_hip(pa::launch_decode_split(a, s), "decode split launch");
     if (phase & kCombine) check_hip(pa::launch_decode_combine(a, s), "decode combine launch");
   });
@@ -688,7 +700,15 @@ pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t*
 
 pa_status pa_prefill_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
                                      int32_t chunk, int32_t max_seq_len, size_t* bytes) {
-  return pa_verify_workspace_bytes(pool, batch, n_q_heads, chunk, max_seq_len, bytes);
+  return guard([&] {
+    check_shapes(pool, batch, n_q_heads, max_seq_len);
+    need(bytes, "bytes");
+    if (chunk < 1 || chunk > kMaxQueries) fail(pa::kInvalidArg, "chunk must be in [1, 4096]");
+    const pa::Desc& d = pool->core.desc();
+    const int32_t qdt = pa::is_raw(d.kv_dtype) ? d.kv_dtype : int32_t(pa::kF16);
+    const Plan pl = make_plan(pool, batch, n_q_heads, max_seq_len, qdt, chunk);
+    *bytes = prefill_tile(pool, pl) ? 0 : pl.ws_bytes;
+  });
 }
 
 pa_status pa_prefill_attention(const void* q, const pa_pool* pool, const int32_t* tables,
@@ -697,7 +717,7 @@ pa_status pa_prefill_attention(const void* q, const pa_pool* pool, const int32_t
                                int32_t max_seq_len, float scale, void* out, void* ws,
                                size_t ws_bytes, void* stream) {
   return decode(kBoth, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
-                scale, out, ws, ws_bytes, stream, chunk);
+                scale, out, ws, ws_bytes, stream, chunk, true);
 }
 
 pa_status pa_stream_read(const void* src, size_t bytes, void* sink, void* stream) {

@@ -57,7 +57,7 @@ def _rows(d, name):
 
 
 def _is_split(name):
-    return "decode_split" in name
+    return "decode_split" in name or "prefill_tile" in name
 
 
 def trace_summary(d):

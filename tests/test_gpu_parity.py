@@ -555,15 +555,16 @@ def expected_prefill_chunk(wl, k, n, seqs):
     return np.stack(out)
 
 
-@pytest.mark.parametrize("hq,chunk", [(32, 256), (64, 128), (8, 512)])
-def test_prefill_chunks_match_oracle(hq, chunk):
+@pytest.mark.parametrize("hq,hkv,chunk", [(32, 8, 256), (64, 8, 128), (8, 8, 512), (12, 4, 200)])
+def test_prefill_chunks_match_oracle(hq, hkv, chunk):
     """A batch of prompts prefilled chunk by chunk (blocks interleaved across
     sequences by the chunk rounds): every chunk's attention -- (query, head)
-    columns cut into 32-column slices once there are more than 32, causal
+    columns in groups of 128 per workgroup, the last group short, causal
     inside the chunk -- matches the oracle; the ragged last chunk of a prompt
-    runs as its own call."""
+    runs as its own call.  (12, 4): a (sequence, KV head) count that is not a
+    multiple of the 8 XCDs."""
     lengths = [3 * chunk, 2 * chunk + 37, chunk]
-    wl = W.chunked_prefill(seed=151, lengths=lengths, chunk=chunk, n_q_heads=hq)
+    wl = W.chunked_prefill(seed=151, lengths=lengths, chunk=chunk, n_q_heads=hq, n_kv_heads=hkv)
     kv = PagedKV(wl, DEV)
     kv.replay()
     for k in range(3):
@@ -574,12 +575,15 @@ def test_prefill_chunks_match_oracle(hq, chunk):
     assert_close(out, expected_prefill_chunk(wl, 2, 37, [1]), "bf16", "ragged last chunk")
 
 
-@pytest.mark.parametrize("env", [{"PA_SPLIT_BLOCKS": "3"}, {"PA_FUSE_MAX_PIECES": "1"},
+@pytest.mark.parametrize("env", [{}, {"PA_PREFILL_TILE": "0"},
+                                 {"PA_PREFILL_TILE": "0", "PA_SPLIT_BLOCKS": "3"},
+                                 {"PA_PREFILL_TILE": "0", "PA_FUSE_MAX_PIECES": "1"},
                                  {"PA_DECODE_KERNEL": "generic"}])
 def test_prefill_chunk_split_merge_and_generic(env):
-    """One 300-token chunk over a 700-token cache: short last column slice
-    (300 x 4 = 1,200 columns = 37.5 slices), fixed small chunks of the work
-    list, the merge as a second launch, and the generic kernel."""
+    """One 300-token chunk over a 700-token cache (300 x 4 = 1,200 columns):
+    the tile kernel (9.4 groups of 128 columns); the split kernel's 32-column
+    slices (37.5, the last one short), with fixed small chunks of the work
+    list and with the merge as a second launch; and the generic kernel."""
     wl = W.chunked_prefill(seed=152, lengths=[700, 700], chunk=400)
     kv = PagedKV(wl, DEV)
     kv.replay()
@@ -589,7 +593,7 @@ def test_prefill_chunk_split_merge_and_generic(env):
 
 def test_prefill_full_workload_last_chunk_sampled():
     """The bench's prefill workload (4 x 4,096 tokens, 512-token chunks): the
-    last chunk's attention, 64 slices of 32 columns per KV head, checked on
+    last chunk's attention, 16 groups of 128 columns per KV head, checked on
     sampled (sequence, query) rows."""
     wl = W.by_name("prefill-chunk")
     kv = PagedKV(wl, DEV)
