@@ -351,7 +351,9 @@ pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t*
 
 /* ---- chunked paged prefill ---------------------------------------------------- */
 
-/* Workspace bytes pa_prefill_attention needs for these shapes. */
+/* Workspace bytes pa_prefill_attention needs for these shapes: 0 for bf16 /
+ * fp16 pools of 16-token blocks (served by a kernel that needs none), else
+ * the split kernel's workspace. */
 pa_status pa_prefill_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
                                      int32_t chunk, int32_t max_seq_len, size_t* bytes);
 
@@ -366,7 +368,12 @@ pa_status pa_prefill_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t
  * for chunks up to 4096 tokens:
  *  q, out: device [batch][chunk][n_q_heads][head_dim] of q_dtype.
  *  chunk: 1..4096.  Other arguments and the workspace contract are those of
- *  pa_decode_attention. */
+ *  pa_decode_attention (workspace may be NULL when
+ *  pa_prefill_workspace_bytes gives 0).
+ * For bf16 / fp16 pools of 16-token blocks one workgroup computes 128
+ * (query, head) columns of one (sequence, KV head) over every block they
+ * see, with the blocks staged once in LDS for all its waves; other pools run
+ * the verify step's split kernel. */
 pa_status pa_prefill_attention(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
                                const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
                                int32_t chunk, int32_t q_dtype, int32_t max_blocks_per_seq,
