@@ -10,7 +10,7 @@ Three runs per workload, each with the program straight after ``--``::
       python3 bench.py --config C --steps 5 --warmup 1 --cpu-budget 0 --copy-calibration
 
 ``python -m paged_kv_cache_18_amd.profiling --config C --trace T --fetch F
---write W --bench-json B`` then writes ``profiles/decode_split_C.md`` and the
+--write W --bench-json B`` then writes ``profiles/<kernel>_C.md`` and the
 workload's entry of ``profiles/hbm_traffic.json``.  FETCH_SIZE and WRITE_SIZE
 (KiB per dispatch) are scaled by what they read for the 1 GiB device copy of
 ``--copy-calibration`` in the same run.  bench.py reports the scaled bytes per
@@ -34,15 +34,16 @@ TRAFFIC_JSON = os.path.join(PROFILES, "hbm_traffic.json")
 COPY_BYTES = 1 << 30
 
 
-# the files that decide the decode split kernel's code and launch
-# configuration (other kernels do not change its counters)
+# the files that decide the timed kernels' code and launch configuration
+# (other kernels do not change their counters)
 HASHED = ["build.py", "csrc/pa_capi.cpp", "csrc/kernels/common.hpp", "csrc/kernels/launch.hpp",
           "csrc/kernels/decode_common.hpp", "csrc/kernels/decode_mfma.hip",
-          "csrc/kernels/decode_quant.hip", "csrc/kernels/decode_generic.hip"]
+          "csrc/kernels/decode_quant.hip", "csrc/kernels/decode_generic.hip",
+          "csrc/kernels/prefill_tile.hip"]
 
 
 def source_hash():
-    """sha256 over the sources of the decode split kernel and its launch."""
+    """sha256 over the sources of the timed kernels and their launch."""
     h = hashlib.sha256()
     for rel in HASHED:
         h.update(rel.encode())
@@ -124,10 +125,11 @@ def summarize(cfg, trace_dir, fetch_dir, write_dir, bench_json, commands, src_ha
         "bench_ms_per_step": bench["ms_per_step"],
     }
     lines = [
-        f"# decode split kernel — `{cfg}` workload: kernel trace and HBM counters",
+        f"# dominant kernel — `{cfg}` workload: kernel trace and HBM counters",
         "",
         f"Workload: {bench['config']['workload']}.",
-        f"Split kernel(s): {', '.join('`' + n + '`' for n in names)}.",
+        f"Timed kernel(s) (the decode split, or the prefill tile kernel): "
+        f"{', '.join('`' + n + '`' for n in names)}.",
         "",
         "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):",
         "",
@@ -188,7 +190,8 @@ def summarize(cfg, trace_dir, fetch_dir, write_dir, bench_json, commands, src_ha
         "",
     ]
     os.makedirs(PROFILES, exist_ok=True)
-    with open(os.path.join(PROFILES, f"decode_split_{cfg}.md"), "w") as f:
+    kernel = "prefill_tile" if any("prefill_tile" in n for n in names) else "decode_split"
+    with open(os.path.join(PROFILES, f"{kernel}_{cfg}.md"), "w") as f:
         f.write("\n".join(lines))
     data = {}
     if os.path.exists(TRAFFIC_JSON):
