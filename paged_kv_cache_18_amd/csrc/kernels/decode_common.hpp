@@ -31,6 +31,11 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 
 template <typename T>
 struct Mfma;
+// pv(a, b, c): c + A B on 16x16x16 (A = a: lane (g, r) holds A[r][4g..4g+3];
+// B = b: lane (g, c) holds B[4g..4g+3][c]).  pv2(a, hi, lo, c) = pv(a, hi,
+// pv(a, lo, c)) up to fp32 rounding in one 16x16x32 product: lane group g
+// covers k = 8g..8g+7 there, and k = 8g + e is paired with token 4g + (e & 3)
+// of part e / 4 -- A = (a, a), B = (hi, lo), so no value moves across lanes.
 
 template <>
 struct Mfma<__bf16> {
@@ -41,6 +46,11 @@ struct Mfma<__bf16> {
   }
   static __device__ inline f32x4 pv(v4 a, v4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // a (hi + lo) in one 16x16x32 product (see pv2 below)
+  static __device__ inline f32x4 pv2(v4 a, v4 hi, v4 lo, f32x4 c) {
+    return qk(v8{a[0], a[1], a[2], a[3], a[0], a[1], a[2], a[3]},
+              v8{hi[0], hi[1], hi[2], hi[3], lo[0], lo[1], lo[2], lo[3]}, c);
   }
 };
 
@@ -53,6 +63,10 @@ struct Mfma<_Float16> {
   }
   static __device__ inline f32x4 pv(v4 a, v4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ inline f32x4 pv2(v4 a, v4 hi, v4 lo, f32x4 c) {
+    return qk(v8{a[0], a[1], a[2], a[3], a[0], a[1], a[2], a[3]},
+              v8{hi[0], hi[1], hi[2], hi[3], lo[0], lo[1], lo[2], lo[3]}, c);
   }
 };
 

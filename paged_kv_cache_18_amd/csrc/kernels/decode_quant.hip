@@ -321,8 +321,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       }
       const u32x2 av = {lo, hi};
       const h4 at = __builtin_bit_cast(h4, av);
-      o[T_] = MF::pv(at, bhi, o[T_]);
-      o[T_] = MF::pv(at, blo, o[T_]);
+      o[T_] = MF::pv2(at, bhi, blo, o[T_]);
     }
   };
 
@@ -367,8 +366,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       for (int par = 0; par < 2; ++par) {
         const u32x2 av = {dw[2 * par], dw[2 * par + 1]};
         const h4 at = __builtin_bit_cast(h4, av);
-        o[2 * u + par] = MF::pv(at, bhi, o[2 * u + par]);
-        o[2 * u + par] = MF::pv(at, blo, o[2 * u + par]);
+        o[2 * u + par] = MF::pv2(at, bhi, blo, o[2 * u + par]);
       }
     }
   };

@@ -23,8 +23,8 @@
 // Per block and wave the arithmetic is the decode kernel's (decode_mfma.hip):
 // S^T = K Q^T with v_mfma_f32_16x16x32 per tile, the causal mask per column,
 // the online softmax in the log2 domain with a lazily moved reference, the
-// weights split into a 16-bit high part and residual, and O^T += V^T P^T with
-// v_mfma_f32_16x16x16 per 16-dim row tile.
+// weights split into a 16-bit high part and residual, and O^T += V^T P^T per
+// 16-dim row tile with both parts in one v_mfma_f32_16x16x32.
 #include "decode_common.hpp"
 
 namespace pa {
@@ -180,8 +180,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
       for (int par = 0; par < 2; ++par) {
         const v4 vt = {vf[u][4 * par + 0], vf[u][4 * par + 1], vf[u][4 * par + 2], vf[u][4 * par + 3]};
-        o[2 * u + par] = Mfma<T>::pv(vt, phi, o[2 * u + par]);
-        o[2 * u + par] = Mfma<T>::pv(vt, plo, o[2 * u + par]);
+        o[2 * u + par] = Mfma<T>::pv2(vt, phi, plo, o[2 * u + par]);
       }
     }
   };
