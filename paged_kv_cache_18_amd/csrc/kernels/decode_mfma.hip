@@ -73,14 +73,25 @@ struct TileId {
   int a, b;  // 8-token blocks: the two block ids
 };
 
-template <typename T, int NB, int NCT, bool CAUSAL, int BS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 && !CAUSAL ? 3 : 2))) void decode_split_mfma16(DecodeArgs a) {
+//
+// SPLIT (two column tiles only): waves 0, 1 compute tile 0 and waves 2, 3
+// tile 1, each pair taking the piece's blocks alternately, so a wave carries
+// one tile's registers (three waves per SIMD instead of two) and every block
+// is read by two waves of the workgroup (the second from L2).
+template <typename T, int NB, int NCT, bool CAUSAL, int BS, bool SPLIT = false>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(
+    NB == 2 && (!CAUSAL || SPLIT) ? 3 : 2))) void decode_split_mfma16(DecodeArgs a) {
   typedef typename Mfma<T>::v8 v8;
   typedef typename Mfma<T>::v4 v4;
+  static_assert(!SPLIT || NCT == 2, "tile split needs two tiles");
+  constexpr int NT = SPLIT ? 1 : NCT;  // tiles a wave computes
   __shared__ SharedT<16 * NCT> sh;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int t0 = SPLIT ? w >> 1 : 0;       // this wave's first tile
+  const int nst = SPLIT ? 2 : kWaves;      // waves sharing a tile's blocks
+  const int ws = SPLIT ? w & 1 : w;        // this wave's place among them
   const int g = lane >> 4, c = lane & 15;
   const PoolDev& p = a.pool;
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H;
@@ -99,12 +110,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   // (KV head h, column slice s)
   int hv = 0, h = 0, L = 0;
   const int32_t* trow = a.tables;
-  v8 qf[NCT][4];
-  f32x4 o[NCT][kNT];
+  v8 qf[NT][4];
+  f32x4 o[NT][kNT];
   // Running statistics per lane and tile (= per packed column): m_ref is the
   // reference the weights are taken against, l_run the running sum of weights.
-  float m_ref[NCT], l_run[NCT];
-  int lim[NCT];  // CAUSAL: last position column 16t + c may see
+  float m_ref[NT], l_run[NT];
+  int lim[NT];  // CAUSAL: last position column 16(t0 + t) + c may see
 
   // K/V of one block into registers (8 x 16-byte loads, 1 KiB contiguous per
   // load across the wave).  The loads are issued unconditionally -- an
@@ -153,7 +164,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   // every path.
   auto consume = [&](int valid, int jl, const v8(&kf)[4], v8(&vf)[4]) {
 #pragma unroll
-    for (int t = 0; t < NCT; ++t) {
+    for (int t = 0; t < NT; ++t) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) sc = Mfma<T>::qk(kf[kk], qf[t][kk], sc);
@@ -210,7 +221,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
           v4 vt = {vf[u][4 * par + 0], vf[u][4 * par + 1], vf[u][4 * par + 2], vf[u][4 * par + 3]};
-          if constexpr (NCT == 1) {
+          if constexpr (NT == 1) {
             o[t][2 * u + par] = Mfma<T>::pv2(vt, phi, plo, o[t][2 * u + par]);
           } else {  // two tiles: the doubled operands would spill (measured 8 % slower)
             o[t][2 * u + par] = Mfma<T>::pv(vt, phi, o[t][2 * u + par]);
@@ -238,11 +249,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     h = hv / nsl;
     const int ncol = om.cols(hv);
 #pragma unroll
-    for (int t = 0; t < NCT; ++t) {
-      // Q^T fragment: lane (g, c) of tile t holds the segment's column
-      // col = 16t + c, i.e. Q[query gc / G][head h*G + gc % G][32kk + 8g .. +7]
+    for (int t = 0; t < NT; ++t) {
+      // Q^T fragment: lane (g, c) of tile t0 + t holds the segment's column
+      // col = 16(t0 + t) + c, i.e. Q[query gc / G][head h*G + gc % G][32kk + 8g .. +7]
       // for gc = s*32 + col in column slice s; zero past the last column
-      const int col = 16 * t + c, qi = om.gcol(hv, col) / G;
+      const int col = 16 * (t0 + t) + c, qi = om.gcol(hv, col) / G;
       const T* qp = static_cast<const T*>(a.q) + om.row(b, hv, min(col, ncol - 1)) * kD + 8 * g;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
@@ -254,15 +265,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       l_run[t] = 0.f;
     }
 
-    // Software pipeline over this wave's blocks jw+4k, k = 0..n-1: the loads
+    // Software pipeline over this wave's blocks jw + nst*k, k = 0..n-1: the loads
     // of blocks k+1 .. k+NB-1 are in flight while block k is consumed.  The
     // buffers rotate inside a fully unrolled trip of NB blocks (no copies, no
     // full waits); loads are unconditional, and past the last block they
     // re-read it (an L2 hit, never consumed).
-    const int jw = jbeg + w;
-    const int n = jw < jend ? (jend - jw + kWaves - 1) / kWaves : 0;
+    const int jw = jbeg + ws;
+    const int n = jw < jend ? (jend - jw + nst - 1) / nst : 0;
     auto id_of = [&](int k) -> Tid {
-      const int jt = jw + kWaves * min(k, n - 1);
+      const int jt = jw + nst * min(k, n - 1);
       if constexpr (BS == 16) {
         return table_entry(trow + jt);
       } else if constexpr (BS == 32) {
@@ -274,11 +285,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     };
     auto valid_of = [&](int k, Tid tid) {
       if constexpr (BS == 16) {
-        return ok(tid) ? L - 16 * (jw + kWaves * k) : 0;
+        return ok(tid) ? L - 16 * (jw + nst * k) : 0;
       } else if constexpr (BS == 32) {
-        return ok(tid >> 1) ? L - 16 * (jw + kWaves * k) : 0;
+        return ok(tid >> 1) ? L - 16 * (jw + nst * k) : 0;
       } else {
-        const int v = L - 16 * (jw + kWaves * k);
+        const int v = L - 16 * (jw + nst * k);
         if (!ok(tid.a)) return 0;
         if constexpr (BS == 8) return ok(tid.b) ? v : min(v, 8);
         return v;
@@ -296,7 +307,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       Tid nid = id_of(NB - 1);
       int k = 0;
       for (; k + NB <= n; k += NB) {
-        prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
+        prio_from_progress(a, pos - pos0 + nst * k, prio_span);
 #pragma unroll
         for (int s = 0; s < NB; ++s) {
           const int nxt = (s + NB - 1) % NB;
@@ -306,20 +317,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
           // no instruction of the block's product may move above the next
           // block's loads (it would wait for data still in flight)
           __builtin_amdgcn_sched_barrier(0);
-          consume(valid_of(k + s, ids[s]), jw + kWaves * (k + s), kb[s], vb[s]);
+          consume(valid_of(k + s, ids[s]), jw + nst * (k + s), kb[s], vb[s]);
         }
       }
 #pragma unroll
       for (int s = 0; s < NB - 1; ++s)
-        if (k + s < n) consume(valid_of(k + s, ids[s]), jw + kWaves * (k + s), kb[s], vb[s]);
+        if (k + s < n) consume(valid_of(k + s, ids[s]), jw + nst * (k + s), kb[s], vb[s]);
     }
 
     // ---- merge the 4 waves of this piece, write it -----------------------------
 #pragma unroll
-    for (int t = 0; t < NCT; ++t) {
+    for (int t = 0; t < NT; ++t) {
       l_run[t] += __shfl_xor(l_run[t], 16, 64);
       l_run[t] += __shfl_xor(l_run[t], 32, 64);
-      stash_piece(sh, w, g, 16 * t + c, o[t], m_ref[t], l_run[t]);
+      stash_piece(sh, w, g, 16 * (t0 + t) + c, o[t], m_ref[t], l_run[t]);
+    }
+    if constexpr (SPLIT) {  // the other tile's columns: nothing from this wave
+      if (g == 0) {
+        sh.m[w][16 * (1 - t0) + c] = -__builtin_inff();
+        sh.l[w][16 * (1 - t0) + c] = 0.f;
+      }
     }
     finish_piece<T>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, hv, fb + hv * nb,
                     nb, um);
@@ -327,6 +344,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     first = false;
   }
   }
+}
+
+// Two-tile verify steps split the tiles over the waves (PA_VERIFY_SPLIT=0:
+// every wave computes both).  Read at every launch.
+bool verify_split() {
+  const char* e = std::getenv("PA_VERIFY_SPLIT");
+  return !(e && std::atoi(e) == 0);
 }
 
 // Prefetch depth (PA_MFMA_NB = 2, 3 or 4; default 2).  Read at every launch,
@@ -344,6 +368,8 @@ hipError_t launch_bs(const DecodeArgs& a, hipStream_t s) {
     const int ncol = a.n_query * (a.n_q_heads / a.pool.n_kv_heads);  // > 32: slices of 32
     if (ncol <= 16)
       hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, true, BS>), grid, block, 0, s, a);
+    else if (verify_split())
+      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 2, true, BS, true>), grid, block, 0, s, a);
     else
       hipLaunchKernelGGL((decode_split_mfma16<T, 2, 2, true, BS>), grid, block, 0, s, a);
     return hipGetLastError();
@@ -373,7 +399,9 @@ template <typename T>
 int occupancy_nb(int nct) {
   int n = 0;
   hipError_t e;
-  if (nct == 2)
+  if (nct == 2 && verify_split())
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 2, true, 16, true>, kWaves * 64, 0);
+  else if (nct == 2)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 2, true, 16>, kWaves * 64, 0);
   else if (nct == 1)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_mfma16<T, 2, 1, true, 16>, kWaves * 64, 0);
@@ -394,9 +422,9 @@ hipError_t launch_decode_split_mfma16(const DecodeArgs& a, hipStream_t s) {
 
 // nct: 0 = decode, 1 or 2 = verify step with that many column tiles.
 int occupancy_mfma16(int32_t kv_dtype, int nct) {
-  static int cache[2][3][5] = {};  // [dtype][column tiles][prefetch depth]
+  static int cache[2][3][5] = {};  // [dtype][column tiles][prefetch depth, or tile split]
   const int i = kv_dtype == kBF16 ? 0 : 1;
-  int& c = cache[i][nct][nct == 0 ? mfma_nb() : 2];
+  int& c = cache[i][nct][nct == 0 ? mfma_nb() : verify_split() ? 1 : 0];
   if (c == 0) c = i == 0 ? occupancy_nb<__bf16>(nct) : occupancy_nb<_Float16>(nct);
   return c;
 }
