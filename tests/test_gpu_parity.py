@@ -375,10 +375,11 @@ VERIFY_LENS = [1, 5, 6, 7, 16, 17, 100, 1000, 2500]
 
 
 @pytest.mark.parametrize("hq,hkv,nq,dt", [(32, 8, 6, "bf16"), (16, 8, 6, "bf16"), (32, 8, 4, "f16"),
-                                          (64, 8, 4, "bf16"), (8, 8, 6, "bf16")])
+                                          (64, 8, 4, "bf16"), (8, 8, 6, "bf16"), (32, 8, 6, "f16")])
 def test_verify_matrix_core_matches_oracle(hq, hkv, nq, dt):
     """Matrix-core verify (one or two 16-column tiles of (query, head)
-    columns), lengths around the block edges and below n_query."""
+    columns; two tiles split over wave pairs), lengths around the block edges
+    and below n_query."""
     from _ref import expected_verify
     wl = W.from_lengths(VERIFY_LENS, hq, hkv, 128, dt, seed=91 + nq + hq)
     _, out = run_verify(wl, nq)
@@ -401,7 +402,7 @@ def test_verify_generic_matches_oracle(kvdt):
 
 @pytest.mark.parametrize("qenv", [{"PA_SPLIT_BLOCKS": "1"}, {"PA_SPLIT_BLOCKS": "3"},
                                   {"PA_FUSE_MAX_PIECES": "1"}, QUEUE_ENVS[0], QUEUE_ENVS[4],
-                                  {"PA_DECODE_KERNEL": "generic"}])
+                                  {"PA_VERIFY_SPLIT": "0"}, {"PA_DECODE_KERNEL": "generic"}])
 def test_verify_split_and_merge_modes(qenv):
     from _ref import expected_verify
     wl = W.from_lengths(VERIFY_LENS, 32, 8, 128, "bf16", seed=97)
@@ -555,8 +556,9 @@ def expected_prefill_chunk(wl, k, n, seqs):
     return np.stack(out)
 
 
-@pytest.mark.parametrize("hq,hkv,chunk", [(32, 8, 256), (64, 8, 128), (8, 8, 512), (12, 4, 200)])
-def test_prefill_chunks_match_oracle(hq, hkv, chunk):
+@pytest.mark.parametrize("hq,hkv,chunk,dt", [(32, 8, 256, "bf16"), (64, 8, 128, "bf16"), (8, 8, 512, "bf16"),
+                                             (12, 4, 200, "bf16"), (32, 8, 96, "f16")])
+def test_prefill_chunks_match_oracle(hq, hkv, chunk, dt):
     """A batch of prompts prefilled chunk by chunk (blocks interleaved across
     sequences by the chunk rounds): every chunk's attention -- (query, head)
     columns in groups of 128 per workgroup, the last group short, causal
@@ -564,15 +566,15 @@ def test_prefill_chunks_match_oracle(hq, hkv, chunk):
     runs as its own call.  (12, 4): a (sequence, KV head) count that is not a
     multiple of the 8 XCDs."""
     lengths = [3 * chunk, 2 * chunk + 37, chunk]
-    wl = W.chunked_prefill(seed=151, lengths=lengths, chunk=chunk, n_q_heads=hq, n_kv_heads=hkv)
+    wl = W.chunked_prefill(seed=151, lengths=lengths, chunk=chunk, n_q_heads=hq, n_kv_heads=hkv, dt=dt)
     kv = PagedKV(wl, DEV)
     kv.replay()
     for k in range(3):
         seqs = [b for b, L in enumerate(lengths) if L >= (k + 1) * chunk]
         out = prefill_chunk_gpu(kv, wl, k, chunk, seqs)
-        assert_close(out, expected_prefill_chunk(wl, k, chunk, seqs), "bf16", f"chunk {k} hq {hq}")
+        assert_close(out, expected_prefill_chunk(wl, k, chunk, seqs), dt, f"chunk {k} hq {hq}")
     out = prefill_chunk_gpu(kv, wl, 2, 37, [1])
-    assert_close(out, expected_prefill_chunk(wl, 2, 37, [1]), "bf16", "ragged last chunk")
+    assert_close(out, expected_prefill_chunk(wl, 2, 37, [1]), dt, "ragged last chunk")
 
 
 @pytest.mark.parametrize("env", [{}, {"PA_PREFILL_TILE": "0"},
