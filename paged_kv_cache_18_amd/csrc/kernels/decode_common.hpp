@@ -409,6 +409,17 @@ __device__ inline bool arrive(const DecodeArgs& a, int c0, int np) {
   return last;
 }
 
+// The merge launch's job for segment (b, hs), which starts at position S of
+// the list and has nb blocks: its first unit (bit 31: its first piece is in
+// that unit's second slot) and its piece count.  Written, every call, by the
+// workgroup of the segment's first piece; read after the split launch ends.
+__device__ inline void write_job(const DecodeArgs& a, const Units& um, int b, int hs, int S, int nb) {
+  const int c0 = um.unit_of(S), np = um.unit_of(S + nb - 1) - c0 + 1;
+  int32_t* j = a.jobs + 2 * (size_t(b) * seg_heads(a) + hs);
+  j[0] = int32_t(unsigned(c0) | (S != um.start(c0) ? 0x80000000u : 0u));
+  j[1] = np;
+}
+
 // Buffer resource word 3 for plain dword-addressed buffers on gfx950, and the
 // cache-policy bit of a buffer load that reads at agent scope (sc1).
 constexpr int kRsrcWord3 = 0x00020000;
@@ -439,16 +450,17 @@ struct Lse {
   }
 };
 
+// c0: the segment's first unit; split_first: its first piece sits in that
+// unit's second slot; rows: the partial rows the workspace holds (bounds of
+// the buffer loads).
 template <typename TO, class SH>
 __device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& om, int b, int h,
-                                     int S, int np, const Units& um, int col0, int ncol) {
+                                     int c0, bool split_first, int np, unsigned rows, int col0,
+                                     int ncol) {
   const int NC = om.ncol();
-  const int c0 = um.unit_of(S);
-  const bool split_first = S != um.start(c0);
   auto row_of = [&](int i) -> unsigned {  // workspace row of column 0 of piece i
     return unsigned((c0 + i) * 2 + ((i == 0 && split_first) ? 1 : 0)) * unsigned(NC);
   };
-  const unsigned rows = unsigned(um.total()) * 2u * unsigned(NC);
   const __amdgpu_buffer_rsrc_t ro =
       __builtin_amdgcn_make_buffer_rsrc(a.ws_o, (short)0, int(rows * kD * 4), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rml =
@@ -584,7 +596,9 @@ __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& o
     __syncthreads();
     if (threadIdx.x == 0) sh.last = arrive(a, c0, np) ? 1 : 0;
     __syncthreads();
-    if (sh.last) merge_segment<TO>(a, sh, om, b, h, S, np, um, 0, NC);
+    if (sh.last)
+      merge_segment<TO>(a, sh, om, b, h, c0, S != um.start(c0), np,
+                        unsigned(um.total()) * 2u * unsigned(NC), 0, NC);
   }
   __syncthreads();
 }

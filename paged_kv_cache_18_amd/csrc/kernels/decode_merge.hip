@@ -4,11 +4,11 @@
 // merge per segment would leave a long serial tail at the end of the split).
 //
 // One workgroup per (sequence b, KV head h, output column c: query head of the
-// group, times the query of a verify step): it rebuilds the work-list cut from
-// the lengths exactly as the split kernel did, finds the segment's pieces and
-// folds the 32 16-byte columns of column c over them (decode_common.hpp,
-// merge_segment), in list order.  A segment of
-// one piece was written by the split kernel and is skipped.
+// group, times the query of a verify step): it reads the segment's job (first
+// unit, first slot, piece count) that the split kernel wrote and folds the 32
+// 16-byte columns of column c over the pieces (decode_common.hpp,
+// merge_segment), in list order.  A segment of one piece was written by the
+// split kernel and is skipped, as is an empty sequence (no job was written).
 #include "decode_common.hpp"
 
 namespace pa {
@@ -25,15 +25,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_merge_kernel(DecodeArgs a)
   const int hc = int(blockIdx.x) % om.ncol(), bh = int(blockIdx.x) / om.ncol();
   const int b = bh / H, h = bh % H;
   if (hc >= om.cols(h)) return;  // past the last column of a short slice
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Units um = setup_units(a, sh, w, lane);
-  const int nb = blocks_of(a, sh, b);
-  if (nb == 0) return;  // workgroup-uniform
-  const int S = seq_start(a, sh, b, lane) + h * nb;  // every wave computes it
-  const int np = um.unit_of(S + nb - 1) - um.unit_of(S) + 1;
-  if (np <= 1) return;
-  merge_segment<TO>(a, sh, om, b, h, S, np, um, hc, 1);
+  const int32_t* job = a.jobs + 2 * (size_t(b) * H + h);
+  const int j0 = job[0], np = job[1];
+  if (seq_len(a, b) == 0 || np <= 1) return;  // workgroup-uniform
+  const unsigned rows = unsigned((a.ws_ml - a.ws_o) / kD);  // partial rows of the workspace
+  merge_segment<TO>(a, sh, om, b, h, j0 & 0x7FFFFFFF, j0 < 0, np, rows, hc, 1);
 }
 
 }  // namespace

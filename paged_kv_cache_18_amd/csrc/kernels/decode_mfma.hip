@@ -338,6 +338,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(
         sh.l[w][16 * (1 - t0) + c] = 0.f;
       }
     }
+    if (a.defer_merge && jbeg == 0 && threadIdx.x == 0) write_job(a, um, b, hv, fb + hv * nb, nb);
     finish_piece<T>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, hv, fb + hv * nb,
                     nb, um);
     pos += jend - jbeg;

@@ -521,6 +521,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       for (int T_ = 0; T_ < kNT; ++T_) o[T_] -= corr;
     }
     if (keep >= 0) stash_piece(sh, w, g, keep, o, m_ref, l_run);
+    if (a.defer_merge && jbeg == 0 && threadIdx.x == 0) write_job(a, um, b, h, fb + h * nb, nb);
     finish_piece<_Float16>(a, sh, out_map(a), jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, h,
                       fb + h * nb, nb, um);
     pos += jend - jbeg;

@@ -56,6 +56,9 @@ struct DecodeArgs {
   // apart; zero between calls
   unsigned* counters;
   int ctr_stride;
+  // matrix-core kernels with the merge launch: per segment (first unit, with
+  // bit 31 set when its first piece is in the unit's second slot; pieces)
+  int32_t* jobs;
   int32_t split_blocks;  // logical blocks per split
   int32_t max_splits;
   int32_t kernel;        // DecodeKernel

@@ -135,6 +135,7 @@ struct Plan {
   size_t ws_bytes;      // bytes the call needs
   size_t ws_o_offset;   // byte offset of the partial sums
   size_t ws_ml_offset;  // float index (from ws_o) of the (max, sum) pairs
+  size_t ws_jobs_offset;  // byte offset of the merge launch's per-segment jobs (0: none)
 };
 
 // The workspace starts with kCtrCap counters of the matrix-core kernels (the
@@ -244,7 +245,8 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
     const size_t rows = size_t(units) * 2 * size_t(pl.col_slices > 1 ? seg_cols : ncol);
     pl.ws_o_offset = kCtrBytes;
     pl.ws_ml_offset = rows * size_t(d.head_dim);
-    pl.ws_bytes = kCtrBytes + rows * (size_t(d.head_dim) + 2) * sizeof(float);
+    pl.ws_jobs_offset = kCtrBytes + rows * (size_t(d.head_dim) + 2) * sizeof(float);
+    pl.ws_bytes = pl.ws_jobs_offset + size_t(segs) * 2 * sizeof(int32_t);
     return pl;
   }
   pl.split_blocks = plan_split_blocks(batch, d.n_kv_heads, max_seq_len);
@@ -332,6 +334,8 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
       a.ws_ml = a.ws_o + pl.ws_ml_offset;
       a.counters = static_cast<unsigned*>(ws);
       a.ctr_stride = kCtrStride;
+      if (pl.ws_jobs_offset)
+        a.jobs = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + pl.ws_jobs_offset);
     }
     a.prio = env_int("PA_PRIO", 1) != 0 ? 1 : 0;  // tuning knob
     a.unit_blocks = pl.unit_blocks;
