@@ -112,13 +112,16 @@ __device__ inline int seg_heads(const DecodeArgs& a) { return a.pool.n_kv_heads 
 // from memory where needed).
 constexpr int kLenCap = 512;
 
-template <int CAP>
+// CAP output columns; NV stash slots (one per wave, or per wave of a pair
+// when the waves split the column tiles).
+template <int CAP, int NV = kWaves>
 struct SharedT {
+  static constexpr int kSlots = NV;
   int len[kLenCap];
   int pre[kLenCap];  // list positions of sequences 0..b (blocks times segments per sequence)
-  float m[kWaves][CAP];
-  float l[kWaves][CAP];
-  alignas(16) float o[kWaves][CAP][kD + 1];
+  float m[NV][CAP];
+  float l[NV][CAP];
+  alignas(16) float o[NV][CAP][kD + 1];
   int b, fb;
   int units[6];
   int next;
@@ -468,7 +471,7 @@ __device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& 
   constexpr int kCols = kD / 4;           // float4 columns of one output column
   float* red = &sh.o[0][0][0];            // [256][6]: m, l, o of each thread
   float2* mls = reinterpret_cast<float2*>(red + 256 * 6);  // [span][nh] (max, sum) of a batch
-  static_assert(256 * 6 + 2 * 256 <= kWaves * 16 * (kD + 1), "LDS reuse");
+  static_assert(256 * 6 + 2 * 256 <= sizeof(sh.o) / sizeof(float), "LDS reuse");
   TO* out = static_cast<TO*>(a.out);
   const int tid = threadIdx.x;
   // float4 columns [col0, col0 + 32*ncol) in trips of at most 256
@@ -569,10 +572,10 @@ __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& o
     const int hc = idx / kD, d = idx % kD;
     float M = -__builtin_inff();
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sh.m[v][hc]);
+    for (int v = 0; v < SH::kSlots; ++v) M = fmaxf(M, sh.m[v][hc]);
     float lsum = 0.f, osum = 0.f;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
+    for (int v = 0; v < SH::kSlots; ++v) {
       if (sh.m[v][hc] == -__builtin_inff()) continue;  // wave saw no block (or no visible token)
       const float wt = exp2f(sh.m[v][hc] - M);
       lsum += sh.l[v][hc] * wt;

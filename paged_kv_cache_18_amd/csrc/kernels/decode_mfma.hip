@@ -76,16 +76,17 @@ struct TileId {
 //
 // SPLIT (two column tiles only): waves 0, 1 compute tile 0 and waves 2, 3
 // tile 1, each pair taking the piece's blocks alternately, so a wave carries
-// one tile's registers (three waves per SIMD instead of two) and every block
-// is read by two waves of the workgroup (the second from L2).
+// one tile's registers and every block is read by two waves of the workgroup
+// (the second from L2).  A pair stashes into two slots (wave w into slot
+// w & 1, its tile's columns), which halves the LDS of the merge.
 template <typename T, int NB, int NCT, bool CAUSAL, int BS, bool SPLIT = false>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(
-    NB == 2 && (!CAUSAL || SPLIT) ? 3 : 2))) void decode_split_mfma16(DecodeArgs a) {
+    NB == 2 && !CAUSAL ? 3 : 2))) void decode_split_mfma16(DecodeArgs a) {
   typedef typename Mfma<T>::v8 v8;
   typedef typename Mfma<T>::v4 v4;
   static_assert(!SPLIT || NCT == 2, "tile split needs two tiles");
   constexpr int NT = SPLIT ? 1 : NCT;  // tiles a wave computes
-  __shared__ SharedT<16 * NCT> sh;
+  __shared__ SharedT<16 * NCT, SPLIT ? 2 : kWaves> sh;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -330,13 +331,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(
     for (int t = 0; t < NT; ++t) {
       l_run[t] += __shfl_xor(l_run[t], 16, 64);
       l_run[t] += __shfl_xor(l_run[t], 32, 64);
-      stash_piece(sh, w, g, 16 * (t0 + t) + c, o[t], m_ref[t], l_run[t]);
-    }
-    if constexpr (SPLIT) {  // the other tile's columns: nothing from this wave
-      if (g == 0) {
-        sh.m[w][16 * (1 - t0) + c] = -__builtin_inff();
-        sh.l[w][16 * (1 - t0) + c] = 0.f;
-      }
+      stash_piece(sh, ws, g, 16 * (t0 + t) + c, o[t], m_ref[t], l_run[t]);
     }
     if (a.defer_merge && jbeg == 0 && threadIdx.x == 0) write_job(a, um, b, hv, fb + hv * nb, nb);
     finish_piece<T>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, hv, fb + hv * nb,

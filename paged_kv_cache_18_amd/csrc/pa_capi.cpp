@@ -157,9 +157,10 @@ constexpr int32_t kUnitBlocks = 16;
 // Average pieces per segment above which split segments are merged by a
 // second launch instead of inside the split kernel.
 constexpr int32_t kFuseMaxPieces = 16;
-// Decode workgroups per compute unit at most: two larger regions per CU
-// measured as fast or faster than the three that fit (fewer piece ends; the
-// long-context batch 2 % and the shared-prefix batch 17 % faster).
+// Split-kernel workgroups per compute unit at most: two larger regions per
+// CU measured as fast or faster than the three that fit (fewer piece ends;
+// the long-context batch 2 %, the shared-prefix batch 17 % and the split-tile
+// verify step 6 % faster).
 constexpr int kDecodePerCu = 2;
 
 // Upper bound of the flattened work list (blocks of all (sequence, kv head)
@@ -216,7 +217,7 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
       if (per_cu <= 0) {
         per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype,
                                             n_query == 1 ? 0 : seg_cols <= 16 ? 1 : 2, d.group_size);
-        if (n_query == 1) per_cu = std::min(per_cu, kDecodePerCu);
+        per_cu = std::min(per_cu, kDecodePerCu);
       }
       pl.max_splits = int32_t(std::max<int64_t>(
           1, std::min<int64_t>({w, int64_t(cu_count()) * per_cu, int64_t(kCtrCap / 2)})));
