@@ -301,6 +301,20 @@ def test_queued_units_match_oracle_and_are_deterministic(kvdt, qenv):
     assert_close(out_a, expected(wl), "bf16" if kvdt == "bf16" else "f16", f"{kvdt} {env}")
 
 
+@pytest.mark.parametrize("kvdt,env", [("bf16", {"PA_MFMA_NB": "3"}), ("bf16", {"PA_MFMA_NB": "4"}),
+                                      ("bf16", {"PA_PRIO": "0"}), ("int4", {"PA_QUANT_NB": "2"}),
+                                      ("int4", {"PA_QUANT_NB": "6"}), ("fp8", {"PA_QUANT_NB": "4"})])
+def test_prefetch_depths_and_priority(kvdt, env):
+    """The split kernels at every register-buffer depth (other occupancies,
+    so other cuts of the work list) and without the progress-based wave
+    priority: the output matches the oracle."""
+    wl = W.from_lengths([2100, 1, 17, 700, 3000, 16], 32, 8, 128, kvdt, seed=83,
+                        group=128 if kvdt == "int4" else 0, sink=kvdt != "bf16",
+                        outliers=kvdt != "bf16")
+    _, out, _, _ = run(wl, env=env)
+    assert_close(out, expected(wl), "bf16" if kvdt == "bf16" else "f16", f"{kvdt} {env}")
+
+
 def test_workspace_reuse_across_calls_and_shapes():
     """One zero-filled workspace serves repeated calls and changing shapes: the
     arrival counters reset themselves, results stay bit-identical and correct."""
