@@ -607,6 +607,17 @@ def test_prefill_chunk_split_merge_and_generic(env):
     assert_close(out, expected_prefill_chunk(wl, 1, 300, [0, 1]), "bf16", f"prefill {env}")
 
 
+@pytest.mark.parametrize("n", [1, 2, 17])
+def test_prefill_short_chunks(n):
+    """Chunks of 1, 2 and 17 queries on the tile kernel (one column group, the
+    group's last column sees the whole cache) match the oracle."""
+    wl = W.chunked_prefill(seed=153, lengths=[300, 300, 300], chunk=100)
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    out = prefill_chunk_gpu(kv, wl, 2, n, [0, 1, 2])
+    assert_close(out, expected_prefill_chunk(wl, 2, n, [0, 1, 2]), "bf16", f"prefill n={n}")
+
+
 def test_prefill_full_workload_last_chunk_sampled():
     """The bench's prefill workload (4 x 4,096 tokens, 512-token chunks): the
     last chunk's attention, 16 groups of 128 columns per KV head, checked on
