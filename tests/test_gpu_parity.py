@@ -315,6 +315,19 @@ def test_prefetch_depths_and_priority(kvdt, env):
     assert_close(out, expected(wl), "bf16" if kvdt == "bf16" else "f16", f"{kvdt} {env}")
 
 
+@pytest.mark.parametrize("kvdt,env", [("bf16", {}), ("bf16", {"PA_FUSE_MAX_PIECES": "1"}),
+                                      ("int4", {})])
+def test_more_sequences_than_the_lds_length_cache(kvdt, env):
+    """700 sequences, more than the 512 whose lengths the split kernels keep in
+    LDS: the rest are located and walked from memory; some are empty."""
+    r = np.random.default_rng(84)
+    lens = [int(x) for x in r.integers(0, 90, size=700)]
+    wl = W.from_lengths(lens, 32, 8, 128, kvdt, seed=84, group=128 if kvdt == "int4" else 0,
+                        sink=kvdt != "bf16")
+    _, out, _, _ = run(wl, env=env)
+    assert_close(out, expected(wl), "bf16" if kvdt == "bf16" else "f16", f"700 seqs {kvdt} {env}")
+
+
 def test_workspace_reuse_across_calls_and_shapes():
     """One zero-filled workspace serves repeated calls and changing shapes: the
     arrival counters reset themselves, results stay bit-identical and correct."""
