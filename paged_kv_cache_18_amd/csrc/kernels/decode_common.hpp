@@ -123,7 +123,7 @@ struct SharedT {
   float l[NV][CAP];
   alignas(16) float o[NV][CAP][kD + 1];
   int b, fb;
-  int units[6];
+  int units[8];
   int next;
   int last;
 };
@@ -175,6 +175,15 @@ __device__ inline OutMap out_map(const DecodeArgs& a) {
 
 // The cut of the work list (see the top of this file).  Unit ids grow with
 // position: region r holds units r*(1+m) (its prefix) .. r*(1+m)+m.
+//
+// Segments of one length n (every sequence equally long) that span four or
+// more regions each are cut one by one when the whole-list cut does not
+// already fall on their ends and this costs no more than ~3 % of balance: q
+// regions of C blocks per segment, so that no region holds the end of one
+// segment and the start of the next.  With long segments only the few regions
+// at segment ends held two pieces (a second pipeline start, a second partial
+// write) and they finished last.  No queue then (m = 0, one unit per
+// region).
 struct Units {
   int W;   // blocks in the list
   int R;   // regions (= the grid)
@@ -182,17 +191,31 @@ struct Units {
   int Cs;  // owner's prefix of a region, >= 1
   int U;   // blocks per queued unit
   int m;   // queued units per region
+  int n;   // segment length of the per-segment cut, 0 = one cut of the whole list
+  int q;   // regions per segment (per-segment cut)
   __device__ int per() const { return 1 + m; }
   __device__ int total() const { return R * per(); }
   __device__ int unit_of(int p) const {
+    if (n > 0) {
+      const int s = p / n;
+      return s * q + (p - s * n) / C;
+    }
     const int r = p / C, o = p - r * C;
     return r * per() + (o < Cs ? 0 : 1 + (o - Cs) / U);
   }
   __device__ int start(int u) const {
+    if (n > 0) {
+      const int s = u / q;
+      return min(W, s * n + min((u - s * q) * C, n));
+    }
     const int r = u / per(), k = u - r * per();
     return r * C + (k == 0 ? 0 : Cs + (k - 1) * U);
   }
   __device__ int end(int u) const {
+    if (n > 0) {
+      const int s = u / q;
+      return min(W, s * n + min((u - s * q + 1) * C, n));
+    }
     const int r = u / per(), k = u - r * per();
     return min(W, r * C + (k == 0 ? Cs : min(C, Cs + k * U)));
   }
@@ -206,10 +229,14 @@ struct Units {
 template <class SH>
 __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane) {
   if (w == 0) {
-    int W = 0;
+    int W = 0, nmin = 0x7fffffff, nmax = 0;
     for (int base = 0; base < a.batch; base += 64) {
       const int bb = base + lane;
       const int L = bb < a.batch ? seq_len(a, bb) : 0;
+      if (bb < a.batch) {
+        nmin = min(nmin, (L + 15) >> 4);
+        nmax = max(nmax, (L + 15) >> 4);
+      }
       const int sz = ((L + 15) >> 4) * seg_heads(a);
       int incl = sz;
 #pragma unroll
@@ -223,17 +250,30 @@ __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane
       }
       W += __shfl(incl, 63, 64);
     }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      nmin = min(nmin, __shfl_xor(nmin, o, 64));
+      nmax = max(nmax, __shfl_xor(nmax, o, 64));
+    }
     const int R = a.max_splits;  // the split kernel's grid
-    int C, Cs, U = 1, m = 0;
+    int C, Cs, U = 1, m = 0, n = 0, q = 0;
     if (a.split_blocks > 0) {
       C = Cs = a.split_blocks;
     } else {
       C = max(1, (W + R - 1) / R);
       Cs = C;
+      const int S = a.batch * seg_heads(a);
       if (a.unit_blocks > 0 && a.static_permille < 1000) {
         U = a.unit_blocks;
         Cs = max(1, int(int64_t(C) * max(a.static_permille, 0) / 1000));
         m = (C - Cs + U - 1) / U;
+      } else if (nmin == nmax && nmin > 0 && R >= 4 * S && nmin % C != 0) {
+        const int qs = R / S, Cq = (nmin + qs - 1) / qs;
+        if (32 * Cq <= 33 * C) {
+          n = nmin;
+          q = qs;
+          C = Cs = Cq;
+        }
       }
     }
     if (lane == 0) {
@@ -243,10 +283,12 @@ __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane
       sh.units[3] = Cs;
       sh.units[4] = U;
       sh.units[5] = m;
+      sh.units[6] = n;
+      sh.units[7] = q;
     }
   }
   __syncthreads();
-  return Units{sh.units[0], sh.units[1], sh.units[2], sh.units[3], sh.units[4], sh.units[5]};
+  return Units{sh.units[0], sh.units[1], sh.units[2], sh.units[3], sh.units[4], sh.units[5], sh.units[6], sh.units[7]};
 }
 
 // The sequence b holding position p0 and the position fb of its first block.
