@@ -20,7 +20,7 @@ What the pages fix, and where:
   (8GB page, section 3, "Copy-on-Write (CoW) Prefix Sharing"; 3-minute page,
   "Compartilhamento e compromissos").
 
-Readings where the pages are silent (each one also listed in the design doc):
+Readings where the pages are silent:
 
 * The initial free order is a permutation passed in; the first pop returns its
   first element (a stack that was pushed in reverse).

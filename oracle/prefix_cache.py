@@ -10,7 +10,7 @@ is mapped into the new request's block table and its prefill skipped; a
 missing piece is prefilled and the resulting block registered.  Requests that
 share a prefix thus point at the same physical blocks.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * Key of full block j: FNV-1a 64 over (key of block j-1 as 8 little-endian
   bytes, then the block's 16 token ids as int32 little-endian), the key of

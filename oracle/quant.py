@@ -13,7 +13,7 @@ Group-Wise Asymmetric INT4 / FP8"):
 * The kernel pattern of section 7 unpacks two codes per byte: the low nibble
   first (``packed & 0x0F``), then the high nibble (``packed >> 4``).
 
-Readings where the pages are silent (also listed in the design doc):
+Readings where the pages are silent:
 
 * INT4 quantize rule, per group of g values held as fp32 (fp16 inputs are
   exact in fp32), every step one IEEE fp32 operation rounded to nearest even:
