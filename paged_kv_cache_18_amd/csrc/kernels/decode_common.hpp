@@ -3,8 +3,13 @@
 // list and its units, the per-piece iteration, and the 4-wave merge.
 //
 // Work list: the blocks of every (sequence b, KV head h) segment laid end to
-// end (b major, then h, then logical block j).  It is cut into regions of C
-// blocks, one per workgroup of the persistent grid.  The first Cs blocks of a
+// end, h major, then b, then logical block j, so every KV head (segment index
+// hv, with column slices) has a list of the same TB blocks.  Normally each
+// head's list is cut into q = grid / heads regions of C blocks (a region never
+// holds two heads); otherwise (grid not a multiple of the heads, or a queue or
+// fixed region size asked for) the whole list is cut into regions of C
+// blocks.  One region per workgroup of the persistent grid; which workgroup
+// owns which region is the kernel's choice (see Units).  The first Cs blocks of a
 // region are its owner's; the rest are cut into units of U blocks that any
 // workgroup takes, in order, from a queue once it has streamed its own prefix
 // (compute units and XCDs do not stream at the same rate, so equal shares
@@ -118,12 +123,12 @@ template <int CAP, int NV = kWaves>
 struct SharedT {
   static constexpr int kSlots = NV;
   int len[kLenCap];
-  int pre[kLenCap];  // list positions of sequences 0..b (blocks times segments per sequence)
+  int pre[kLenCap];  // blocks of sequences 0..b: the place after b in every head's list
   float m[NV][CAP];
   float l[NV][CAP];
   alignas(16) float o[NV][CAP][kD + 1];
   int b, fb;
-  int units[8];
+  int units[10];
   int next;
   int last;
 };
@@ -174,16 +179,18 @@ __device__ inline OutMap out_map(const DecodeArgs& a) {
 }
 
 // The cut of the work list (see the top of this file).  Unit ids grow with
-// position: region r holds units r*(1+m) (its prefix) .. r*(1+m)+m.
+// position: region r holds units r*(1+m) (its prefix) .. r*(1+m)+m; with the
+// per-head cut (n = TB > 0, no queue: m = 0) unit h*q + k is region k of
+// head h's list.
 //
-// Segments of one length n (every sequence equally long) that span four or
-// more regions each are cut one by one when the whole-list cut does not
-// already fall on their ends and this costs no more than ~3 % of balance: q
-// regions of C blocks per segment, so that no region holds the end of one
-// segment and the start of the next.  With long segments only the few regions
-// at segment ends held two pieces (a second pipeline start, a second partial
-// write) and they finished last.  No queue then (m = 0, one unit per
-// region).
+// Owners.  Workgroups go to the 8 XCDs round robin.  owned_by_head gives
+// region k of head h to workgroup k*heads + h, so with 8 heads each XCD
+// streams one head's slabs of every block (the 16-bit kernel: 2 % shorter on
+// the ragged Llama-3-8B-shaped batch than with unit = workgroup).  The
+// identity (owned) gives the regions over the same blocks of different heads
+// to workgroups h*q + k, on one XCD when q is a multiple of 8, where the
+// quantized kernel's scale and zero rows of several heads, which share cache
+// lines, are fetched once.
 struct Units {
   int W;   // blocks in the list
   int R;   // regions (= the grid)
@@ -191,9 +198,13 @@ struct Units {
   int Cs;  // owner's prefix of a region, >= 1
   int U;   // blocks per queued unit
   int m;   // queued units per region
-  int n;   // segment length of the per-segment cut, 0 = one cut of the whole list
-  int q;   // regions per segment (per-segment cut)
+  int n;   // list length of the per-head cut (= TB), 0 = one cut of the whole list
+  int TB;  // blocks of one head's list: W = TB * heads
+  int hs;  // heads (segment indices) of the per-head cut, else 0
+  int q;   // regions per head (per-head cut)
   __device__ int per() const { return 1 + m; }
+  __device__ int owned(int bid) const { return bid * per(); }
+  __device__ int owned_by_head(int bid) const { return hs > 0 ? (bid % hs) * q + bid / hs : bid * per(); }
   __device__ int total() const { return R * per(); }
   __device__ int unit_of(int p) const {
     if (n > 0) {
@@ -229,15 +240,11 @@ struct Units {
 template <class SH>
 __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane) {
   if (w == 0) {
-    int W = 0, nmin = 0x7fffffff, nmax = 0;
+    int W = 0;
     for (int base = 0; base < a.batch; base += 64) {
       const int bb = base + lane;
       const int L = bb < a.batch ? seq_len(a, bb) : 0;
-      if (bb < a.batch) {
-        nmin = min(nmin, (L + 15) >> 4);
-        nmax = max(nmax, (L + 15) >> 4);
-      }
-      const int sz = ((L + 15) >> 4) * seg_heads(a);
+      const int sz = (L + 15) >> 4;
       int incl = sz;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -250,30 +257,24 @@ __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane
       }
       W += __shfl(incl, 63, 64);
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      nmin = min(nmin, __shfl_xor(nmin, o, 64));
-      nmax = max(nmax, __shfl_xor(nmax, o, 64));
-    }
+    const int TB = W;
+    W *= seg_heads(a);
     const int R = a.max_splits;  // the split kernel's grid
-    int C, Cs, U = 1, m = 0, n = 0, q = 0;
+    int C, Cs, U = 1, m = 0, n = 0, q = 0, hs = 0;
     if (a.split_blocks > 0) {
       C = Cs = a.split_blocks;
     } else {
       C = max(1, (W + R - 1) / R);
       Cs = C;
-      const int S = a.batch * seg_heads(a);
       if (a.unit_blocks > 0 && a.static_permille < 1000) {
         U = a.unit_blocks;
         Cs = max(1, int(int64_t(C) * max(a.static_permille, 0) / 1000));
         m = (C - Cs + U - 1) / U;
-      } else if (nmin == nmax && nmin > 0 && R >= 4 * S && nmin % C != 0) {
-        const int qs = R / S, Cq = (nmin + qs - 1) / qs;
-        if (32 * Cq <= 33 * C) {
-          n = nmin;
-          q = qs;
-          C = Cs = Cq;
-        }
+      } else if (R % seg_heads(a) == 0 && TB > 0) {
+        hs = seg_heads(a);
+        n = TB;
+        q = R / hs;
+        C = Cs = (TB + q - 1) / q;
       }
     }
     if (lane == 0) {
@@ -285,25 +286,28 @@ __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane
       sh.units[5] = m;
       sh.units[6] = n;
       sh.units[7] = q;
+      sh.units[8] = TB;
+      sh.units[9] = hs;
     }
   }
   __syncthreads();
-  return Units{sh.units[0], sh.units[1], sh.units[2], sh.units[3], sh.units[4], sh.units[5], sh.units[6], sh.units[7]};
+  return Units{sh.units[0], sh.units[1], sh.units[2], sh.units[3], sh.units[4], sh.units[5], sh.units[6], sh.units[8], sh.units[9], sh.units[7]};
 }
 
-// The sequence b holding position p0 and the position fb of its first block.
-// Every wave reads them from the running sums in LDS where the batch fits
+// The sequence b holding position p0 and the place fb of its first block in
+// its head's list (p0 = h * TB + fb + j).  Every wave reads them from the running sums in LDS where the batch fits
 // there; otherwise wave 0 scans the lengths and every thread gets them.
 template <class SH>
-__device__ inline void locate(const DecodeArgs& a, SH& sh, int w, int lane, int p0, int& b,
+__device__ inline void locate(const DecodeArgs& a, SH& sh, const Units& um, int w, int lane, int p0, int& b,
                               int& fb) {
-  const int H = seg_heads(a), B = a.batch;
+  const int B = a.batch;
+  const int r0 = p0 % um.TB;
   if (B <= kLenCap) {
     b = B;
     fb = 0;
     for (int base = 0; base < B; base += 64) {
       const int bb = base + lane;
-      const unsigned long long hit = __ballot(bb < B && sh.pre[bb] > p0);
+      const unsigned long long hit = __ballot(bb < B && sh.pre[bb] > r0);
       if (hit) {
         b = base + __builtin_ctzll(hit);
         fb = b > 0 ? __builtin_amdgcn_readfirstlane(sh.pre[b - 1]) : 0;
@@ -316,14 +320,14 @@ __device__ inline void locate(const DecodeArgs& a, SH& sh, int w, int lane, int 
     int run = 0, f = 0, fbi = B;
     for (int base = 0; base < B; base += 64) {
       const int bb = base + lane;
-      const int sz = bb < B ? blocks_of(a, sh, bb) * H : 0;
+      const int sz = bb < B ? blocks_of(a, sh, bb) : 0;
       int incl = sz;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int t = __shfl_up(incl, o, 64);
         if (lane >= o) incl += t;
       }
-      const unsigned long long hit = __ballot(run + incl > p0);
+      const unsigned long long hit = __ballot(run + incl > r0);
       if (hit) {
         const int fl = __builtin_ctzll(hit);
         fbi = base + fl;
@@ -390,20 +394,26 @@ __device__ inline void zero_empty_rows(const DecodeArgs& a, const SH& sh) {
 }
 
 // The next piece [jbeg, jend) of segment (b, h) starting at position pos;
-// advances (b, fb) past finished or empty sequences.  False when done.
+// advances (b, fb) past finished or empty sequences, back to the first
+// sequence where pos enters the next head's list.  False when done.
 template <class SH>
-__device__ inline bool next_piece(const DecodeArgs& a, const SH& sh, int pos, int pos1, int& b,
-                                  int& fb, int& h, int& jbeg, int& jend, int& nb) {
-  const int H = seg_heads(a);
-  while (pos < pos1 && b < a.batch) {
+__device__ inline bool next_piece(const DecodeArgs& a, const SH& sh, const Units& um, int pos, int pos1,
+                                  int& b, int& fb, int& h, int& jbeg, int& jend, int& nb) {
+  while (pos < pos1) {
+    const int hv = pos / um.TB, r = pos - hv * um.TB;
+    if (r < fb) {
+      b = 0;
+      fb = 0;
+    }
+    if (b >= a.batch) return false;
     nb = blocks_of(a, sh, b);
-    if (pos >= fb + nb * H) {
-      fb += nb * H;
+    if (r >= fb + nb) {
+      fb += nb;
       ++b;
       continue;
     }
-    h = (pos - fb) / nb;
-    jbeg = (pos - fb) % nb;
+    h = hv;
+    jbeg = r - fb;
     jend = min(nb, jbeg + (pos1 - pos));
     return true;
   }

@@ -373,18 +373,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     }
   };
 
-  const int own_unit = int(blockIdx.x) * um.per();
+  const int own_unit = um.owned(int(blockIdx.x));
   for (int unit = own_unit; unit >= 0; unit = next_unit(a, sh, um)) {
   const int pos0 = um.start(unit), pos1 = um.end(unit);
   if (pos0 >= pos1) continue;  // a region past the end of the work
-  locate(a, sh, w, lane, pos0, b, fb);
+  locate(a, sh, um, w, lane, pos0, b, fb);
   // progress-based priority in the owner's prefix; queued units run at the
   // base priority, behind the workgroups still streaming their own prefix
   const int prio_span = unit == own_unit ? pos1 - pos0 : 0;
   int pos = pos0;
   bool first = true;
   int jbeg = 0, jend = 0, nb = 0;
-  while (next_piece(a, sh, pos, pos1, b, fb, h, jbeg, jend, nb)) {
+  while (next_piece(a, sh, um, pos, pos1, b, fb, h, jbeg, jend, nb)) {
     L = len_of(a, sh, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
     const int lo = max(jbeg, SP);  // first non-sink block of the piece
@@ -523,9 +523,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       for (int T_ = 0; T_ < kNT; ++T_) o[T_] -= corr;
     }
     if (keep >= 0) stash_piece(sh, w, g, keep, o, m_ref, l_run);
-    if (a.defer_merge && jbeg == 0 && threadIdx.x == 0) write_job(a, um, b, h, fb + h * nb, nb);
+    if (a.defer_merge && jbeg == 0 && threadIdx.x == 0) write_job(a, um, b, h, h * um.TB + fb, nb);
     finish_piece<_Float16>(a, sh, out_map(a), jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, h,
-                      fb + h * nb, nb, um);
+                      h * um.TB + fb, nb, um);
     pos += jend - jbeg;
     first = false;
   }
