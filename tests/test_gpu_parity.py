@@ -146,7 +146,7 @@ def test_decode_16bit_edge_lengths(kernel, dt):
 
 
 @pytest.mark.parametrize("hq,hkv,D", [(8, 8, 128), (16, 1, 128), (64, 8, 128), (4, 2, 64),
-                                      (8, 2, 256), (6, 3, 32)])
+                                      (8, 2, 256), (6, 3, 32), (24, 6, 128)])
 def test_decode_head_shapes(hq, hkv, D):
     wl = W.from_lengths([40, 3, 129, 77], hq, hkv, D, "bf16", seed=hq * 7 + D)
     kv, out, t, l = run(wl)
