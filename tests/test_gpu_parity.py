@@ -187,6 +187,17 @@ def test_quantized_codes_and_decode(kvdt, group):
     log(f"[gpu] {kvdt} g{group} max err {err:.3g}")
 
 
+@pytest.mark.parametrize("kvdt,group", [("int4", 128), ("fp8", 0)])
+def test_quantized_six_kv_heads(kvdt, group):
+    """Six KV heads: the grid is not a multiple of the heads, so the quantized
+    kernel cuts the work list as a whole instead of per head."""
+    wl = W.from_lengths([300, 16, 9, 1000], 24, 6, 128, kvdt, seed=53, group=group,
+                        sink=True, outliers=True)
+    kv, out, t, l = run(wl)
+    check_stored(kv, wl, t, l)
+    assert_close(out, expected(wl), "f16", f"{kvdt} g{group} six kv heads")
+
+
 def test_mixed_precision_decode_steps():
     """Config-4 shape, shortened: prefill, then single-token appends each
     quantized on write; codes stay bit-exact and decode matches after each."""
