@@ -323,6 +323,38 @@ pa_status pa_decode_combine(const void* q, const pa_pool* pool, const int32_t* b
                             float scale, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* ---- allocation-free decode --------------------------------------------------- */
+
+/* Bytes of the library's static scratch array: shapes whose
+ * pa_decode_workspace_bytes exceeds this are refused by
+ * pa_decode_attention_noalloc. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the decode
+ * of pa_decode_attention (same arguments and results, same kernels) with no
+ * workspace argument.  The split partials, arrival counters and merge jobs
+ * live in a static device array of PA_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds, one copy per GPU it runs on, until the process ends.
+ *  - The first call on a GPU (with that GPU current) looks the array up
+ *    (hipGetSymbolAddress) and clears its counter area with a fill kernel on
+ *    `stream`; every call leaves the counters at zero again.  After that the
+ *    call allocates nothing: no hipMalloc, hipFree or allocating library
+ *    routine.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents.  Calls that can overlap on one GPU (several streams
+ *    without ordering, several host threads) race and give wrong rows: order
+ *    them, as calls sharing a workspace are ordered.
+ *  - PA_ERR_INVALID_ARG, before any device work, when
+ *    pa_decode_workspace_bytes for these shapes exceeds
+ *    PA_NOALLOC_SCRATCH_BYTES; pa_decode_attention with a caller workspace
+ *    serves such shapes. */
+pa_status pa_decode_attention_noalloc(const void* q, const pa_pool* pool,
+                                      const int32_t* block_tables_dev, const int32_t* seq_lens_dev,
+                                      int32_t batch, int32_t n_q_heads, int32_t q_dtype,
+                                      int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                                      void* out, void* stream);
+
 /* ---- speculative verify step ----------------------------------------------- */
 
 /* Workspace bytes pa_verify_attention needs for these shapes. */

@@ -84,6 +84,7 @@ _PROTOS = {
     "pa_stream_read": [vp, sz, vp, vp],
     "pa_seq_settle": [vp, i32, vp, P32],
     "pa_decode_attention": _DECODE_ARGS,
+    "pa_decode_attention_noalloc": [vp, vp, P32, P32, i32, i32, i32, i32, i32, f32, vp, vp],
     "pa_verify_workspace_bytes": [vp, i32, i32, i32, i32, C.POINTER(sz)],
     "pa_verify_attention": [vp, vp, P32, P32, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz, vp],
     "pa_prefill_workspace_bytes": [vp, i32, i32, i32, i32, C.POINTER(sz)],
@@ -339,6 +340,18 @@ def pa_decode_attention(q, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype
                         max_seq_len, scale, out, workspace, workspace_bytes, stream=None):
     _decode(lib().pa_decode_attention, q, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype,
             max_blocks, max_seq_len, scale, out, workspace, workspace_bytes, stream)
+
+
+# bytes of the library's static scratch (include/pa.h, PA_NOALLOC_SCRATCH_BYTES)
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def pa_decode_attention_noalloc(q, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype,
+                                max_blocks, max_seq_len, scale, out, stream=None):
+    dt = DTYPES[q_dtype] if isinstance(q_dtype, str) else int(q_dtype)
+    _check(lib().pa_decode_attention_noalloc(_ptr(q), pool, _i32ptr(tables_dev), _i32ptr(lens_dev),
+                                             batch, n_q_heads, dt, max_blocks, max_seq_len, scale,
+                                             _ptr(out), _ptr(stream)))
 
 
 def pa_decode_split(q, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype, max_blocks,

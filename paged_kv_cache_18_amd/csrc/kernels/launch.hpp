@@ -82,6 +82,9 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
 // of 128 (query, head) columns), no workspace.
 hipError_t launch_prefill_tile(const DecodeArgs& a, hipStream_t s);
 
+// Zero `bytes` (a multiple of 16) at p with plain vector stores.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
 // Streaming read of `bytes` (a multiple of 16) at src with `grid` workgroups.
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, int grid, hipStream_t s);
 

@@ -3,7 +3,10 @@
 // workgroup reads contiguous 32 KiB spans in a grid-stride loop (eight
 // 16-byte loads in flight per lane) and folds them into one word that decides
 // a (practically never taken) store to sink[0], so the loads cannot be
-// dropped.
+// dropped.  Also the plain zero fill that clears the allocation-free
+// decode's static scratch counters.
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace pa {
@@ -32,7 +35,21 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Plain zero fill, 16 bytes per thread and trip.
+__global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ dst, size_t n16) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256)
+    dst[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 }  // namespace
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const unsigned grid = unsigned(std::min<size_t>((n16 + 255) / 256, 1024));
+  hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, static_cast<u32x4*>(p), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, int grid, hipStream_t s) {
   hipLaunchKernelGGL(stream_read_kernel, dim3(unsigned(grid)), dim3(256), 0, s,

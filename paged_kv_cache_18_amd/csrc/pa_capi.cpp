@@ -10,6 +10,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -279,10 +280,15 @@ bool prefill_tile(const pa_pool* pool, const Plan& pl) {
          env_int("PA_PREFILL_TILE", 1) != 0;
 }
 
+void* noalloc_scratch(hipStream_t s);
+
+// noalloc: take the workspace from the library's static scratch array
+// (pa_decode_attention_noalloc) instead of ws / ws_bytes.
 pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* tables,
                  const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t q_dtype,
                  int32_t max_blocks, int32_t max_seq_len, float scale, void* out, void* ws,
-                 size_t ws_bytes, void* stream, int32_t n_query = 1, bool prefill = false) {
+                 size_t ws_bytes, void* stream, int32_t n_query = 1, bool prefill = false,
+                 bool noalloc = false) {
   return guard([&] {
     need_device(pool);
     check_shapes(pool, batch, n_q_heads, max_seq_len);
@@ -306,6 +312,15 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     const bool tile = prefill && prefill_tile(pool, pl);
     if (pl.kernel == pa::kKernGeneric && int64_t(batch) * n_query > 65535)
       fail(pa::kUnsupported, "batch * n_query above 65535 on the generic kernel");
+    if (noalloc && !tile && pl.ws_bytes > 0) {
+      if (pl.ws_bytes > PA_NOALLOC_SCRATCH_BYTES)
+        fail(pa::kInvalidArg, "these shapes need " + std::to_string(pl.ws_bytes) +
+                                  " bytes of workspace, above the static scratch of " +
+                                  std::to_string(size_t(PA_NOALLOC_SCRATCH_BYTES)) +
+                                  " bytes: use pa_decode_attention with a workspace");
+      ws = noalloc_scratch(static_cast<hipStream_t>(stream));
+      ws_bytes = PA_NOALLOC_SCRATCH_BYTES;
+    }
     if (!tile && pl.ws_bytes > 0) {
       need(ws, "workspace");
       if (ws_bytes < pl.ws_bytes)
@@ -350,6 +365,42 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     if (phase & kCombine) check_hip(pa::launch_decode_combine(a, s), "decode combine launch");
   });
 }
+
+// ---- static scratch of the allocation-free decode ---------------------------------
+// One copy per GPU (each device that loads the library's code object holds
+// its own), kept until the process ends.  Host code never passes the array's
+// name to a kernel or a copy: in host code it is a stand-in, not a device
+// address.  The device address comes from hipGetSymbolAddress, once per
+// device with that device current, and is kept per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The current device's scratch address; the first call on a device looks it
+// up and clears the counter area (the only part a call expects at zero, and
+// which every call leaves at zero) with a fill kernel on `s`.
+void* noalloc_scratch(hipStream_t s) {
+  int dev = -1;
+  check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) fail(pa::kUnsupported, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p || reinterpret_cast<uintptr_t>(p) % 256) fail(pa::kHip, "scratch address not 256-byte aligned");
+    check_hip(pa::launch_zero(p, kCtrBytes, s), "scratch clear launch");
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+static_assert(kCtrBytes <= PA_NOALLOC_SCRATCH_BYTES, "the counters fit the static scratch");
 
 }  // namespace
 
@@ -664,6 +715,14 @@ pa_status pa_decode_attention(const void* q, const pa_pool* pool, const int32_t*
                               void* ws, size_t ws_bytes, void* stream) {
   return decode(kBoth, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
                 scale, out, ws, ws_bytes, stream);
+}
+
+pa_status pa_decode_attention_noalloc(const void* q, const pa_pool* pool, const int32_t* tables,
+                                      const int32_t* lens, int32_t batch, int32_t n_q_heads,
+                                      int32_t q_dtype, int32_t max_blocks, int32_t max_seq_len,
+                                      float scale, void* out, void* stream) {
+  return decode(kBoth, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
+                scale, out, nullptr, 0, stream, 1, false, true);
 }
 
 pa_status pa_decode_split(const void* q, const pa_pool* pool, const int32_t* tables,

@@ -37,6 +37,12 @@ def test_exports_match_header(libpa):
         assert hasattr(lib, s), s
 
 
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.PA_NOALLOC_SCRATCH_BYTES
+
+
 def _state(pool_lib, oracle, sids):
     tables_lib = [B.pa_block_tables(pool_lib, [s], 4096)[0][0] for s in sids]
     lens_lib = [B.pa_seq_info(pool_lib, s)[0] for s in sids]
