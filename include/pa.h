@@ -284,6 +284,12 @@ pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t 
  *       b is the id of logical block j (tokens 16j..16j+15) of sequence b.
  *  seq_lens_dev: device int32 [batch], each in [0, max_seq_len]; entries past
  *       ceil(len/16) are not read.  Out-of-range ids are skipped.
+ *       With a sink arena, the entries of logical blocks below
+ *       sink_blocks_per_seq must be sink-arena ids (tables the library
+ *       exports always are); any later entry may be of either arena: with a
+ *       window, FP16 blocks can sit between body blocks (a table read
+ *       between a multi-block pa_seq_reserve and its pa_seq_settle, or after
+ *       a settle refused for want of body blocks) and are read as FP16.
  *  n_q_heads: multiple of n_kv_heads; query head h reads KV head
  *       h / (n_q_heads / n_kv_heads).
  *  scale: softmax scale (1/sqrt(head_dim) in the usual case).

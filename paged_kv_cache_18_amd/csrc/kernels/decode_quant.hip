@@ -160,12 +160,15 @@ __device__ inline float half_sel(const uint32_t (&m)[2 * NG], int i, int sel) {
 // softmax statistics.  On the K side each group has its own accumulator
 // (dims 32kk.. lie in group kk * NG / 4).
 //
-// FP16 blocks (sink and window): a table row reads sink blocks, then body
-// blocks, then the FP16 blocks of the window (ids >= num_blocks).  The body
-// loop runs over every non-sink block of the piece and gives the window's
-// blocks no weight; the window's run at the end of the piece is found by a
-// backward scan of the table (issued before the body loop, read after it) and
-// streamed, with the piece's sink blocks, by a second pipelined loop.
+// FP16 blocks (sink and window): a settled table row reads sink blocks, then
+// body blocks, then the FP16 blocks of the window (ids >= num_blocks).  The
+// body loop runs over every non-sink block of the piece and gives FP16 ids no
+// weight; the window's run at the end of the piece is found by a backward
+// scan of the table (issued before the body loop, read after it) and
+// streamed, with the piece's sink blocks, by a second pipelined loop.  FP16
+// ids the body loop met before that run (a table between a multi-block
+// reserve and its settle: FP16 runs between body runs) are streamed after
+// it, one block at a time, by the wave that met them.
 template <int KIND, int NB, int NG>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 3 : 2))) void decode_split_quant(DecodeArgs a) {
   typedef typename Quant<KIND, NG>::Buf Buf;
@@ -429,6 +432,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     // their waits (past the end the last block is re-read: an L2 hit)
     const int jw = lo + w;
     const int n = jw < jend ? (jend - jw + kWaves - 1) / kWaves : 0;
+    // the first position of this wave at which the body loop met an FP16 id
+    // (given no weight there; see the FP16 blocks below)
+    int first16 = jend;
     if (n > 0) {
       auto id_of = [&](int k) { return table_entry(trow + jw + kWaves * min(k, n - 1)); };
       auto valid_of = [&](int k, int id) { return ok(id) ? L - 16 * (jw + kWaves * k) : 0; };
@@ -456,13 +462,27 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
           // block's loads (it would wait for data still in flight)
           __builtin_amdgcn_sched_barrier(0);
           consume(valid_of(k + s, ids[s]), buf[s]);
+          if (ok16(ids[s])) first16 = min(first16, jw + kWaves * (k + s));
         }
       }
 #pragma unroll
       for (int s = 0; s < NB - 1; ++s)
-        if (k + s < n) consume(valid_of(k + s, ids[s]), buf[s]);
+        if (k + s < n) {
+          consume(valid_of(k + s, ids[s]), buf[s]);
+          if (ok16(ids[s])) first16 = min(first16, jw + kWaves * (k + s));
+        }
     } else {
       prep_q();
+    }
+    // the query fragments in natural element order, for the FP16 blocks
+    h8 qf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const h8 q = qp[kk];
+      if constexpr (KIND == kInt4)
+        qf[kk] = h8{q[0], q[2], q[4], q[6], q[1], q[3], q[5], q[7]};
+      else
+        qf[kk] = q;
     }
 
     // the window's FP16 run [jt, jend): count FP16 ids backward from jend - 1
@@ -485,15 +505,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     const int nf = ns + (jend - jt);
     const int n16 = w < nf ? (nf - w + kWaves - 1) / kWaves : 0;
     if (n16 > 0) {
-      h8 qf[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const h8 q = qp[kk];
-        if constexpr (KIND == kInt4)
-          qf[kk] = h8{q[0], q[2], q[4], q[6], q[1], q[3], q[5], q[7]};
-        else
-          qf[kk] = q;
-      }
       auto j16 = [&](int k) {
         const int i = w + kWaves * min(k, n16 - 1);
         return i < ns ? jbeg + i : jt + (i - ns);
@@ -513,6 +524,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
         consume16(valid16(k + 1, ids[1]), bb[1], qf);
       }
       if (k < n16) consume16(valid16(k, ids[0]), bb[0], qf);
+    }
+    // FP16 blocks before the window's run: a table read between a reserve of
+    // several blocks and its settle holds the old window's FP16 blocks
+    // between body runs (and a failed settle leaves them there).  The body
+    // loop gave them no weight; this wave streams the ones at its own
+    // positions in [first16, jt) here, one at a time (a settled table never
+    // takes this path).
+    for (int j = first16; j < jt; j += kWaves) {
+      const int id = table_entry(trow + j);
+      if (ok16(id)) {
+        Buf16 one;
+        fetch16(id, one);
+        consume16(L - 16 * j, one, qf);
+      }
     }
 
     // ---- finish the piece: zero-point correction, merge ------------------------------

@@ -192,17 +192,21 @@ def mixed_precision(seed=4, kv="int4", length=65536, steps=64, group=128,
 
 
 def window_batch(lengths, steps=0, window=128, group=64, kv="int4", n_q_heads=32, n_kv_heads=8,
-                 head_dim=128, seed=12, settle=True):
+                 head_dim=128, seed=12, settle=True, chunk=1):
     """Sequences of the given lengths with a one-block FP16 sink and a local
-    FP16 window of ``window`` tokens, then ``steps`` decode steps (one token
-    per sequence, each followed by a settle unless ``settle`` is False: then
-    the blocks that leave the window stay FP16), INT4 groups of ``group`` or
-    FP8 body, 1 % outlier channels x10."""
+    FP16 window of ``window`` tokens, then ``steps`` steps that each add
+    ``chunk`` tokens per sequence (1: decode steps; more: verify steps or
+    prefill chunks), each followed by a settle unless ``settle`` is False:
+    then the blocks that leave the window stay FP16, and a chunk of several
+    blocks leaves the table with FP16 runs between body runs.  INT4 groups
+    of ``group`` or FP8 body, 1 % outlier channels x10."""
     lengths = [int(L) for L in lengths]
     B = len(lengths)
-    body = sum(max(0, -(-(L + steps) // BLOCK) - 1) for L in lengths)
+    grow = steps * chunk
+    body = sum(max(0, -(-(L + grow) // BLOCK) - 1) for L in lengths)
     n = max(1, _pool_size(body))
-    n_sink = B * (1 + -(-window // BLOCK) + 2 + (0 if settle else -(-steps // BLOCK)))
+    n_sink = B * (1 + -(-window // BLOCK) + 2 + (0 if settle else steps * (-(-window // BLOCK) + 1)
+                                                  + -(-grow // BLOCK)))
     ops = []
     src = {}
     for b, L in enumerate(lengths):
@@ -210,8 +214,8 @@ def window_batch(lengths, steps=0, window=128, group=64, kv="int4", n_q_heads=32
         src[b] = [(1, b, L)]
     for s in range(steps):
         for b in range(B):
-            ops += [("reserve", b, 1)] + ([("settle", b)] if settle else [])
-            src[b].append((6, s * 4096 + b, 1))
+            ops += [("reserve", b, chunk)] + ([("settle", b)] if settle else [])
+            src[b].append((6, s * 4096 + b, chunk))
     n_o = max(1, int(round(0.01 * n_kv_heads * head_dim)))
     outl = np.sort(rng(seed, 4).choice(n_kv_heads * head_dim, size=n_o, replace=False))
     return Workload(f"window-{kv}-w{window}" + ("" if settle else "-lag"), seed, n_q_heads, n_kv_heads, head_dim, kv, "f16", "f16",
@@ -219,7 +223,7 @@ def window_batch(lengths, steps=0, window=128, group=64, kv="int4", n_q_heads=32
                     group_size=group if kv == "int4" else 0, num_sink_blocks=n_sink,
                     sink_blocks_per_seq=1, sink_free_order=rng(seed, 5).permutation(n_sink),
                     outlier_channels=outl, window_tokens=window,
-                    extra={"lengths": [L + steps for L in lengths], "steps": steps})
+                    extra={"lengths": [L + grow for L in lengths], "steps": steps})
 
 
 def chunked_prefill(seed=9, lengths=(4096, 4096, 4096, 4096), chunk=512, n_q_heads=32, n_kv_heads=8,

@@ -526,6 +526,38 @@ def test_window_quant_kernel(kvdt, group, window, settle, split):
         assert_close(out_g, ref, "f16", f"window generic {kvdt} g{group} w{window}")
 
 
+@pytest.mark.parametrize("kvdt,group", [("int4", 64), ("fp8", 0), ("int4", 128)])
+@pytest.mark.parametrize("split", range(len(WINDOW_SPLITS)))
+def test_window_fp16_runs_between_body_runs(kvdt, group, split):
+    """Reserves of 200 tokens (13 blocks, more than the 128-token window)
+    with no settle after them: each reserve sends its blocks that are already
+    out of the window straight to the body, while the previous window's
+    blocks stay FP16, so the tables hold FP16 runs between body runs.  The
+    quantized kernel streams every FP16 block wherever it sits (decode and a
+    verify step); the generic kernel does too."""
+    from _ref import expected_verify, oracle_pool
+    wl = W.window_batch([1, 500, 1300], steps=3, window=128, chunk=200, group=group or 64,
+                        kv=kvdt, seed=161, settle=False)
+    pool = oracle_pool(wl)
+    runs = []
+    for sid in wl.decode_seqs:
+        f = "".join("F" if x >= wl.num_blocks else "b" for x in pool.seq_table(sid))
+        runs.append(len([r for r in f.split("b") if r]))
+    assert min(runs) >= 4, runs                  # sink + three window runs per table
+    key = ("runs", kvdt, group)
+    if key not in _window_ref:
+        _window_ref[key] = expected(wl)
+    env = WINDOW_SPLITS[split]
+    kv, out, t, l = run(wl, env=env)
+    assert_close(out, _window_ref[key], "f16", f"fp16 runs {kvdt} g{group} {env}")
+    if split == 0:
+        check_stored(kv, wl, t, l)
+        _, out_g, _, _ = run(wl, env={"PA_DECODE_KERNEL": "generic"})
+        assert_close(out_g, _window_ref[key], "f16", f"fp16 runs generic {kvdt} g{group}")
+        _, outv = run_verify(wl, 6)
+        assert_close(outv, expected_verify(wl, 6), "f16", f"fp16 runs verify {kvdt} g{group}")
+
+
 @pytest.mark.parametrize("nb", ["2", "3", "4"])
 def test_int4_g64_eight_query_heads_per_kv_head(nb):
     """INT4 groups of 64 with 8 query heads per KV head: the matrix-core B
