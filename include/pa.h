@@ -19,9 +19,11 @@
  *    library state is unchanged (calls are all-or-nothing) and
  *    pa_last_error() returns a thread-local message.  No C++ exception
  *    crosses this boundary.
- *  - The library never allocates device memory.  Every device buffer (pool
- *    memory, q/k/v/out, tables, lengths, slots, workspace) is owned by the
- *    caller and must outlive the calls that use it.  Host arrays passed in are
+ *  - The library never allocates device memory at run time.  Every device
+ *    buffer (pool memory, q/k/v/out, tables, lengths, slots, workspace) is
+ *    owned by the caller and must outlive the calls that use it.  The one
+ *    exception is static: the scratch array of pa_decode_attention_noalloc,
+ *    which comes with the library's code object.  Host arrays passed in are
  *    copied during the call.
  *  - "stream" is a hipStream_t passed as void* (NULL = the default stream).
  *    Device work is asynchronous on that stream; no call synchronizes.
@@ -195,7 +197,12 @@ pa_status pa_num_clones(const pa_pool* pool, int64_t* out);
 
 /* New empty sequence; ids are 0, 1, 2, ... and are not reused. */
 pa_status pa_seq_create(pa_pool* pool, int32_t* out_seq);
-/* Child sharing all of parent's blocks (each gains one reference). */
+/* Child sharing all of parent's blocks (each gains one reference): several
+ * requests or samples over one prompt hold the same physical blocks ([8GB]
+ * section 3, "Copy-on-Write (CoW) Prefix Sharing"; [PR8] 8.1: reference-
+ * counted block sharing makes best-of-8 over a 2,000-token prompt take 2,800
+ * token slots instead of 16,800).  A later write into a shared partial tail
+ * clones it first (pa_seq_reserve). */
 pa_status pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* out_child);
 /* Append n_tokens slots to `seq`: a new block only when the tail is full
  * ([60Y] "a ideia roubada"); logical blocks < sink_blocks_per_seq, and with
@@ -219,11 +226,16 @@ pa_status pa_seq_reserve(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* 
 pa_status pa_seq_settle(pa_pool* pool, int32_t seq, void* stream, int32_t* n_moved);
 /* Shorten to new_len tokens; blocks no longer used are released last-first. */
 pa_status pa_seq_truncate(pa_pool* pool, int32_t seq, int32_t new_len);
-/* Release all blocks (last-first) and forget the sequence. */
+/* Release all blocks (last-first) and forget the sequence: blocks go back to
+ * the pool once no longer needed ([3MIN] "A analogia com memoria virtual");
+ * a block still shared keeps its other references. */
 pa_status pa_seq_release(pa_pool* pool, int32_t seq);
 pa_status pa_seq_info(const pa_pool* pool, int32_t seq, int32_t* len, int32_t* n_blocks);
 /* Export tables of `n` sequences into host tables_out [n][max_blocks] (int32,
- * padded with -1) and host lens_out [n]; the caller uploads them. */
+ * padded with -1) and host lens_out [n]; the caller uploads them.  Entry j
+ * is the physical id of logical block j ([8GB] section 3, "How
+ * Logical-to-Physical Block Tables Work"; [PR8] 8.1: the table maps logical
+ * positions to physical block ids and is an extra input of the kernel). */
 pa_status pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n,
                           int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
 
@@ -395,8 +407,9 @@ pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t*
 pa_status pa_prefill_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
                                      int32_t chunk, int32_t max_seq_len, size_t* bytes);
 
-/* Attention of one prefill chunk ([8GB] section 6: a long prompt is
- * prefilled in slices of 512 tokens, so the Q K^T tile never spans the whole
+/* Attention of one prefill chunk ([8GB] section 5, "Notice two critical
+ * details", item 1 "Chunked Prefill": a long prompt is prefilled in slices
+ * of 512 tokens, so the Q K^T tile never spans the whole
  * prompt; the slice's K/V go into the paged cache through the tables first).
  * The chunk's tokens are already reserved and appended, so they are the last
  * `chunk` cached tokens of every sequence; query i of the chunk attends to

@@ -80,8 +80,9 @@ def verify_attention_one(q, K, V, scale):
 def causal_attention(q, K, V, scale):
     """Causal self-attention of a whole prompt in one pass: token i's query
     sees tokens 0..i.  Written as one masked score matrix (the form that
-    chunked prefill avoids materializing: 8GB page, section 6, "Chunked
-    Prefill"), independently of the per-query loops above.
+    chunked prefill avoids materializing: 8GB page, section 5, "Notice two
+    critical details", item 1 "Chunked Prefill"), independently of the
+    per-query loops above.
 
     q: [P][Hq][D]; K, V: [P][Hkv][D].  Returns [P][Hq][D] float64.
     """
@@ -104,7 +105,8 @@ def causal_attention(q, K, V, scale):
 
 
 def prefill_chunks(q, K, V, scale, chunk):
-    """A prompt prefilled in chunks of `chunk` tokens (8GB page, section 6):
+    """A prompt prefilled in chunks of `chunk` tokens (8GB page, section 5,
+    "Notice two critical details", item 1 "Chunked Prefill"):
     chunk c's K/V join the cache, then its queries attend over the cache so
     far, causally among themselves -- the verify step's operation with
     n_query = the chunk's length.  Returns [P][Hq][D] float64."""

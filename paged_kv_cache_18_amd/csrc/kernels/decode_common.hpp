@@ -144,19 +144,6 @@ __device__ inline int blocks_of(const DecodeArgs& a, const SH& sh, int b) {
   return (len_of(a, sh, b) + 15) >> 4;
 }
 
-// Start of sequence b's segments in the flattened list: seg_heads * sum_{b'<b} nb_b'.
-template <class SH>
-__device__ inline int seq_start(const DecodeArgs& a, const SH& sh, int b, int lane) {
-  if (b == 0) return 0;
-  if (b <= kLenCap) return sh.pre[b - 1];
-  int acc = 0;
-  for (int base = 0; base < b; base += 64) {
-    const int bb = base + lane;
-    acc += bb < b ? blocks_of(a, sh, bb) : 0;
-  }
-  return wave_sum_int(acc) * seg_heads(a);
-}
-
 // Output columns of a segment (b, hv), hv = h*nsl + s (KV head h, column
 // slice s of SW columns): its column col is the (query, head) column
 // gc = s*SW + col = qi*G + gi, query qi of the sequence's n_query (1 for

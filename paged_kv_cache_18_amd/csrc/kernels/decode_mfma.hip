@@ -8,18 +8,21 @@
 // aplica memoria virtual ao cache KV de LLMs").  The pages' kernel was written
 // for a consumer GPU in CUDA/Triton; this one is laid out for CDNA4.
 //
-// Work decomposition.  The blocks of every (sequence b, KV head h) segment are
-// laid end to end in one list (b major, then h, then logical block j), and
-// workgroup c owns the chunk [c*C, (c+1)*C) of it, whatever the sequence
-// lengths.  By default the grid is one workgroup per resident slot of the
-// GPU and C = ceil(W / grid) for the W blocks of this call (read from the
-// lengths on the device), so every workgroup streams the same number of
-// blocks and all finish together; a fixed C can be requested instead.  A segment that lies inside one chunk
-// is finished there (normalized and written to out).  A segment crossing chunk
-// boundaries leaves one partial (max, sum, weighted sum) per chunk it touches;
-// a chunk holds at most two such pieces (its first and its last), so the
-// workspace is two slots per workgroup; the workgroup that completes a
-// segment merges its partials.
+// Work decomposition (decode_common.hpp).  The blocks of every (sequence b,
+// KV head h) segment are laid end to end in one list, KV head major (h, then
+// b, then logical block j), so every head's list holds the same TB blocks.
+// By default the grid is one workgroup per resident slot of the GPU (at most
+// two per compute unit) and each head's list is cut into q = grid / heads
+// regions of C = ceil(TB / q) blocks (sized on the device from the lengths),
+// so every workgroup streams the same number of blocks; a fixed C can be
+// requested instead.  Region k of head h goes to workgroup k*heads + h
+// (Units::owned_by_head): workgroups are dealt to the 8 XCDs round robin, so
+// with 8 KV heads each XCD streams one head's slabs of every block.  A
+// segment that lies inside one region is finished there (normalized and
+// written to out).  A segment crossing region boundaries leaves one partial
+// (max, sum, weighted sum) per region it touches; a region holds at most two
+// such pieces (its first and its last), so the workspace is two slots per
+// workgroup; the workgroup that completes a segment merges its partials.
 //
 // Inside a workgroup (4 wavefronts) a piece's blocks go round-robin to the
 // waves.  All G = Hq/Hkv query heads of the KV head are packed into one

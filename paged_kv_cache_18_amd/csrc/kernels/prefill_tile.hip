@@ -1,7 +1,8 @@
 // Chunked-prefill attention on the matrix cores, for 16-bit pools of 16-token
 // blocks and head_dim 128.
 //
-// "The 8GB VRAM Breakthrough ...", section 6: a long prompt is prefilled in
+// "The 8GB VRAM Breakthrough ...", section 5 ("Notice two critical details",
+// item 1, "Chunked Prefill"): a long prompt is prefilled in 512-token
 // chunks; each chunk's queries attend, causally, over everything the
 // sequence has cached so far (earlier chunks plus the chunk itself, appended
 // through the block table first).  Query qi of a chunk of n_query sits at

@@ -228,7 +228,8 @@ def window_batch(lengths, steps=0, window=128, group=64, kv="int4", n_q_heads=32
 
 def chunked_prefill(seed=9, lengths=(4096, 4096, 4096, 4096), chunk=512, n_q_heads=32, n_kv_heads=8,
                     head_dim=128, dt="bf16"):
-    """Prompts prefilled in chunks of `chunk` tokens (8GB page, section 6):
+    """Prompts prefilled in chunks of `chunk` tokens (8GB page, section 5,
+    "Notice two critical details", item 1 "Chunked Prefill"):
     round k reserves (and writes) every unfinished prompt's next chunk, so
     the sequences' blocks interleave in the pool as a chunk scheduler would
     leave them.  Chunk k's queries: q_chunk(k, n)."""

@@ -1,5 +1,5 @@
-"""Pins of the chunked-prefill oracle (8GB page, section 6, "Chunked
-Prefill"): slicing a prompt into chunks changes no result, so the chunked
+"""Pins of the chunked-prefill oracle (8GB page, section 5, "Notice two
+critical details", item 1 "Chunked Prefill"): slicing a prompt into chunks changes no result, so the chunked
 evaluation (per-query prefix loops, the verify step's operation) must equal
 causal attention written as one masked score matrix, for every chunk size;
 plus closed forms that hold whatever the chunking."""
