@@ -17,7 +17,10 @@ its own launch durations, measured with HIP events on the launch stream;
 (profiles/hbm_traffic.json) over the same duration.  `stream_read_gbs` is a
 plain streaming read of the same byte count (the achievable rate).
 `cpu_baseline` times the CPU oracle (logical rebuild through the tables +
-float64 attention) on a bounded sample of the same batch.
+float64 attention) on a bounded sample of the same batch.  `warm` and `cold`
+give the median / p10 / p90 of per-step HIP-event times, each step timed on
+its own: warm behind a spin kernel (no memory traffic), cold after a 512 MiB
+device read that evicts the 256 MB Infinity Cache and the L2s.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config llama3-8b]
 """
@@ -160,8 +163,8 @@ def main():
     ap.add_argument("--config", default="llama3-8b", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time the split kernel with a 512 MiB cache flush between steps")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed one by one after a 512 MiB cache flush (0 = skip)")
     ap.add_argument("--identity-tables", action="store_true",
                     help="physical blocks in logical order (free order 0..N-1): the contiguous "
                          "comparator for the paging overhead")
@@ -274,24 +277,51 @@ def main():
     achieved = byts / (split_avg * 1e-3) / 1e9
 
     extra = {}
-    if args.cold:
+
+    def one_by_one(n, pre):
+        """Per-step event times (us) of n steps and of their split launches,
+        each step preceded by `pre` (queued GPU work, so the host has
+        enqueued the step's launches before the GPU reaches them)."""
+        ev = []
+        for _ in range(n):
+            pre()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, n_new, sh)
+            e[1].record(stream)
+            attn_split()
+            e[2].record(stream)
+            attn_rest()
+            e[3].record(stream)
+            ev.append(e)
+        torch.cuda.synchronize()
+        step = [1e3 * e[0].elapsed_time(e[3]) for e in ev]
+        split = [1e3 * e[1].elapsed_time(e[2]) for e in ev]
+        return step, split
+
+    def dist(x):
+        p10, p50, p90 = np.percentile(np.asarray(x), [10, 50, 90])
+        return {"median": round(float(p50), 2), "p10": round(float(p10), 2),
+                "p90": round(float(p90), 2), "n": len(x)}
+
+    # warm: a spin kernel (no memory traffic) ahead of each step
+    warm_step, warm_split = one_by_one(args.steps, lambda: torch.cuda._sleep(300_000))
+    extra["warm"] = {"step_us": dist(warm_step), "split_us": dist(warm_split)}
+    if args.cold_steps > 0:
         # evict the caches by *reading* 512 MiB (more than the 256 MB
         # Infinity Cache plus the L2s); a write would leave dirty lines whose
         # write-back would compete with the timed kernel
         flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-        cold = []
-        for _ in range(max(10, args.steps // 2)):
-            flush.sum()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            attn_split()
-            e1.record(stream)
-            attn_rest()
-            torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1))
-        extra["cold_split_ms_median"] = round(float(np.median(cold)), 4)
-        extra["cold_split_gbs"] = round(byts / (np.median(cold) * 1e-3) / 1e9, 1)
+        cold_step, cold_split = one_by_one(args.cold_steps, lambda: flush.sum())
+        med = float(np.median(cold_split))
+        extra["cold"] = {"step_us": dist(cold_step), "split_us": dist(cold_split),
+                         "split_gbs_median": round(byts / (med * 1e-6) / 1e9, 1),
+                         "flush": "512 MiB device read before each step"}
+        if args.config in MFMA_BOUND:
+            tfl = causal_flops(lens, nq, wl.n_q_heads, wl.head_dim) / (med * 1e-6) / 1e12
+            extra["cold"]["split_frac_median"] = round(tfl / MFMA_PEAK_TFLOPS, 4)
+        else:
+            extra["cold"]["split_frac_median"] = round(byts / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         del flush
     # achievable read rate: the library's plain streaming-read kernel over a
     # buffer of the same byte count (reported beside the result; the roofline
