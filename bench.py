@@ -57,13 +57,19 @@ WORKLOADS = {
     "spec-verify": "speculative verify step (gamma = 5: 6 causal queries per sequence) on the "
                    "Llama-3-8B-shaped batch: 64 sequences, lengths U[512,4096], 32 q / 8 kv heads, "
                    "head_dim 128, bf16, shuffled tables",
+    "spec-verify-int4": "speculative verify step (gamma = 5: 6 causal queries) on the mixed-precision "
+                        "sequence: 1 x 65,536 (+64 appended) tokens, FP16 sink block, INT4 g128 body, "
+                        "32 q / 8 kv heads, head_dim 128, 1% outlier channels x10",
+    "spec-verify-window": "speculative verify step (gamma = 5: 6 causal queries) on the pages' scheme: "
+                          "1 x 65,536 (+64 appended, each settled) tokens, FP16 sink block and "
+                          "last-128-token FP16 window, INT4 g64 body, 32 q / 8 kv heads, head_dim 128",
     "llama3-8b-bs8": "the Llama-3-8B-shaped decode batch in a pool of 8-token blocks",
     "llama3-8b-bs32": "the Llama-3-8B-shaped decode batch in a pool of 32-token blocks",
     "prefill-chunk": "chunked paged prefill: the last 512-token chunk of 4 prompts of 4,096 tokens "
                      "(causal over the cached prefix and the chunk), 32 q / 8 kv heads, head_dim 128, "
                      "bf16, prompts reserved chunk by chunk",
 }
-N_QUERY = {"spec-verify": 6, "prefill-chunk": 512}   # queries per sequence of the step (1 = decode)
+N_QUERY = {"spec-verify": 6, "spec-verify-int4": 6, "spec-verify-window": 6, "prefill-chunk": 512}   # queries per sequence of the step (1 = decode)
 # configs whose dominant launch is a matrix-core contraction: roofline in
 # TFLOP/s against the dense bf16 peak
 MFMA_BOUND = {"prefill-chunk"}

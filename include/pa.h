@@ -323,7 +323,8 @@ pa_status pa_decode_attention(const void* q, const pa_pool* pool, const int32_t*
                               float scale, void* out, void* workspace, size_t workspace_bytes,
                               void* stream);
 /* Phase 1: split-K attention.  The matrix-core kernels (bf16/fp16 pools, and
- * INT4 with group = head_dim or FP8 pools, head_dim 128, Hq/Hkv <= 16) give
+ * INT4 with group 128 or 64 or FP8 pools, head_dim 128, Hq/Hkv <= 16, or
+ * <= 8 for INT4 groups of 64) give
  * every workgroup an equal chunk of all sequences' blocks; a (sequence, kv
  * head) that spans several chunks is merged by the workgroup completing it,
  * so this phase alone writes every output row.  Other shapes use per-sequence
@@ -392,7 +393,14 @@ pa_status pa_verify_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t 
  *  q, out: device [batch][n_query][n_q_heads][head_dim] of q_dtype.
  *  n_query: 1..4096 (gamma + 1).  Other arguments and the workspace contract
  *  are those of pa_decode_attention.  Rollback of rejected tokens is
- *  pa_seq_truncate (their blocks return to the free stack last-first). */
+ *  pa_seq_truncate (their blocks return to the free stack last-first).
+ *  The matrix-core kernels read each block once for all n_query x G
+ *  (query, head) columns of a KV head: 16-bit pools with D = 128, and
+ *  INT4 (groups of 128 or 64) or FP8 pools with D = 128, whose codes are
+ *  dequantized in registers ([8GB] section 5; the section 8 benchmark's
+ *  "Paged + Sink-INT4 KV + Speculative" combination).  Columns beyond two
+ *  tiles of 16 (32 columns; 16 for INT4 groups of 64, which hold each
+ *  column once per group) are cut into slices that read the blocks again. */
 pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
                               const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
                               int32_t n_query, int32_t q_dtype, int32_t max_blocks_per_seq,
@@ -424,7 +432,7 @@ pa_status pa_prefill_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t
  * For bf16 / fp16 pools of 16-token blocks one workgroup computes 128
  * (query, head) columns of one (sequence, KV head) over every block they
  * see, with the blocks staged once in LDS for all its waves; other pools run
- * the verify step's split kernel. */
+ * the verify step's split kernels (quantized pools: in-register dequant). */
 pa_status pa_prefill_attention(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
                                const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
                                int32_t chunk, int32_t q_dtype, int32_t max_blocks_per_seq,

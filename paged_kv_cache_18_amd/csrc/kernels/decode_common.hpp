@@ -162,7 +162,7 @@ struct OutMap {
 
 __device__ inline OutMap out_map(const DecodeArgs& a) {
   const int G = a.n_q_heads / a.pool.n_kv_heads, nq = max(a.n_query, 1), nsl = max(a.col_slices, 1);
-  return OutMap{G, a.n_q_heads, nq, nsl, nsl > 1 ? 32 : nq * G};
+  return OutMap{G, a.n_q_heads, nq, nsl, nsl > 1 ? a.slice_cols : nq * G};
 }
 
 // The cut of the work list (see the top of this file).  Unit ids grow with

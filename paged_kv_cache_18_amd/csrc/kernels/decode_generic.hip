@@ -210,11 +210,11 @@ hipError_t launch_decode_split_mfma16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_split_quant(const DecodeArgs& a, hipStream_t s);
 
 int occupancy_mfma16(int32_t kv_dtype, int nct);
-int occupancy_quant(int32_t kv_dtype, int32_t group_size);
+int occupancy_quant(int32_t kv_dtype, int32_t group_size, int nct);
 
 int decode_split_occupancy(int32_t kernel, int32_t kv_dtype, int nct, int32_t group_size) {
   if (kernel == kKernMfma16) return occupancy_mfma16(kv_dtype, nct);
-  if (kernel == kKernQuant) return occupancy_quant(kv_dtype, group_size);
+  if (kernel == kKernQuant) return occupancy_quant(kv_dtype, group_size, nct);
   return 1;
 }
 

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_merge_kernel(DecodeArgs a)
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
   const int nsl = max(a.col_slices, 1);
-  const int ncol = nsl > 1 ? 32 : max(a.n_query, 1) * (a.n_q_heads / a.pool.n_kv_heads);
+  const int ncol = nsl > 1 ? a.slice_cols : max(a.n_query, 1) * (a.n_q_heads / a.pool.n_kv_heads);
   const dim3 grid(unsigned(a.batch) * unsigned(a.pool.n_kv_heads * nsl) * unsigned(ncol));
   if (a.q_dtype == kBF16)
     hipLaunchKernelGGL(decode_merge_kernel<__bf16>, grid, dim3(kWaves * 64), 0, s, a);

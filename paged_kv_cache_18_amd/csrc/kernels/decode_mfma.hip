@@ -189,12 +189,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(
       // numerator and denominator share the reference.
       const bool move = bm > m_ref[t] + 8.f;
       if (__any(move)) {
-        const float m_new = move ? bm : m_ref[t];
-        const float alpha = __builtin_amdgcn_exp2f(m_ref[t] - m_new);
+        // factor 1 where the reference stays (no NaN from -inf - -inf for
+        // a column that has seen no token yet)
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_ref[t] - bm) : 1.f;
         l_run[t] *= alpha;
 #pragma unroll
         for (int T_ = 0; T_ < kNT; ++T_) o[t][T_] *= alpha;
-        m_ref[t] = m_new;
+        m_ref[t] = move ? bm : m_ref[t];
       }
       if (t == 0 && valid < 16) {
         // Unwritten tail slots may hold anything (even NaN bit patterns): zero

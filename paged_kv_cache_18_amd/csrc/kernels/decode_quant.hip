@@ -149,16 +149,23 @@ __device__ inline float half_sel(const uint32_t (&m)[2 * NG], int i, int sel) {
   return v;
 }
 
-// NB = register buffers per wave (NB-1 blocks prefetched ahead).
+// NB = register buffers per wave (NB-1 blocks prefetched ahead).  NCT column
+// tiles of 16; CAUSAL: a verify step or prefill chunk (n_query queries per
+// sequence, each seeing the cache up to its own position).
 //
-// Groups (NG > 1, INT4 only; the launch guarantees NG * G <= 16): the
-// matrix-core B operand has 16 columns and a KV head serves G query heads, so
-// column c computes head c % G with the V weights scaled by group c / G.
-// Output tile row r holds dim 8r + T, which lies in group (8r) / group_size =
-// g * NG / 4 for the rows 4g..4g+3 a lane holds: lane (g, c) keeps column
-// c - (g * NG / 4) * G.  The scores of the copies are identical, so are their
-// softmax statistics.  On the K side each group has its own accumulator
-// (dims 32kk.. lie in group kk * NG / 4).
+// Columns.  A tile's 16 matrix-core columns hold S = 16 / NG logical columns
+// once per scale group: column c is logical column c % S of group c / S (NG
+// = 1: every column its own).  Logical column l of tile t is the segment's
+// (query, head) column t*S + l -- for decode the query head, for a verify
+// step query gc / G of head gc % G -- so the B operand computes every query
+// head of the KV head (and every query of the step) against one fetch of
+// the block.  The V weights of column c are scaled by group c / S.  Output
+// tile row r holds dim 8r + T, which lies in group (8r) / group_size =
+// g * NG / 4 for the rows 4g..4g+3 a lane holds: lane (g, c) keeps its
+// column when c / S is that group.  The copies of a logical column compute
+// identical scores, so identical softmax statistics.  On the K side each
+// group has its own accumulator (dims 32kk.. lie in group kk * NG / 4).
+// The codes of a block are converted to fp16 once and serve every tile.
 //
 // FP16 blocks (sink and window): a settled table row reads sink blocks, then
 // body blocks, then the FP16 blocks of the window (ids >= num_blocks).  The
@@ -169,11 +176,12 @@ __device__ inline float half_sel(const uint32_t (&m)[2 * NG], int i, int sel) {
 // ids the body loop met before that run (a table between a multi-block
 // reserve and its settle: FP16 runs between body runs) are streamed after
 // it, one block at a time, by the wave that met them.
-template <int KIND, int NB, int NG>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 3 : 2))) void decode_split_quant(DecodeArgs a) {
+template <int KIND, int NB, int NG, int NCT, bool CAUSAL>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 && NCT == 1 ? 3 : 2))) void decode_split_quant(DecodeArgs a) {
   typedef typename Quant<KIND, NG>::Buf Buf;
   typedef Mfma<_Float16> MF;
-  __shared__ Shared sh;
+  constexpr int S = 16 / NG;  // logical columns per tile
+  __shared__ SharedT<S * NCT> sh;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -181,9 +189,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   const PoolDev& p = a.pool;
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H, N = p.num_blocks;
   const int SP = p.sink_per_seq, NS = p.num_sink_blocks;
-  const int qcol = c < NG * G ? (NG == 1 ? c : c % G) : -1;  // query head (within the group) of column c
-  const int gsel = NG == 1 ? 0 : min(c / G, NG - 1);  // scale group of column c
-  const int keep = c - (NG == 1 ? 0 : (g * NG / 4) * G);  // column this lane writes
+  const int gsel = c / S;                       // scale group of column c
+  const int lcol = c % S;                       // its logical column within a tile
+  const bool keep = gsel == g * NG / 4;         // this lane's output rows lie in that group
+  const OutMap om = out_map(a);
+  const int nq = om.nq, nsl = om.nsl;
   const Units um = setup_units(a, sh, w, lane);
   zero_empty_rows<_Float16>(a, sh);
   int b = 0, fb = 0;
@@ -191,33 +201,45 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   const float sl2 = a.scale_log2;
   const uint8_t* base = p.base;
   const int32_t* trow = a.tables;
-  int h = 0, L = 0;
-  h8 qp[4];         // Q^T fragments in the code's element order
-  float qs[NG];     // per-group sums of the head's query (INT4 zero-point terms)
-  f32x4 o[kNT];
-  float m_ref = -__builtin_inff(), l_run = 0.f, corr = 0.f;
+  int hv = 0, h = 0, L = 0;  // segment hv = h * nsl + column slice
+  h8 qp[NCT][4];             // Q^T fragments in the code's element order
+  float qs[NCT][NG];         // per-group sums of the column's query (INT4 zero-point terms)
+  f32x4 o[NCT][kNT];
+  float m_ref[NCT], l_run[NCT], corr[NCT];
+  int lim[NCT];              // CAUSAL: last position the lane's column of tile t may see
 
   auto ok = [&](int id) { return id >= 0 && id < N; };
   auto ok16 = [&](int id) { return id >= N && id < N + NS; };
 
-  // softmax update for one block's 4 scores per lane; returns the weights
-  auto softmax = [&](const float (&x)[4], int valid, float (&pw)[4]) {
+  // visibility of the lane's 4 tokens of logical block jl for tile t
+  auto visible = [&](int t, int valid, int jl, int i) {
+    bool v = 4 * g + i < valid;
+    if constexpr (CAUSAL) v = v && 16 * jl + 4 * g + i <= lim[t];
+    return v;
+  };
+
+  // softmax update of tile t for one block's 4 scores per lane; returns the
+  // weights (0 for tokens the column does not see)
+  auto softmax = [&](int t, const float (&x)[4], const bool (&vis)[4], float (&pw)[4]) {
     float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     bm = rows_max(bm);
-    const bool move = bm > m_ref + 2.f;
+    const bool move = bm > m_ref[t] + 2.f;
     if (__any(move)) {
-      const float m_new = move ? bm : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_run *= alpha;
-      corr *= alpha;
+      // a lane whose reference stays keeps its sums (factor 1): a column
+      // that has seen no token yet keeps m_ref = -inf, where exp2(-inf -
+      // -inf) would be NaN -- and a causal column can see nothing in one
+      // block and something in a later one (the FP16 blocks come last)
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_ref[t] - bm) : 1.f;
+      l_run[t] *= alpha;
+      corr[t] *= alpha;
 #pragma unroll
-      for (int T_ = 0; T_ < kNT; ++T_) o[T_] *= alpha;
-      m_ref = m_new;
+      for (int T_ = 0; T_ < kNT; ++T_) o[t][T_] *= alpha;
+      m_ref[t] = move ? bm : m_ref[t];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pw[i] = (4 * g + i < valid) ? __builtin_amdgcn_exp2f(x[i] - m_ref) : 0.f;
-      l_run += pw[i];
+      pw[i] = vis[i] ? __builtin_amdgcn_exp2f(x[i] - m_ref[t]) : 0.f;
+      l_run[t] += pw[i];
     }
   };
 
@@ -245,72 +267,84 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     }
   };
 
-  auto consume = [&](int valid, const Buf& bf) {
-    float x[4];
-    if constexpr (KIND == kInt4) {
-      f32x4 acc[NG];
+  // jl: the block's logical index (causal limits)
+  auto consume = [&](int valid, int jl, const Buf& bf) {
+    // K codes as exact fp16 operand fragments, shared by the tiles
+    u32x4 kav[4];
 #pragma unroll
-      for (int k = 0; k < NG; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t cw = bf.kc[kk];
-        const u32x4 av = nib4(cw);
-        acc[kk * NG / 4] = MF::qk(__builtin_bit_cast(h8, av), qp[kk], acc[kk * NG / 4]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sc = 0.f;
-#pragma unroll
-        for (int k = 0; k < NG; ++k)
-          sc += half_at(bf.ks, i * NG + k) * (acc[k][i] - half_at(bf.kz, i * NG + k) * qs[k]);
-        const float xs = pin(sc * sl2);
-        x[i] = (4 * g + i < valid) ? xs : -__builtin_inff();
-      }
-    } else {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 4; ++kk) {
+      if constexpr (KIND == kInt4) {
+        kav[kk] = nib4(bf.kc[kk]);
+      } else {
         const u32x4 u = kk < 2 ? bf.kc0 : bf.kc1;
         const uint32_t x0 = u[(kk & 1) * 2], x1 = u[(kk & 1) * 2 + 1];
-        const u32x4 av = {fp8pair<false>(x0), fp8pair<true>(x0), fp8pair<false>(x1), fp8pair<true>(x1)};
-        acc = MF::qk(__builtin_bit_cast(h8, av), qp[kk], acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float xs = pin(half_at(bf.ks, i) * acc[i] * sl2);
-        x[i] = (4 * g + i < valid) ? xs : -__builtin_inff();
+        kav[kk] = u32x4{fp8pair<false>(x0), fp8pair<true>(x0), fp8pair<false>(x1), fp8pair<true>(x1)};
       }
     }
-    float pw[4];
-    softmax(x, valid, pw);
-    // weights times the V scale of this column's group; tail tokens' metadata
-    // may be garbage: select
-    float pv[4];
+    // B operands of the P V products, per tile
+    h4 bhi[NCT], blo[NCT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float w_ = pin(half_sel<NG>(bf.vs, i, gsel) * pw[i]);
-      pv[i] = (4 * g + i < valid) ? w_ : 0.f;
+    for (int t = 0; t < NCT; ++t) {
+      bool vis[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vis[i] = visible(t, valid, jl, i);
+      float x[4];
+      if constexpr (KIND == kInt4) {
+        f32x4 acc[NG];
+#pragma unroll
+        for (int k = 0; k < NG; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          acc[kk * NG / 4] = MF::qk(__builtin_bit_cast(h8, kav[kk]), qp[t][kk], acc[kk * NG / 4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sc = 0.f;
+#pragma unroll
+          for (int k = 0; k < NG; ++k)
+            sc += half_at(bf.ks, i * NG + k) * (acc[k][i] - half_at(bf.kz, i * NG + k) * qs[t][k]);
+          const float xs = pin(sc * sl2);
+          x[i] = vis[i] ? xs : -__builtin_inff();
+        }
+      } else {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = MF::qk(__builtin_bit_cast(h8, kav[kk]), qp[t][kk], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float xs = pin(half_at(bf.ks, i) * acc[i] * sl2);
+          x[i] = vis[i] ? xs : -__builtin_inff();
+        }
+      }
+      float pw[4];
+      softmax(t, x, vis, pw);
+      // weights times the V scale of this column's group; tail tokens'
+      // metadata may be garbage: select
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float w_ = pin(half_sel<NG>(bf.vs, i, gsel) * pw[i]);
+        pv[i] = vis[i] ? w_ : 0.f;
+      }
+      if constexpr (KIND == kInt4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float z_ = pin(half_sel<NG>(bf.vz, i, gsel) * pv[i]);
+          corr[t] += vis[i] ? z_ : 0.f;
+        }
+      }
+      // B operand in the token order of the code pairs: INT4 (t0, t2),
+      // (t1, t3); FP8 natural
+      const int ord[4] = {0, KIND == kInt4 ? 2 : 1, KIND == kInt4 ? 1 : 2, 3};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bhi[t][e] = _Float16(pv[ord[e]]);
+        blo[t][e] = _Float16(pv[ord[e]] - float(bhi[t][e]));
+      }
     }
     // FP8: zero the bytes of tail tokens (unwritten slots may hold NaN codes)
     const int t0 = 4 * g;
     const uint32_t vmask = (t0 + 0 < valid ? 0x000000FFu : 0u) | (t0 + 1 < valid ? 0x0000FF00u : 0u) |
                            (t0 + 2 < valid ? 0x00FF0000u : 0u) | (t0 + 3 < valid ? 0xFF000000u : 0u);
-    if constexpr (KIND == kInt4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float z_ = pin(half_sel<NG>(bf.vz, i, gsel) * pv[i]);
-        corr += (4 * g + i < valid) ? z_ : 0.f;
-      }
-    }
-    // B operand in the token order of the code pairs: INT4 (t0, t2), (t1, t3);
-    // FP8 natural
-    h4 bhi, blo;
-    const int ord[4] = {0, KIND == kInt4 ? 2 : 1, KIND == kInt4 ? 1 : 2, 3};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      bhi[e] = _Float16(pv[ord[e]]);
-      blo[e] = _Float16(pv[ord[e]] - float(bhi[e]));
-    }
 #pragma unroll
     for (int T_ = 0; T_ < kNT; ++T_) {
       uint32_t lo, hi;
@@ -326,7 +360,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       }
       const u32x2 av = {lo, hi};
       const h4 at = __builtin_bit_cast(h4, av);
-      o[T_] = MF::pv2(at, bhi, blo, o[T_]);
+#pragma unroll
+      for (int t = 0; t < NCT; ++t) o[t][T_] = MF::pv2(at, bhi[t], blo[t], o[t][T_]);
     }
   };
 
@@ -341,21 +376,27 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     for (int u = 0; u < 4; ++u) bf.v[u] = *reinterpret_cast<const u32x4*>(vs + (u * 64 + lane) * 8);
   };
 
-  // qf: the query fragments in natural element order
-  auto consume16 = [&](int valid, const Buf16& bf, const h8 (&qf)[4]) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // qf: the query fragments in natural element order, per tile
+  auto consume16 = [&](int valid, int jl, const Buf16& bf, const h8 (&qf)[NCT][4]) {
+    h4 bhi[NCT], blo[NCT];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) acc = MF::qk(bf.k[kk], qf[kk], acc);
-    float x[4], pw[4];
+    for (int t = 0; t < NCT; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (4 * g + i < valid) ? acc[i] * sl2 : -__builtin_inff();
-    softmax(x, valid, pw);
-    h4 bhi, blo;
+      for (int kk = 0; kk < 4; ++kk) acc = MF::qk(bf.k[kk], qf[t][kk], acc);
+      bool vis[4];
+      float x[4], pw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pe = pw[i];
-      bhi[i] = _Float16(pe);
-      blo[i] = _Float16(pe - float(bhi[i]));
+      for (int i = 0; i < 4; ++i) {
+        vis[i] = visible(t, valid, jl, i);
+        x[i] = vis[i] ? acc[i] * sl2 : -__builtin_inff();
+      }
+      softmax(t, x, vis, pw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bhi[t][i] = _Float16(pw[i]);
+        blo[t][i] = _Float16(pw[i] - float(bhi[t][i]));
+      }
     }
     const int t0 = 4 * g;
     const uint32_t m01 = (t0 + 0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
@@ -371,7 +412,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       for (int par = 0; par < 2; ++par) {
         const u32x2 av = {dw[2 * par], dw[2 * par + 1]};
         const h4 at = __builtin_bit_cast(h4, av);
-        o[2 * u + par] = MF::pv2(at, bhi, blo, o[2 * u + par]);
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) o[t][2 * u + par] = MF::pv2(at, bhi[t], blo[t], o[t][2 * u + par]);
       }
     }
   };
@@ -387,45 +429,55 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   int pos = pos0;
   bool first = true;
   int jbeg = 0, jend = 0, nb = 0;
-  while (next_piece(a, sh, um, pos, pos1, b, fb, h, jbeg, jend, nb)) {
+  while (next_piece(a, sh, um, pos, pos1, b, fb, hv, jbeg, jend, nb)) {
     L = len_of(a, sh, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
+    h = hv / nsl;
+    const int ncol = om.cols(hv);
     const int lo = max(jbeg, SP);  // first non-sink block of the piece
     // the table's last 64 entries of the piece, for the window scan below
     int tid = p.window_tokens > 0 ? trow[max(jend - 1 - lane, 0)] : 0;
-    // Q^T fragment of head qcol (dims 32kk + 8g + 0..7): loaded here, and
-    // permuted into the order in which the code conversion delivers the K
-    // elements (and summed per group) once the body's first blocks are in
-    // flight
-    h8 qraw[4];
-    {
-      const _Float16* qn =
-          static_cast<const _Float16*>(a.q) + (size_t(b) * Hq + h * G + max(qcol, 0)) * kD + 8 * g;
+    // Q^T fragments of the lane's logical column in every tile (dims
+    // 32kk + 8g + 0..7): loaded here, and permuted into the order in which
+    // the code conversion delivers the K elements (and summed per group)
+    // once the body's first blocks are in flight
+    h8 qraw[NCT][4];
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) {
+      const int lc = t * S + lcol;
+      const _Float16* qn = static_cast<const _Float16*>(a.q) + om.row(b, hv, min(lc, ncol - 1)) * kD + 8 * g;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        qraw[kk] = qcol >= 0 ? *reinterpret_cast<const h8*>(qn + 32 * kk) : h8{};
+        qraw[t][kk] = lc < ncol ? *reinterpret_cast<const h8*>(qn + 32 * kk) : h8{};
+      lim[t] = L - nq + om.gcol(hv, min(lc, ncol - 1)) / G;
     }
     auto prep_q = [&]() {
 #pragma unroll
-      for (int k = 0; k < NG; ++k) qs[k] = 0.f;
+      for (int t = 0; t < NCT; ++t) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const h8 q = qraw[kk];
+        for (int k = 0; k < NG; ++k) qs[t][k] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qs[kk * NG / 4] += float(q[e]);
-        if constexpr (KIND == kInt4)
-          qp[kk] = h8{q[0], q[4], q[1], q[5], q[2], q[6], q[3], q[7]};
-        else
-          qp[kk] = q;
+        for (int kk = 0; kk < 4; ++kk) {
+          const h8 q = qraw[t][kk];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qs[t][kk * NG / 4] += float(q[e]);
+          if constexpr (KIND == kInt4)
+            qp[t][kk] = h8{q[0], q[4], q[1], q[5], q[2], q[6], q[3], q[7]};
+          else
+            qp[t][kk] = q;
+        }
+#pragma unroll
+        for (int k = 0; k < NG; ++k) qs[t][k] = rows_sum(qs[t][k]);
       }
-#pragma unroll
-      for (int k = 0; k < NG; ++k) qs[k] = rows_sum(qs[k]);
     };
 #pragma unroll
-    for (int T_ = 0; T_ < kNT; ++T_) o[T_] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_ref = -__builtin_inff();
-    l_run = 0.f;
-    corr = 0.f;
+    for (int t = 0; t < NCT; ++t) {
+#pragma unroll
+      for (int T_ = 0; T_ < kNT; ++T_) o[t][T_] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_ref[t] = -__builtin_inff();
+      l_run[t] = 0.f;
+      corr[t] = 0.f;
+    }
 
     // body blocks, software-pipelined NB-1 blocks ahead with NB register
     // buffers; loads are unconditional so no branch separates them from
@@ -461,29 +513,31 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
           // no instruction of the block's product may move above the next
           // block's loads (it would wait for data still in flight)
           __builtin_amdgcn_sched_barrier(0);
-          consume(valid_of(k + s, ids[s]), buf[s]);
+          consume(valid_of(k + s, ids[s]), jw + kWaves * (k + s), buf[s]);
           if (ok16(ids[s])) first16 = min(first16, jw + kWaves * (k + s));
         }
       }
 #pragma unroll
       for (int s = 0; s < NB - 1; ++s)
         if (k + s < n) {
-          consume(valid_of(k + s, ids[s]), buf[s]);
+          consume(valid_of(k + s, ids[s]), jw + kWaves * (k + s), buf[s]);
           if (ok16(ids[s])) first16 = min(first16, jw + kWaves * (k + s));
         }
     } else {
       prep_q();
     }
     // the query fragments in natural element order, for the FP16 blocks
-    h8 qf[4];
+    h8 qf[NCT][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const h8 q = qp[kk];
-      if constexpr (KIND == kInt4)
-        qf[kk] = h8{q[0], q[2], q[4], q[6], q[1], q[3], q[5], q[7]};
-      else
-        qf[kk] = q;
-    }
+    for (int t = 0; t < NCT; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const h8 q = qp[t][kk];
+        if constexpr (KIND == kInt4)
+          qf[t][kk] = h8{q[0], q[2], q[4], q[6], q[1], q[3], q[5], q[7]};
+        else
+          qf[t][kk] = q;
+      }
 
     // the window's FP16 run [jt, jend): count FP16 ids backward from jend - 1
     int jt = jend;
@@ -518,12 +572,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       for (; k + 2 <= n16; k += 2) {
         ids[1] = table_entry(trow + j16(k + 1));
         fetch16(ids[1], bb[1]);
-        consume16(valid16(k, ids[0]), bb[0], qf);
+        consume16(valid16(k, ids[0]), j16(k), bb[0], qf);
         ids[0] = table_entry(trow + j16(k + 2));
         fetch16(ids[0], bb[0]);
-        consume16(valid16(k + 1, ids[1]), bb[1], qf);
+        consume16(valid16(k + 1, ids[1]), j16(k + 1), bb[1], qf);
       }
-      if (k < n16) consume16(valid16(k, ids[0]), bb[0], qf);
+      if (k < n16) consume16(valid16(k, ids[0]), j16(k), bb[0], qf);
     }
     // FP16 blocks before the window's run: a table read between a reserve of
     // several blocks and its settle holds the old window's FP16 blocks
@@ -536,21 +590,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       if (ok16(id)) {
         Buf16 one;
         fetch16(id, one);
-        consume16(L - 16 * j, one, qf);
+        consume16(L - 16 * j, j, one, qf);
       }
     }
 
     // ---- finish the piece: zero-point correction, merge ------------------------------
-    l_run = rows_sum(l_run);
-    if constexpr (KIND == kInt4) {
-      corr = rows_sum(corr);
 #pragma unroll
-      for (int T_ = 0; T_ < kNT; ++T_) o[T_] -= corr;
+    for (int t = 0; t < NCT; ++t) {
+      l_run[t] = rows_sum(l_run[t]);
+      if constexpr (KIND == kInt4) {
+        corr[t] = rows_sum(corr[t]);
+#pragma unroll
+        for (int T_ = 0; T_ < kNT; ++T_) o[t][T_] -= corr[t];
+      }
+      if (keep) stash_piece(sh, w, g, t * S + lcol, o[t], m_ref[t], l_run[t]);
     }
-    if (keep >= 0) stash_piece(sh, w, g, keep, o, m_ref, l_run);
-    if (a.defer_merge && jbeg == 0 && threadIdx.x == 0) write_job(a, um, b, h, h * um.TB + fb, nb);
-    finish_piece<_Float16>(a, sh, out_map(a), jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, h,
-                      h * um.TB + fb, nb, um);
+    if (a.defer_merge && jbeg == 0 && threadIdx.x == 0) write_job(a, um, b, hv, hv * um.TB + fb, nb);
+    finish_piece<_Float16>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, hv,
+                           hv * um.TB + fb, nb, um);
     pos += jend - jbeg;
     first = false;
   }
@@ -570,32 +627,48 @@ int quant_nb() {
   return (v == 2 || v == 3 || v == 4 || v == 6) ? v : 3;
 }
 
-template <int KIND, int NB, int NG>
+// Verify steps and prefill chunks: prefetch depth 3 with one column tile,
+// 2 with two (their accumulators take the registers of a buffer).
+template <int NCT>
+constexpr int kVerifyNB = NCT == 1 ? 3 : 2;
+
+template <int KIND, int NB, int NG, int NCT, bool CAUSAL>
 int occ_of() {
   int n = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_quant<KIND, NB, NG>,
-                                                                     kWaves * 64, 0);
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &n, decode_split_quant<KIND, NB, NG, NCT, CAUSAL>, kWaves * 64, 0);
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 
+// nct: 0 = decode, else the verify kernel with that many column tiles
 template <int KIND, int NG>
-int occ_kind() {
+int occ_kind(int nct) {
+  if (nct == 1) return occ_of<KIND, kVerifyNB<1>, NG, 1, true>();
+  if (nct == 2) return occ_of<KIND, kVerifyNB<2>, NG, 2, true>();
   switch (quant_nb<NG>()) {
-    case 3: return occ_of<KIND, 3, NG>();
-    case 4: return occ_of<KIND, 4, NG>();
-    case 6: return occ_of<KIND, 6, NG>();
-    default: return occ_of<KIND, 2, NG>();
+    case 3: return occ_of<KIND, 3, NG, 1, false>();
+    case 4: return occ_of<KIND, 4, NG, 1, false>();
+    case 6: return occ_of<KIND, 6, NG, 1, false>();
+    default: return occ_of<KIND, 2, NG, 1, false>();
   }
 }
 
 template <int KIND, int NG>
 void launch_kind(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.max_splits)), block(kWaves * 64);
+  if (a.n_query > 1) {  // verify step / prefill chunk: logical columns of a segment
+    const int cols = a.col_slices > 1 ? a.slice_cols : a.n_query * (a.n_q_heads / a.pool.n_kv_heads);
+    if (cols * NG <= 16)
+      hipLaunchKernelGGL((decode_split_quant<KIND, kVerifyNB<1>, NG, 1, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_split_quant<KIND, kVerifyNB<2>, NG, 2, true>), grid, block, 0, s, a);
+    return;
+  }
   switch (quant_nb<NG>()) {
-    case 3: hipLaunchKernelGGL((decode_split_quant<KIND, 3, NG>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_quant<KIND, 4, NG>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((decode_split_quant<KIND, 6, NG>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_split_quant<KIND, 2, NG>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_split_quant<KIND, 3, NG, 1, false>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_quant<KIND, 4, NG, 1, false>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((decode_split_quant<KIND, 6, NG, 1, false>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_split_quant<KIND, 2, NG, 1, false>), grid, block, 0, s, a); break;
   }
 }
 
@@ -604,17 +677,18 @@ int groups_of(int32_t kv_dtype, int32_t group_size) {
   return kv_dtype == kInt4 && group_size > 0 ? kD / group_size : 1;
 }
 
-int occupancy_quant(int32_t kv_dtype, int32_t group_size) {
-  static int cache[3][7] = {};  // [INT4 NG = 1, INT4 NG = 2, FP8][prefetch depth]
+// nct: 0 for decode, else the verify kernel's column tiles (1 or 2).
+int occupancy_quant(int32_t kv_dtype, int32_t group_size, int nct) {
+  static int cache[3][3][7] = {};  // [INT4 NG = 1, INT4 NG = 2, FP8][nct][prefetch depth]
   const int ng = groups_of(kv_dtype, group_size);
   const int i = kv_dtype == kInt4 ? (ng == 1 ? 0 : 1) : 2;
-  const int nb = i == 1 ? quant_nb<2>() : quant_nb<1>();
-  int& c = cache[i][nb];
+  const int nb = nct == 1 ? kVerifyNB<1> : nct == 2 ? kVerifyNB<2> : i == 1 ? quant_nb<2>() : quant_nb<1>();
+  int& c = cache[i][nct][nb];
   if (c == 0) {
     switch (i) {
-      case 0: c = occ_kind<kInt4, 1>(); break;
-      case 1: c = occ_kind<kInt4, 2>(); break;
-      default: c = occ_kind<kFp8, 1>(); break;
+      case 0: c = occ_kind<kInt4, 1>(nct); break;
+      case 1: c = occ_kind<kInt4, 2>(nct); break;
+      default: c = occ_kind<kFp8, 1>(nct); break;
     }
   }
   return c;

@@ -47,6 +47,7 @@ struct DecodeArgs {
   // (b, h * col_slices + s) of 32 (query, head) columns each; 1 = one
   // segment of all n_query * G columns
   int32_t col_slices;
+  int32_t slice_cols;    // (query, head) columns of a column slice when col_slices > 1
   float scale_log2;      // softmax scale * log2(e): scores live in the log2 domain
   void* out;
   float* ws_o;           // [batch][n_q_heads][max_splits][head_dim] partial sums

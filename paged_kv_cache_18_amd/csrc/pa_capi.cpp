@@ -132,7 +132,8 @@ struct Plan {
   int32_t split_blocks, max_splits, kernel;
   int32_t unit_blocks, static_permille;  // the cut of the matrix-core kernels
   int32_t defer_merge;                   // split segments merged by a second launch
-  int32_t col_slices;                    // matrix-core kernels: 32-column slices per (seq, kv head)
+  int32_t col_slices;                    // matrix-core kernels: column slices per (seq, kv head)
+  int32_t slice_cols;                    // (query, head) columns of a slice
   size_t ws_bytes;      // bytes the call needs
   size_t ws_o_offset;   // byte offset of the partial sums
   size_t ws_ml_offset;  // float index (from ws_o) of the (max, sum) pairs
@@ -177,17 +178,21 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
   Plan pl{};
   const int32_t G = n_q_heads / d.n_kv_heads;
   const int32_t ncol = n_query * G;  // output columns per (sequence, kv head)
-  // more than 32 (query, head) columns (a long verify step, a prefill chunk):
-  // slices of 32 columns, each its own segment of the work list
-  const int32_t nsl = n_query > 1 && ncol > 32 ? (ncol + 31) / 32 : 1;
-  const int32_t seg_cols = nsl > 1 ? 32 : ncol;
   const bool mfma_ok = (d.kv_dtype == pa::kBF16 || d.kv_dtype == pa::kF16) &&
                        q_dtype == d.kv_dtype && d.head_dim == 128 && G <= 16 && d.num_sink_blocks == 0;
   // INT4 groups of 128 or 64 dims: the matrix-core B operand's 16 columns
-  // hold every query head of the KV head once per group
+  // hold every logical column once per group (16 / groups of them per tile);
+  // decode needs one tile for the G query heads, a verify step or prefill
+  // chunk takes two tiles and slices beyond them
   const int32_t ngroups = d.kv_dtype == pa::kInt4 ? d.head_dim / d.group_size : 1;
   const bool quant_ok = (d.kv_dtype == pa::kInt4 || d.kv_dtype == pa::kFp8) && q_dtype == pa::kF16 &&
-                        d.head_dim == 128 && ngroups <= 2 && ngroups * G <= 16 && n_query == 1;
+                        d.head_dim == 128 && ngroups <= 2 && (n_query > 1 || ngroups * G <= 16);
+  // more (query, head) columns than two tiles hold (a long verify step, a
+  // prefill chunk): slices of that many columns, each its own segment of the
+  // work list -- 32 for 16-bit pools, 32 / groups for quantized ones
+  const int32_t slice = mfma_ok ? 32 : 32 / ngroups;
+  const int32_t nsl = n_query > 1 && ncol > slice ? (ncol + slice - 1) / slice : 1;
+  const int32_t seg_cols = nsl > 1 ? slice : ncol;
   const char* force = std::getenv("PA_DECODE_KERNEL");  // "generic" forces the VALU kernel
   const bool generic = force && std::strcmp(force, "generic") == 0;
   pl.kernel = generic ? pa::kKernGeneric
@@ -199,7 +204,8 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
   const int64_t nb = (int64_t(max_seq_len) + 15) / 16;
   if (pl.kernel != pa::kKernGeneric) {
     // Fixed chunks of the flattened list; two partial slots per workgroup.
-    pl.col_slices = pl.kernel == pa::kKernMfma16 ? nsl : 1;
+    pl.col_slices = nsl;
+    pl.slice_cols = slice;
     const int64_t w = flat_upper(batch, d.n_kv_heads, max_seq_len) * pl.col_slices;
     if (w >= (int64_t(1) << 31) - 4096) fail(pa::kInvalidArg, "batch * n_kv_heads * blocks too large");
     int32_t c = env_int("PA_SPLIT_BLOCKS", 0);  // fixed chunk size (tuning/tests)
@@ -217,7 +223,8 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
       int per_cu = env_int("PA_WG_PER_CU", 0);  // tuning knob; default: resident slots
       if (per_cu <= 0) {
         per_cu = pa::decode_split_occupancy(pl.kernel, d.kv_dtype,
-                                            n_query == 1 ? 0 : seg_cols <= 16 ? 1 : 2, d.group_size);
+                                            n_query == 1 ? 0 : seg_cols * ngroups <= 16 ? 1 : 2,
+                                            d.group_size);
         per_cu = std::min(per_cu, kDecodePerCu);
       }
       pl.max_splits = int32_t(std::max<int64_t>(
@@ -358,6 +365,7 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     a.static_permille = pl.static_permille;
     a.defer_merge = pl.defer_merge;
     a.col_slices = std::max(pl.col_slices, 1);
+    a.slice_cols = pl.slice_cols;
     a.split_blocks = pl.split_blocks;
     a.max_splits = pl.max_splits;
     a.kernel = pl.kernel;

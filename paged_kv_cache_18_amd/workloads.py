@@ -303,6 +303,9 @@ def by_name(name, **kw):
         "shared-prefix": shared_prefix,
         "shared-prefix-partial": lambda **k: shared_prefix(prefix=1992, **k),
         "spec-verify": llama3_8b,   # the same batch, scored by a verify step
+        # the mixed-precision sequence scored by a verify step (gamma = 5)
+        "spec-verify-int4": lambda **k: mixed_precision(kv="int4", **k),
+        "spec-verify-window": lambda **k: mixed_precision(kv="int4", group=64, window=128, **k),
         "llama3-8b-bs8": lambda **k: llama3_8b(block_size=8, **k),
         "llama3-8b-bs32": lambda **k: llama3_8b(block_size=32, **k),
         # the pages' own scheme: FP16 sink block and last-128-token window, INT4 g = 64

@@ -520,8 +520,91 @@ def test_verify_generic_matches_oracle(kvdt):
         wl = W.from_lengths([2, 6, 40, 700], 32, 8, 128, kvdt, seed=96,
                             group=128 if kvdt == "int4" else 0, sink=True, outliers=True)
         nq, odt = 6, "f16"
-    _, out = run_verify(wl, nq)
+    _, out = run_verify(wl, nq, env={"PA_DECODE_KERNEL": "generic"})
     assert_close(out, expected_verify(wl, nq), odt, f"verify generic {kvdt}")
+
+
+QV_SHAPES = [(32, 8, 6), (16, 8, 2), (64, 8, 4), (8, 8, 6), (32, 8, 1)]
+
+
+@pytest.mark.parametrize("kvdt,group", [("int4", 128), ("int4", 64), ("fp8", 0)])
+@pytest.mark.parametrize("shape", range(len(QV_SHAPES)))
+def test_quantized_verify_matrix_core(kvdt, group, shape):
+    """Verify steps on INT4/FP8 pools with an FP16 sink on the quantized
+    matrix-core kernel: (query, head) columns in one tile, two tiles, or
+    slices of two tiles (INT4 groups of 64 hold each column once per group,
+    so 24 columns make two slices), causal per column, lengths around the
+    block edges and below n_query; matches the oracle and the generic
+    kernel."""
+    from _ref import expected_verify
+    hq, hkv, nq = QV_SHAPES[shape]
+    wl = W.from_lengths(VERIFY_LENS, hq, hkv, 128, kvdt, seed=93 + shape + group, group=group,
+                        sink=True, outliers=True)
+    ref = expected_verify(wl, nq)
+    _, out = run_verify(wl, nq)
+    assert_close(out, ref, "f16", f"quant verify {kvdt} g{group} {hq}/{hkv} nq={nq}")
+    if shape == 0:
+        _, outg = run_verify(wl, nq, env={"PA_DECODE_KERNEL": "generic"})
+        assert_close(outg, ref, "f16", f"generic verify {kvdt} g{group}")
+
+
+@pytest.mark.parametrize("name", ["spec-verify-int4", "spec-verify-window"])
+def test_full_quantized_spec_verify_every_row(name):
+    """The pages' headline combination at full size: one 65,536 (+64)-token
+    sequence with an FP16 sink (and, for the window scheme, INT4 groups of 64
+    and the last-128-token FP16 window) scored by a gamma = 5 verify step:
+    all 6 x 32 rows against the oracle."""
+    from _ref import expected_verify
+    wl = W.by_name(name)
+    _, out = run_verify(wl, 6)
+    assert np.all(np.isfinite(out))
+    err = assert_close(out, expected_verify(wl, 6), "f16", name)
+    log(f"[gpu] {name} every row max |out - rn(oracle)| {err:.3g}")
+
+
+@pytest.mark.parametrize("kvdt,group", [("int4", 128), ("int4", 64), ("fp8", 0)])
+@pytest.mark.parametrize("qenv", [{"PA_SPLIT_BLOCKS": "1"}, {"PA_SPLIT_BLOCKS": "3"},
+                                  {"PA_FUSE_MAX_PIECES": "1"}, QUEUE_ENVS[0]])
+def test_quantized_verify_split_and_merge_modes(kvdt, group, qenv):
+    from _ref import expected_verify
+    wl = W.from_lengths(VERIFY_LENS, 32, 8, 128, kvdt, seed=99, group=group, sink=True)
+    _, out_a = run_verify(wl, 6, env=qenv)
+    _, out_b = run_verify(wl, 6, env=qenv)
+    assert np.array_equal(out_a, out_b), f"{kvdt} {qenv}: not deterministic"
+    assert_close(out_a, expected_verify(wl, 6), "f16", f"quant verify {kvdt} g{group} {qenv}")
+
+
+@pytest.mark.parametrize("kvdt,group", [("int4", 128), ("int4", 64), ("fp8", 0)])
+def test_quantized_verify_one_query_is_decode(kvdt, group):
+    wl = W.from_lengths([300, 17, 1, 1000], 32, 8, 128, kvdt, seed=98, group=group, sink=True)
+    kv, out_d, t, l = run(wl)
+    q = torch.from_numpy(wl.q()).to(torch.float16).to(DEV)[:, None]
+    tdev, ldev, _, _ = kv.device_tables()
+    out = torch.empty_like(q)
+    ml = int(l.max())
+    need = B.pa_verify_workspace_bytes(kv.pool, wl.batch, wl.n_q_heads, 1, ml)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV)
+    B.pa_verify_attention(q, kv.pool, tdev, ldev, wl.batch, wl.n_q_heads, 1, "f16", tdev.shape[1], ml,
+                          wl.scale, out, ws, ws.numel(), kv.stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(out[:, 0].double().cpu().numpy(), out_d)
+
+
+@pytest.mark.parametrize("kvdt,group", [("int4", 128), ("int4", 64), ("fp8", 0)])
+def test_quantized_prefill_chunks_match_oracle(kvdt, group):
+    """Prefill chunks of a quantized pool (sink + INT4/FP8 body): 120 and
+    37 queries per sequence, so 480 and 148 (query, head) columns in slices
+    of two tiles, causal over the cached prefix and the chunk."""
+    lengths = [360, 277]
+    base = W.chunked_prefill(seed=154, lengths=lengths, chunk=120)
+    wl = W.from_lengths(lengths, 32, 8, 128, kvdt, seed=154, group=group, sink=True, outliers=True)
+    wl.ops = [op for op in base.ops]
+    wl.extra["chunk"] = 120
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    for k, n, seqs in ((1, 120, [0, 1]), (2, 37, [1])):
+        out = prefill_chunk_gpu(kv, wl, k, n, seqs)
+        assert_close(out, expected_prefill_chunk(wl, k, n, seqs), "f16", f"{kvdt} chunk {k} n={n}")
 
 
 @pytest.mark.parametrize("qenv", [{"PA_SPLIT_BLOCKS": "1"}, {"PA_SPLIT_BLOCKS": "3"},
