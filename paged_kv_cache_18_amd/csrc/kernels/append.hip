@@ -21,6 +21,28 @@ namespace {
 
 constexpr int kWaves = 4;  // waves per workgroup
 
+// Min / max over the 64 lanes of a wave (all lanes active), every lane gets
+// the result: DPP moves inside each 16-lane row (quad swaps, then the half-row
+// and row mirrors), then the gfx950 row swaps across the four rows -- all in
+// registers, no LDS round trip.  Exact in any order.
+template <int CTRL>
+__device__ inline float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <bool MAX>
+__device__ inline float wave_extreme(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+  x = op(x, dpp_move<0xB1>(x));   // quad [1,0,3,2]
+  x = op(x, dpp_move<0x4E>(x));   // quad [2,3,0,1]
+  x = op(x, dpp_move<0x141>(x));  // row half mirror
+  x = op(x, dpp_move<0x140>(x));  // row mirror
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Quantize one (token t, kv head h, K-or-V) vector of a body block `id` and
 // store codes, scales and zeros: lane l holds dims 2k, 2k+1 for
 // k = l + 64*m (valid where has[m]).  Inputs are first rounded to fp16.
@@ -40,7 +62,7 @@ __device__ inline void quantize_store(const PoolDev& p, int id, int t, int h, in
 #pragma unroll
     for (int m = 0; m < MP; ++m)
       if (has[m]) amax = fmaxf(amax, fmaxf(fabsf(x[m][0]), fabsf(x[m][1])));
-    amax = wave_max(amax);
+    amax = wave_extreme<true>(amax);
     uint16_t sb = f32_to_f16_bits(__fdiv_rn(amax, 448.0f));
     float s = f16_bits_to_f32(sb);
     if (s == 0.f) {
@@ -84,8 +106,8 @@ __device__ inline void quantize_store(const PoolDev& p, int id, int t, int h, in
         mx = fmaxf(mx, fmaxf(x[m][0], x[m][1]));
       }
     }
-    mn = wave_min(mn);
-    mx = wave_max(mx);
+    mn = wave_extreme<false>(mn);
+    mx = wave_extreme<true>(mx);
     uint16_t sb = f32_to_f16_bits(__fdiv_rn(__fsub_rn(mx, mn), 15.0f));
     float s = f16_bits_to_f32(sb);
     if (s == 0.f) {
@@ -132,12 +154,8 @@ __global__ __launch_bounds__(kWaves * 64) void append_kv_kernel(PoolDev p, const
   const long tok = th / H;
   const int h = int(th % H);
   if (tok >= n) return;
-  const int slot = slots[tok];
-  if (slot < 0) return;
-  const int bs = p.block_size;  // 16; 8 or 32 for raw 16-bit pools
-  const int id = slot / bs, t = slot % bs;
-  if (id >= N + p.num_sink_blocks) return;
-
+  // the token's values and its slot are loaded together (the values do not
+  // depend on the slot: one memory round trip instead of two)
   const void* src = kind ? vin : kin;
   const size_t base = (size_t(tok) * H + h) * D;
   const int npairs = D >> 1;
@@ -150,6 +168,11 @@ __global__ __launch_bounds__(kWaves * 64) void append_kv_kernel(PoolDev p, const
     x[m][0] = has[m] ? load_as_f32(src, base + 2 * k, in_dt) : 0.f;
     x[m][1] = has[m] ? load_as_f32(src, base + 2 * k + 1, in_dt) : 0.f;
   }
+  const int slot = slots[tok];
+  if (slot < 0) return;
+  const int bs = p.block_size;  // 16; 8 or 32 for raw 16-bit pools
+  const int id = slot / bs, t = slot % bs;
+  if (id >= N + p.num_sink_blocks) return;
 
   // ---- FP16 sink arena and raw bodies: plain stores --------------------------
   const bool sink = id >= N;

@@ -75,6 +75,15 @@ struct Mfma<_Float16> {
   }
 };
 
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wave's LDS operations (not for its vector-memory loads, which stay in
+// flight across it), and keeps LDS accesses on their side of it.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // A block-table entry at a wave-uniform index, read through the scalar
 // (constant) cache: the tables are read-only for the whole call.  A plain
 // load becomes a vector load here (the kernels store to other buffers), and
@@ -599,13 +608,16 @@ __device__ inline void stash_piece(SH& sh, int w, int g, int col, const f32x4 (&
 // `slot` of unit `unit`, counted on the segment's arrival counter; the
 // completing arrival merges the segment (unless the merge launch will).  S =
 // the segment's start position, nb its blocks.  Ends with a barrier (LDS is
-// reused by the next piece).
+// reused by the next piece).  Its barriers wait on LDS only, so loads a wave
+// issued for its next piece keep flying through the merge; the one exchange
+// through memory (a partial read by the completing arrival) waits for this
+// workgroup's stores explicitly before the arrival counts.
 template <typename TO, class SH>
 __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& om, bool complete,
                                     int slot, int unit, int b, int h, int S, int nb,
                                     const Units& um) {
   const int NC = om.ncol();
-  __syncthreads();
+  lds_barrier();
   TO* out = static_cast<TO*>(a.out);
   for (int idx = threadIdx.x; idx < NC * kD; idx += kWaves * 64) {
     const int hc = idx / kD, d = idx % kD;
@@ -635,14 +647,14 @@ __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& o
     const int c0 = um.unit_of(S);
     const int np = um.unit_of(S + nb - 1) - c0 + 1;
     wait_stores();  // this workgroup's partial is complete before its arrival counts
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x == 0) sh.last = arrive(a, c0, np) ? 1 : 0;
-    __syncthreads();
+    lds_barrier();
     if (sh.last)
       merge_segment<TO>(a, sh, om, b, h, c0, S != um.start(c0), np,
                         unsigned(um.total()) * 2u * unsigned(NC), 0, NC);
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 }  // namespace dec
