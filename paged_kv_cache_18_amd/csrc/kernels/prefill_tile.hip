@@ -10,23 +10,35 @@
 //
 // A chunk has many queries per KV block (n_query x G columns per KV head), so
 // the work is a dense product and the design point differs from decode: a
-// workgroup of eight waves owns 128 (query, head) columns of one (sequence,
-// KV head) -- one 16-column tile per wave -- and streams every block that its
-// columns can see through LDS once for all eight.  Each wave moves an eighth
-// of the block (one 1 KiB chunk of K or of V, 16 bytes per lane) from HBM
-// straight into a three-slot LDS ring (global_load_lds_dwordx4: no register
-// staging); after a barrier every wave reads the whole K and V^T of the block
-// in matrix-core operand order.  Two blocks are in flight while one is
-// consumed.  Small waves (one tile) keep four of them per SIMD to hide each
-// other's matrix-core and softmax latencies.  No split: a workgroup sees all
-// of its columns' tokens and writes the normalized rows itself.
+// workgroup of four waves owns 128 (query, head) columns of one (sequence,
+// KV head) -- 32 per wave -- and streams every block its columns can see
+// through LDS once for all four, two blocks (32 tokens) per step.  Each wave
+// moves one 4 KiB slab of the step (K or V of one block, 16 bytes per lane
+// per load) from HBM straight into a three-slot LDS ring
+// (global_load_lds_dwordx4: no register staging); two steps are in flight
+// while one is consumed.  No split: a workgroup sees all of its columns'
+// tokens and writes the normalized rows itself.
 //
-// Per block and wave the arithmetic is the decode kernel's (decode_mfma.hip):
-// S^T = K Q^T with v_mfma_f32_16x16x32 per tile, the causal mask per column,
-// the online softmax in the log2 domain with a lazily moved reference, the
-// weights split into a 16-bit high part and residual, and O^T += V^T P^T per
-// 16-dim row tile with both parts in one v_mfma_f32_16x16x32.
+// Per step and wave, on v_mfma_f32_32x32x16 (32 tokens x 32 columns):
+//   S^T = K Q^T, 8 products over the 128 dimensions.  A = K: lane l reads the
+//     16-byte chunk of token l % 32, dimensions 8 (l / 32) + 16 kk, which the
+//     pool's K layout stores whole; B = Q^T from registers.  The result gives
+//     lane l column l % 32 and 16 tokens, 8 (i / 4) + 4 (l / 32) + i % 4, so a
+//     column's max or sum is 16 values in the lane plus one swap with lane
+//     l ^ 32.
+//   The causal mask (only for steps that reach past the wave's first column's
+//     limit), the online softmax in the log2 domain with a lazily moved
+//     reference, the weights split into a 16-bit high part and residual.
+//   O^T += V^T P^T per 32-dimension tile, block by block, high part then
+//     residual.  The score layout is the B operand as it stands: slot
+//     8 (l / 32) + e of block t's product is the lane's score i = 8t + e, i.e.
+//     token 16t + 8 (e / 4) + 4 (l / 32) + e % 4, and A = V^T takes the same
+//     token order: lane (h = l / 32, m = l % 32) reads tokens 4h..4h+3 and
+//     8+4h..8+4h+3 of dimension 8 (m % 16) + 2u + m / 16 (tile u), two 8-byte
+//     pieces of the pool's V layout.
 #include "decode_common.hpp"
+
+#include <type_traits>
 
 namespace pa {
 
@@ -43,20 +55,75 @@ __device__ inline void load_lds16(const void* src, void* lds) {
 #endif
 }
 
-constexpr int kPrefillWaves = 8;
-constexpr int kPrefillCols = 16 * kPrefillWaves;  // (query, head) columns per workgroup
-constexpr int kSlotElems = 2 * 16 * kD;  // one block's K and V slabs
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+// c + A B on 32x32x16: lane l holds A[l % 32][8 (l / 32) .. + 7] and
+// B[8 (l / 32) .. + 7][l % 32]; element i of the result is
+// C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
+template <typename T>
+struct Mma32;
+template <>
+struct Mma32<__bf16> {
+  typedef __bf16 v8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+  static __device__ inline f32x16 run(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mma32<_Float16> {
+  typedef _Float16 v8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+  static __device__ inline f32x16 run(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// the two values of lanes l and l ^ 32 (one swap of the wave's halves)
+__device__ inline float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// p0, p1 (weights of two consecutive B-operand slots e, e + 1) as a 16-bit
+// high part and the residual: p = hi + lo up to the residual's rounding.
+// bf16: hi is p with the low 16 bits cut (the upper halves of both words
+// in one byte permute), lo = p - hi exact in fp32, then rounded.
+template <typename T, typename V8>
+__device__ inline void split2(float p0, float p1, V8& hi, V8& lo, int e) {
+  if constexpr (std::is_same<T, __bf16>::value) {
+    const uint32_t h0 = __float_as_uint(p0) & 0xFFFF0000u, h1 = __float_as_uint(p1) & 0xFFFF0000u;
+    const uint32_t hp = __builtin_amdgcn_perm(h1, h0, 0x07060302u);
+    hi[e] = __builtin_bit_cast(__bf16, uint16_t(hp));
+    hi[e + 1] = __builtin_bit_cast(__bf16, uint16_t(hp >> 16));
+    lo[e] = T(p0 - __uint_as_float(h0));
+    lo[e + 1] = T(p1 - __uint_as_float(h1));
+  } else {
+    const T a = T(p0), b = T(p1);
+    hi[e] = a;
+    hi[e + 1] = b;
+    lo[e] = T(p0 - float(a));
+    lo[e + 1] = T(p1 - float(b));
+  }
+}
+
+constexpr int kPrefillWaves = 4;
+constexpr int kWaveCols = 32;
+constexpr int kPrefillCols = kWaveCols * kPrefillWaves;  // (query, head) columns per workgroup
+constexpr int kSlab = 16 * kD;                            // elements of one block's K or V slab
+constexpr int kStepElems = 4 * kSlab;                     // K of both blocks, then V of both
 
 template <typename T>
-__global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void prefill_tile_kernel(
+__global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_tile_kernel(
     DecodeArgs a, int ngrp) {
-  typedef typename Mfma<T>::v8 v8;
-  typedef typename Mfma<T>::v4 v4;
-  __shared__ __attribute__((aligned(16))) T ring[3][kSlotElems];
+  typedef typename Mma32<T>::v8 v8;
+  __shared__ __attribute__((aligned(16))) T ring[3][kStepElems];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int g = lane >> 4, c = lane & 15;
+  const int hh = lane >> 5, n = lane & 31;
   const PoolDev& p = a.pool;
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H, nq = a.n_query, N = p.num_blocks;
   const int ncols = nq * G;
@@ -79,141 +146,190 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
   const int32_t* trow = a.tables + size_t(b) * a.max_blocks_per_seq;
   const T* kbase = reinterpret_cast<const T*>(p.base + p.off[kArrK]);
   const T* vbase = reinterpret_cast<const T*>(p.base + p.off[kArrV]);
-  const float sl2 = a.scale_log2;
   T* out = static_cast<T*>(a.out);
 
-  // this wave's column col0 + c: query col / G, head h*G + col % G
-  const int col0 = grp * kPrefillCols + 16 * w;
-  const int col = col0 + c;
+  // this lane's column col0 + n: query col / G, head h*G + col % G
+  const int col0 = grp * kPrefillCols + kWaveCols * w;
+  const int col = col0 + n;
   const bool colok = col < ncols;
   const int qi = colok ? col / G : 0, gi = colok ? col % G : 0;
   const size_t orow = (size_t(b) * nq + qi) * Hq + size_t(h) * G + gi;
   const int lim = colok ? L - nq + qi : -1;
-  v8 qf[4];
+  // x = s * scale; a negative scale runs as |scale| on -q (exact), so the
+  // max of the raw scores scales to the max of x
+  const float sl2 = fabsf(a.scale_log2);
+  const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  v8 qf[8];
   {
-    const T* qp = static_cast<const T*>(a.q) + orow * kD + 8 * g;
+    const T* qp = static_cast<const T*>(a.q) + orow * kD + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[kk] = colok ? *reinterpret_cast<const v8*>(qp + 32 * kk) : v8{};
+    for (int kk = 0; kk < 8; ++kk) {
+      u32x4 d = colok ? *reinterpret_cast<const u32x4*>(qp + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+      d ^= qflip;
+      qf[kk] = __builtin_bit_cast(v8, d);
+    }
   }
   // tokens the group's last column sees bound the blocks streamed
   const int last = min(ncols, (grp + 1) * kPrefillCols) - 1;
   const int seen = max(0, min(L, L - nq + last / G + 1));
   const int nblk = (seen + 15) >> 4;
+  const int nstep = (nblk + 1) >> 1;
   const bool active = col0 < ncols;  // wave-uniform: the wave has a column to compute
+  // the wave's first column sees the fewest tokens: a step wholly within its
+  // limit needs no mask (and holds no token at or past L)
+  const int minlim = L - nq + col0 / G;
 
-  f32x4 o[kNT];
+  f32x16 o[4];
 #pragma unroll
-  for (int T_ = 0; T_ < kNT; ++T_) o[T_] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 4; ++u) o[u] = f32x16{};
   float m_ref = -__builtin_inff(), l_run = 0.f;
 
-  // this wave's eighth of block j into LDS slot `slot`: K chunk w (waves
-  // 0..3) or V chunk w - 4 (waves 4..7), lane l's 16 bytes at l * 16 of the
-  // chunk; a slot holds K then V, so chunk w lands at w * 512 elements.  One
-  // load, always issued, so the wait counts below are fixed.  Past the last
-  // block it re-reads that block into a slot nobody reads.
-  const T* cbase = w < 4 ? kbase : vbase;
-  auto load = [&](int j, int slot) {
-    const int id_ = table_entry(trow + min(j, nblk - 1));
-    const size_t slab = (size_t(id_ >= 0 && id_ < N ? id_ : 0) * H + h) * (16 * kD);
-    load_lds16(cbase + slab + size_t(w & 3) * 512 + size_t(lane) * 8, &ring[slot][w * 512]);
+  // this wave's slab of step s_ into LDS slot `slot`: K (waves 0, 1) or V
+  // (waves 2, 3) of block 2 s_ + (w & 1), four 1 KiB loads, lane l's 16 bytes
+  // at l * 16 of each.  Always issued, so the wait counts below are fixed:
+  // past the last block it re-reads that block (masked where it is read).
+  const T* cbase = w < 2 ? kbase : vbase;
+  auto load = [&](int s_, int slot) {
+    const int id_ = table_entry(trow + min(2 * s_ + (w & 1), nblk - 1));
+    const T* src = cbase + (size_t(id_ >= 0 && id_ < N ? id_ : 0) * H + h) * kSlab + lane * 8;
+    T* dst = &ring[slot][w * kSlab];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) load_lds16(src + k * 512, dst + k * 512);
   };
 
-  // block j from LDS slot `slot`: S^T, causal mask, online softmax, O^T += V^T P^T
-  auto consume = [&](int slot, int j) {
-    if (!active) return;
-    v8 kf[4], vf[4];
+  // LDS element offsets of this lane's operand chunks within a slot
+  const int kl = (n >> 4) * kSlab + (hh * 16 + (n & 15)) * 8;
+  const int vl = 2 * kSlab + ((hh * 16 + (n & 15)) * 2 + (n >> 4)) * 4;
+
+  // step s_ from LDS slot `slot`.  masked: the step reaches past the limit
+  // of the wave's first column (the causal diagonal, the last step); TAIL:
+  // the last step, which may hold tokens at or past L (a short block, a
+  // re-read one).
+  auto consume = [&](int slot, int s_, bool masked, auto tailc) {
+    constexpr bool TAIL = decltype(tailc)::value;
+    const T* base = ring[slot];
+    f32x16 sc = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kf[kk] = *reinterpret_cast<const v8*>(&ring[slot][kk * 512 + lane * 8]);
+    for (int kk = 0; kk < 8; ++kk)
+      sc = Mma32<T>::run(*reinterpret_cast<const v8*>(base + kl + kk * 256), qf[kk], sc);
+
+    float x[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) vf[u] = *reinterpret_cast<const v8*>(&ring[slot][2048 + u * 512 + lane * 8]);
-    const int valid = min(16, L - 16 * j);
-    if (valid < 16) {
-      // unwritten tail slots may hold any bits (NaN too): zero them so a zero
-      // weight never meets one; each dword holds two tokens
-      const int t0 = 4 * g;
-      const uint32_t m01 = (t0 + 0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
-      const uint32_t m23 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+    for (int i = 0; i < 16; ++i) x[i] = sc[i];
+    if (masked) {
+      const int t0 = 32 * s_ + 4 * hh;  // token of score i: t0 + 8 (i / 4) + i % 4
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        u32x4 dw = __builtin_bit_cast(u32x4, vf[u]);
-        dw[0] &= m01;
-        dw[1] &= m23;
-        dw[2] &= m01;
-        dw[3] &= m23;
-        vf[u] = __builtin_bit_cast(v8, dw);
-      }
+      for (int i = 0; i < 16; ++i) x[i] = t0 + 8 * (i >> 2) + (i & 3) <= lim ? x[i] : -__builtin_inff();
     }
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    // NaN-propagating maximum (v_maximum3_f32): no input quieting, and no
+    // score is NaN here (a token past L is masked to -inf first)
+    float bm = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), x[2]);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) sc = Mfma<T>::qk(kf[kk], qf[kk], sc);
-    float x[4];
-    bool vis[4];
-    float bm = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * j + 4 * g + i;
-      vis[i] = 4 * g + i < valid && tok <= lim;
-      x[i] = vis[i] ? sc[i] * sl2 : -__builtin_inff();
-      bm = fmaxf(bm, x[i]);
-    }
-    bm = rows_max(bm);
-    // the reference moves only when a block's max passes it by more than 8
-    // (weights stay <= 2^8); numerator and denominator share it
+    for (int i = 3; i < 15; i += 2)
+      bm = __builtin_elementwise_maximum(__builtin_elementwise_maximum(bm, x[i]), x[i + 1]);
+    bm = halves_max(__builtin_elementwise_maximum(bm, x[15])) * sl2;
+    // the reference moves only when a step's max passes it by more than 8
+    // (weights stay <= 2^8); numerator and denominator share it.  A column
+    // that does not move keeps its sums as they are (alpha 1: with nothing
+    // seen yet, m_ref - m_ref would be -inf - -inf).
     const bool move = bm > m_ref + 8.f;
     if (__any(move)) {
-      const float m_new = move ? bm : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - bm) : 1.f;
+      m_ref = move ? bm : m_ref;
       l_run *= alpha;
 #pragma unroll
-      for (int T_ = 0; T_ < kNT; ++T_) o[T_] *= alpha;
-      m_ref = m_new;
+      for (int u = 0; u < 4; ++u) o[u] *= alpha;
     }
-    v4 phi, plo;
+    // a column with nothing seen yet has m_ref = -inf and only masked
+    // scores: against the most negative float they still weigh exp2(-inf) = 0
+    const float mu = fmaxf(m_ref, -__FLT_MAX__);
+    v8 phi[2], plo[2];
+    float ps[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pw = vis[i] ? __builtin_amdgcn_exp2f(x[i] - m_ref) : 0.f;
-      l_run += pw;
-      phi[i] = T(pw);
-      plo[i] = T(pw - float(phi[i]));
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sl2, -mu));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i + 1], sl2, -mu));
+      ps[i] = p0;
+      ps[i + 1] = p1;
+      split2<T>(p0, p1, phi[i >> 3], plo[i >> 3], i & 7);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int st = 1; st < 16; st *= 2)
 #pragma unroll
-      for (int par = 0; par < 2; ++par) {
-        const v4 vt = {vf[u][4 * par + 0], vf[u][4 * par + 1], vf[u][4 * par + 2], vf[u][4 * par + 3]};
-        o[2 * u + par] = Mfma<T>::pv2(vt, phi, plo, o[2 * u + par]);
+      for (int i = 0; i < 16; i += 2 * st) ps[i] += ps[i + st];
+    l_run += ps[0];
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      v8 vf[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const T* vp = base + vl + t * kSlab + u * 512;
+        typedef T v4 __attribute__((__vector_size__(4 * sizeof(T))));
+        const v4 p0 = *reinterpret_cast<const v4*>(vp);
+        const v4 p1 = *reinterpret_cast<const v4*>(vp + 256);
+        vf[u] = v8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       }
+      if constexpr (TAIL) {
+        // V of tokens at or past L is zeroed: unwritten slots may hold any
+        // bits (NaN too) and a zero weight must not meet one.  Piece 0 of
+        // block t holds tokens 16t + 4hh + 0..3, piece 1 tokens
+        // 16t + 8 + 4hh + 0..3; each dword two tokens.
+        u32x4 vm;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int tk = 32 * s_ + 16 * t + 8 * (d >> 1) + 4 * hh + 2 * (d & 1);
+          vm[d] = (tk < L ? 0x0000FFFFu : 0u) | (tk + 1 < L ? 0xFFFF0000u : 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) vf[u] = __builtin_bit_cast(v8, __builtin_bit_cast(u32x4, vf[u]) & vm);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = Mma32<T>::run(vf[u], phi[t], o[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = Mma32<T>::run(vf[u], plo[t], o[u]);
     }
   };
 
-  if (nblk > 0) {
-    // block j lives in slot j % 3.  At the top of step j this wave's loads of
-    // blocks j and j + 1 are outstanding (one each): waiting down to one
-    // leaves block j + 1 in flight; the barrier then publishes every wave's
-    // eighth of block j and frees the slot of block j - 1 for block j + 2.
+  if (nstep > 0) {
+    // step s lives in slot s % 3.  At the top of step s this wave's loads of
+    // steps s and s + 1 are outstanding (four each): waiting down to four
+    // leaves step s + 1 in flight; the barrier then publishes every wave's
+    // slab of step s and frees the slot of step s - 1 for step s + 2.  Only
+    // the last step can hold tokens at or past L (the blocks before it end
+    // below the tokens the group sees): it runs on its own, masked.
     load(0, 0);
     load(1, 1);
-    for (int j = 0; j < nblk; ++j) {
-      asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    for (int s_ = 0; s_ < nstep - 1; ++s_) {
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       __syncthreads();
-      load(j + 2, (j + 2) % 3);
-      consume(j % 3, j);
+      load(s_ + 2, (s_ + 2) % 3);
+      if (active) consume(s_ % 3, s_, 32 * s_ + 31 > minlim, std::false_type{});
     }
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    __syncthreads();
+    if (active) consume((nstep - 1) % 3, nstep - 1, true, std::true_type{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
-  // normalized row: lane (g, c) holds dims 32g + 8i + T of its column
-  const float l = rows_sum(l_run);
+  // normalized column: lane (hh, n) holds, of tile u, element i = dimension
+  // 8 r + 2u + p with r = 4hh + i % 4 + 8 ((i / 4) % 2), p = i / 8 -- for each
+  // of its eight rows r, the 8 dimensions 8r .. 8r + 7
+  const float l = halves_sum(l_run);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (colok) {
-    T* op = out + orow * kD + 32 * g;
+    T* op = out + orow * kD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v8 v;
+    for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-      for (int T_ = 0; T_ < kNT; ++T_) v[T_] = T(o[T_][i] * inv);
-      *reinterpret_cast<v8*>(op + 8 * i) = v;
-    }
+      for (int j = 0; j < 4; ++j) {
+        v8 v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int par = 0; par < 2; ++par) v[2 * u + par] = T(o[u][4 * rr + j + 8 * par] * inv);
+        *reinterpret_cast<v8*>(op + 8 * (4 * hh + j + 8 * rr)) = v;
+      }
   }
 }
 
