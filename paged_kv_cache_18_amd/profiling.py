@@ -156,7 +156,8 @@ def summarize(cfg, trace_dir, fetch_dir, write_dir, bench_json, commands, src_ha
         f"launches, so the gaps between launches count too): "
         f"{entry['bench_split_avg_us_events']} µs. "
         f"Bench line of the trace run: ms_per_step {bench['ms_per_step']}, value "
-        f"{bench['value']} GB/s, roofline achieved {bench['roofline']['achieved']} GB/s.",
+        f"{bench['value']} GB/s, roofline achieved {bench['roofline']['achieved']} "
+        f"{bench['roofline']['unit']}.",
         "",
     ]
     if plain_json:
