@@ -399,8 +399,9 @@ pa_status pa_verify_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t 
  *  INT4 (groups of 128 or 64) or FP8 pools with D = 128, whose codes are
  *  dequantized in registers ([8GB] section 5; the section 8 benchmark's
  *  "Paged + Sink-INT4 KV + Speculative" combination).  Columns beyond two
- *  tiles of 16 (32 columns; 16 for INT4 groups of 64, which hold each
- *  column once per group) are cut into slices that read the blocks again. */
+ *  tiles of 16 (32 columns; for INT4 groups of 64, which hold each column
+ *  once per group, one tile of 8) are cut into slices that read the blocks
+ *  again. */
 pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
                               const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
                               int32_t n_query, int32_t q_dtype, int32_t max_blocks_per_seq,

@@ -187,10 +187,18 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
   const int32_t ngroups = d.kv_dtype == pa::kInt4 ? d.head_dim / d.group_size : 1;
   const bool quant_ok = (d.kv_dtype == pa::kInt4 || d.kv_dtype == pa::kFp8) && q_dtype == pa::kF16 &&
                         d.head_dim == 128 && ngroups <= 2 && (n_query > 1 || ngroups * G <= 16);
-  // more (query, head) columns than two tiles hold (a long verify step, a
+  // more (query, head) columns than a segment takes (a long verify step, a
   // prefill chunk): slices of that many columns, each its own segment of the
-  // work list -- 32 for 16-bit pools, 32 / groups for quantized ones
-  const int32_t slice = mfma_ok ? 32 : 32 / ngroups;
+  // work list -- 32 for 16-bit pools and INT4 groups of 128 / FP8 (two
+  // tiles), 8 for INT4 groups of 64 (one tile: the two-tile kernel of that
+  // group size holds more registers than a SIMD gives it, and its spills cost
+  // more than the extra pass over the cache a third slice makes -- the
+  // 6-query verify of 65,536 tokens: 73 us against 88)
+  int32_t slice = mfma_ok ? 32 : ngroups == 2 ? 8 : 32;
+  if (!mfma_ok) {  // tuning knob: quantized slice width, 1 .. 32 / groups
+    const int q = env_int("PA_QUANT_SLICE", 0);
+    if (q > 0) slice = std::min(q, 32 / ngroups);
+  }
   const int32_t nsl = n_query > 1 && ncol > slice ? (ncol + slice - 1) / slice : 1;
   const int32_t seg_cols = nsl > 1 ? slice : ncol;
   const char* force = std::getenv("PA_DECODE_KERNEL");  // "generic" forces the VALU kernel

@@ -532,10 +532,11 @@ QV_SHAPES = [(32, 8, 6), (16, 8, 2), (64, 8, 4), (8, 8, 6), (32, 8, 1)]
 def test_quantized_verify_matrix_core(kvdt, group, shape):
     """Verify steps on INT4/FP8 pools with an FP16 sink on the quantized
     matrix-core kernel: (query, head) columns in one tile, two tiles, or
-    slices of two tiles (INT4 groups of 64 hold each column once per group,
-    so 24 columns make two slices), causal per column, lengths around the
-    block edges and below n_query; matches the oracle and the generic
-    kernel."""
+    slices (two tiles; for INT4 groups of 64, which hold each column once per
+    group, one tile of 8 columns, so 24 columns make three slices -- and the
+    two-tile slices of 16 that the slice knob selects), causal per column,
+    lengths around the block edges and below n_query; matches the oracle and
+    the generic kernel."""
     from _ref import expected_verify
     hq, hkv, nq = QV_SHAPES[shape]
     wl = W.from_lengths(VERIFY_LENS, hq, hkv, 128, kvdt, seed=93 + shape + group, group=group,
@@ -546,6 +547,9 @@ def test_quantized_verify_matrix_core(kvdt, group, shape):
     if shape == 0:
         _, outg = run_verify(wl, nq, env={"PA_DECODE_KERNEL": "generic"})
         assert_close(outg, ref, "f16", f"generic verify {kvdt} g{group}")
+    if group == 64 and nq * hq // hkv > 8:
+        _, out16 = run_verify(wl, nq, env={"PA_QUANT_SLICE": "16"})
+        assert_close(out16, ref, "f16", f"quant verify g64 slices of 16 {hq}/{hkv} nq={nq}")
 
 
 @pytest.mark.parametrize("name", ["spec-verify-int4", "spec-verify-window"])
