@@ -168,8 +168,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
   const size_t orow = (size_t(b) * nq + qi) * Hq + size_t(h) * G + gi;
   const int lim = colok ? L - nq + qi : -1;
   // x = s * scale; a negative scale runs as |scale| on -q (exact), so the
-  // max of the raw scores scales to the max of x
-  const float sl2 = fabsf(a.scale_log2);
+  // max of the raw scores scales to the max of x.  A zero scale runs as the
+  // smallest normal float: every visible weight is still exp2(0) = 1 exactly,
+  // and a masked score stays -inf instead of becoming -inf * 0 = NaN.
+  const float sl2 = fmaxf(fabsf(a.scale_log2), __FLT_MIN__);
   const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   v8 qf[8];
   {

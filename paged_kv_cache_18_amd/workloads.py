@@ -68,6 +68,7 @@ class Workload:
     window_tokens: int = 0
     block_size: int = BLOCK       # tokens per pool block (8 and 32: raw 16-bit, D 128)
     extra: dict = field(default_factory=dict)
+    softmax_scale: float | None = None  # None: 1 / sqrt(head_dim)
 
     @property
     def batch(self):
@@ -75,7 +76,7 @@ class Workload:
 
     @property
     def scale(self):
-        return 1.0 / math.sqrt(self.head_dim)
+        return 1.0 / math.sqrt(self.head_dim) if self.softmax_scale is None else self.softmax_scale
 
     def q(self):
         return rng(self.seed, 3).standard_normal(

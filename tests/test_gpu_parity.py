@@ -846,6 +846,20 @@ def test_prefill_short_chunks(n):
     assert_close(out, expected_prefill_chunk(wl, 2, n, [0, 1, 2]), "bf16", f"prefill n={n}")
 
 
+@pytest.mark.parametrize("scale", [-0.0883883, 0.5, 0.0])
+def test_prefill_scale_signs(scale):
+    """The tile kernel with a negative softmax scale (run as |scale| on -q,
+    which must equal the plain definition), a large one (peaked weights) and
+    zero (uniform weights over each query's visible tokens), on a chunk whose
+    columns fill both column groups of a workgroup and end in a ragged one."""
+    wl = W.chunked_prefill(seed=155, lengths=[300, 280], chunk=100)
+    wl.softmax_scale = scale
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    out = prefill_chunk_gpu(kv, wl, 2, 80, [0, 1])
+    assert_close(out, expected_prefill_chunk(wl, 2, 80, [0, 1]), "bf16", f"prefill scale {scale}")
+
+
 def test_prefill_full_workload_last_chunk_sampled():
     """The bench's prefill workload (4 x 4,096 tokens, 512-token chunks): the
     last chunk's attention, 16 groups of 128 columns per KV head, checked on
