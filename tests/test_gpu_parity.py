@@ -846,6 +846,36 @@ def test_prefill_short_chunks(n):
     assert_close(out, expected_prefill_chunk(wl, 2, n, [0, 1, 2]), "bf16", f"prefill n={n}")
 
 
+def test_prefill_sixteen_heads_per_kv_head():
+    """G = 16 (128 q / 8 kv heads), the largest group the tile kernel takes:
+    a 70-query chunk is 1,120 columns, so a workgroup's 256 columns span 16
+    queries and the last one is short."""
+    wl = W.chunked_prefill(seed=156, lengths=[210, 140], chunk=70, n_q_heads=128, n_kv_heads=8)
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    out = prefill_chunk_gpu(kv, wl, 1, 70, [0, 1])
+    assert_close(out, expected_prefill_chunk(wl, 1, 70, [0, 1]), "bf16", "prefill G=16")
+
+
+def test_prefill_long_chunk_sampled():
+    """A 2,048-query chunk over a 2,560-token cache (8,192 columns per KV
+    head, 32 workgroups each): sampled (sequence, query) rows, among them the
+    first and last query."""
+    wl = W.chunked_prefill(seed=157, lengths=[2560], chunk=2048, n_q_heads=32, n_kv_heads=8)
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    out = prefill_chunk_gpu(kv, wl, 1, 512, [0])  # the second chunk: 512 queries over 2,560 tokens
+    assert_close(out, expected_prefill_chunk(wl, 1, 512, [0]), "bf16", "prefill 512 of 2,560")
+    out = prefill_chunk_gpu(kv, wl, 0, 2048, [0])
+    assert np.all(np.isfinite(out))
+    from _ref import cast64
+    q = cast64(wl.q_chunk(0, 2048), wl.q_dtype)
+    K, V, _ = stored_values(wl, 0)
+    for i in [0, 1, 255, 256, 1023, 2046, 2047]:
+        ref = AT.attention_one(q[0, i], K[:i + 1], V[:i + 1], wl.scale)
+        assert_close(out[0, i][None], ref[None], "bf16", f"prefill 2,048 row {i}")
+
+
 @pytest.mark.parametrize("scale", [-0.0883883, 0.5, 0.0])
 def test_prefill_scale_signs(scale):
     """The tile kernel with a negative softmax scale (run as |scale| on -q,
