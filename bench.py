@@ -15,7 +15,10 @@ INT4/FP8 bytes plus their fp16 scales) divided by the measured step time.
 its own launch durations, measured with HIP events on the launch stream;
 `roofline.traffic` is the HBM bytes rocprofv3 counted for one launch
 (profiles/hbm_traffic.json) over the same duration.  `stream_read_gbs` is a
-plain streaming read of the same byte count (the achievable rate).
+plain streaming read of the same byte count (the achievable rate);
+`paged_read` a plain read of exactly the slabs the attention reads, through
+the same tables (the paged access pattern without the arithmetic): its time,
+bytes (whole slabs), rate and the split launch's time over it.
 `cpu_baseline` times the CPU oracle (logical rebuild through the tables +
 float64 attention) on a bounded sample of the same batch.  `warm` and `cold`
 give the median / p10 / p90 of per-step HIP-event times, each step timed on
@@ -117,6 +120,22 @@ def algorithmic_bytes(wl, lens, tables):
         fp16 = np.asarray(row[:nb]) >= wl.num_blocks
         tok = np.minimum(16, L - 16 * np.arange(nb))
         total += int(tok[fp16].sum()) * raw + int(tok[~fp16].sum()) * per
+    return int(total)
+
+
+def paged_bytes(kv, wl, lens, tables):
+    """Bytes pa_paged_read reads: every block of each table up to its length,
+    whole slabs of every array of the block's arena, for every KV head."""
+    from paged_kv_cache_18_amd import binding as B
+    lay = B.pa_pool_layout(kv.pool)["slab_bytes"]
+    body = sum(lay.get(a, 0) for a in ("K", "V", "KS", "KZ", "VS", "VZ"))
+    sink = sum(lay.get(a, 0) for a in ("SK", "SV"))
+    total = 0
+    for row, L in zip(tables, lens):
+        ids = np.asarray(row[:-(-int(L) // wl.block_size)])
+        nb_body = int(((ids >= 0) & (ids < wl.num_blocks)).sum())
+        nb_sink = int(((ids >= wl.num_blocks) & (ids < wl.num_blocks + wl.num_sink_blocks)).sum())
+        total += (nb_body * body + nb_sink * sink) * wl.n_kv_heads
     return int(total)
 
 
@@ -345,6 +364,19 @@ def main():
     torch.cuda.synchronize()
     extra["stream_read_gbs"] = round(nread / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9, 1)
     del ceil_buf
+    # the paged read: the library's plain read of exactly the slabs this
+    # step's attention reads, through the same tables (the paged access
+    # pattern with none of the arithmetic); its bytes are whole slabs
+    B.pa_paged_read(kv.pool, tdev, ldev, wl.batch, tdev.shape[1], max_len, sink, sh)
+    c0.record(stream)
+    for _ in range(10):
+        B.pa_paged_read(kv.pool, tdev, ldev, wl.batch, tdev.shape[1], max_len, sink, sh)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    pr_us = c0.elapsed_time(c1) / 10 * 1e3
+    pbytes = paged_bytes(kv, wl, lens, t)
+    extra["paged_read"] = {"us": round(pr_us, 2), "bytes": pbytes, "gbs": round(pbytes / (pr_us * 1e-6) / 1e9, 1),
+                           "split_over_paged_read": round(split_avg * 1e3 / pr_us, 3)}
     if args.copy_calibration:
         a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)

@@ -453,6 +453,23 @@ pa_status pa_decode_split_blocks(const pa_pool* pool, int32_t batch, int32_t n_q
  * decode.  sink: device, >= 4 bytes, may be written.  Asynchronous on stream. */
 pa_status pa_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
+/* Measurement aid (not a step of the method): read, with no arithmetic,
+ * every slab a decode of this batch reads -- for each sequence, each block of
+ * its table up to its length (blocks of block_size tokens) and each KV head,
+ * the block's slab in every array of its arena (K and V; codes, scales and
+ * zeros of a quantized body; the FP16 arrays for sink-arena ids) -- with a
+ * plain grid-stride kernel: the paged read rate of exactly those bytes,
+ * reported beside the decode.  Table entries outside both arenas are
+ * skipped.  Arguments as for pa_decode_attention.  Head dim 128 pools only
+ * (16-bit of 8-, 16- or 32-token blocks, INT4, FP8); others give
+ * PA_ERR_UNSUPPORTED.
+ *  sink: device, >= 4 bytes, 4-byte aligned; receives sink[0] ^= the XOR of
+ *  every 32-bit word read (a check that the reads happened).
+ * Asynchronous on stream. */
+pa_status pa_paged_read(const pa_pool* pool, const int32_t* block_tables_dev, const int32_t* seq_lens_dev,
+                        int32_t batch, int32_t max_blocks_per_seq, int32_t max_seq_len, void* sink,
+                        void* stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 const char* pa_last_error(void);
 

@@ -82,6 +82,7 @@ _PROTOS = {
     "pa_decode_workspace_bytes": [vp, i32, i32, i32, C.POINTER(sz)],
     "pa_decode_split_blocks": [vp, i32, i32, i32, P32],
     "pa_stream_read": [vp, sz, vp, vp],
+    "pa_paged_read": [vp, P32, P32, i32, i32, i32, vp, vp],
     "pa_seq_settle": [vp, i32, vp, P32],
     "pa_decode_attention": _DECODE_ARGS,
     "pa_decode_attention_noalloc": [vp, vp, P32, P32, i32, i32, i32, i32, i32, f32, vp, vp],
@@ -409,6 +410,13 @@ def pa_prefill_attention(q, pool, tables_dev, lens_dev, batch, n_q_heads, chunk,
 def pa_stream_read(src, nbytes, sink, stream=None):
     """Measurement aid: stream-read nbytes of device memory at src."""
     _check(lib().pa_stream_read(_ptr(src), nbytes, _ptr(sink), _ptr(stream)))
+
+
+def pa_paged_read(pool, tables_dev, lens_dev, batch, max_blocks, max_seq_len, sink, stream=None):
+    """Measurement aid: read every slab a decode of this batch reads, with no
+    arithmetic; sink[0] ^= the XOR of every 32-bit word read."""
+    _check(lib().pa_paged_read(pool, _i32ptr(tables_dev), _i32ptr(lens_dev), batch, max_blocks,
+                               max_seq_len, _ptr(sink), _ptr(stream)))
 
 
 def pa_last_error():

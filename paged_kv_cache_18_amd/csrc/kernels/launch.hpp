@@ -89,4 +89,11 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 // Streaming read of `bytes` (a multiple of 16) at src with `grid` workgroups.
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, int grid, hipStream_t s);
 
+// Plain read of every slab a decode of the batch reads (through the tables);
+// sink[0] ^= the XOR of every 32-bit word read.  Head dim 128: 16-bit pools
+// of 8-, 16- or 32-token blocks, INT4 and FP8 pools (with their FP16 sinks).
+bool paged_read_supported(const PoolDev& p);
+hipError_t launch_paged_read(const PoolDev& p, const int32_t* tables, const int32_t* lens, int32_t batch,
+                             int32_t max_blocks, int32_t max_seq_len, void* sink, int grid, hipStream_t s);
+
 }  // namespace pa

@@ -812,6 +812,30 @@ pa_status pa_stream_read(const void* src, size_t bytes, void* sink, void* stream
   });
 }
 
+pa_status pa_paged_read(const pa_pool* pool, const int32_t* tables, const int32_t* lens, int32_t batch,
+                        int32_t max_blocks, int32_t max_seq_len, void* sink, void* stream) {
+  return guard([&] {
+    need_device(pool);
+    const pa::Desc& d = pool->core.desc();
+    if (batch < 0 || batch > 65535) fail(pa::kInvalidArg, "batch must be in [0, 65535]");
+    if (max_seq_len < 0) fail(pa::kInvalidArg, "negative max_seq_len");
+    if (max_blocks < 1) fail(pa::kInvalidArg, "max_blocks_per_seq must be >= 1");
+    if (int64_t(max_seq_len) > int64_t(max_blocks) * d.block_size)
+      fail(pa::kInvalidArg, "max_seq_len exceeds block_size * max_blocks_per_seq");
+    if (batch == 0) return;
+    need(tables, "block_tables_dev");
+    need(lens, "seq_lens_dev");
+    need(sink, "sink");
+    if (!pa::paged_read_supported(dev_view(pool)))
+      fail(pa::kUnsupported, "the paged read covers head_dim 128 pools (16-bit, INT4, FP8)");
+    if (int64_t(batch) * max_blocks * d.n_kv_heads >= (int64_t(1) << 31))
+      fail(pa::kUnsupported, "batch * max_blocks_per_seq * n_kv_heads too large for the paged read");
+    check_hip(pa::launch_paged_read(dev_view(pool), tables, lens, batch, max_blocks, max_seq_len, sink,
+                                    cu_count() * 2, static_cast<hipStream_t>(stream)),
+              "paged read launch");
+  });
+}
+
 const char* pa_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"
