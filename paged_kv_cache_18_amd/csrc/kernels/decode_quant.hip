@@ -13,10 +13,12 @@
 //   INT4  S[t] = sum_k s_tk * (sum_{d in k} q_d c_td - z_tk * sum_{d in k} q_d)
 //         O[d] = sum_t c_td (s_tk p_t) - sum_t z_tk s_tk p_t   (k = group of d)
 //   FP8   S[t] = s_t * sum_d q_d e(c_td),  O[d] = sum_t e(c_td) (s_t p_t)
-// The codes enter the fp16 matrix cores exactly: an INT4 nibble n becomes the
-// fp16 value n (0x6400|n is 1024+n, then an exact packed-fp16 subtract); an
-// E4M3 code goes through the hardware FP8->fp16 conversion with scale 1
-// (every E4M3 value is an fp16 value).  The weights
+// The codes enter the fp16 matrix cores exactly: an INT4 nibble n at bits 0..3
+// of a half is the fp16 subnormal n * 2^-24, at bits 4..7 the subnormal
+// 16n * 2^-24 (one AND per two codes; the matrix cores take subnormal fp16
+// operands exactly), and the powers of two are taken out again after the
+// products; an E4M3 code goes through the hardware FP8->fp16 conversion with
+// scale 1 (every E4M3 value is an fp16 value).  The weights
 // s_t p_t are split into an fp16 high part and residual (~22 bits).  The
 // softmax reference moves only when a block's max passes it by more than 2
 // (log2 units), so every weight is <= 4; the largest scales -- INT4
@@ -28,6 +30,7 @@
 // quantized blocks (2,176 B for INT4, 4,160 B for FP8 per (block, head)) are
 // prefetched NB-1 blocks ahead per wave.
 #include <cstdlib>
+#include <type_traits>
 
 #include "decode_common.hpp"
 
@@ -41,30 +44,37 @@ typedef _Float16 h8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef _Float16 h4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
 typedef _Float16 h2 __attribute__((__vector_size__(2 * sizeof(_Float16))));
 
-// INT4 codes to exact fp16 values.  A nibble n placed in the low mantissa
-// bits under 0x6400 reads as 1024 + n; one bit-select and one packed
-// subtract give n.  A nibble at mantissa bits 4..7 reads as 1024 + 16n, and
-// one packed fma, x/16 - 64, gives n (both steps exact in fp16).
-// nib4(x): the fp16 pairs of the nibbles at bits (s, s + 16), s = 0, 4, 8, 12.
-__device__ inline uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
-  return r;
-}
-__device__ inline uint32_t nib_lo(uint32_t x) {  // bits 0..3 and 16..19
-  const h2 v = __builtin_bit_cast(h2, and_or(x, 0x000F000Fu, 0x64006400u));
-  return __builtin_bit_cast(uint32_t, v - h2{_Float16(1024.f), _Float16(1024.f)});
-}
-__device__ inline uint32_t nib_hi(uint32_t x) {  // bits 4..7 and 20..23
-  const h2 v = __builtin_bit_cast(h2, and_or(x, 0x00F000F0u, 0x64006400u));
-  return __builtin_bit_cast(
-      uint32_t, __builtin_elementwise_fma(v, h2{_Float16(0.0625f), _Float16(0.0625f)},
-                                          h2{_Float16(-64.f), _Float16(-64.f)}));
-}
-__device__ inline u32x4 nib4(uint32_t x) {
+// INT4 codes to exact fp16 subnormals.  sub4(x): the half pairs of the
+// nibbles at bits (0, 16) and (8, 24) at scale 1 -- n reads as n * 2^-24 --
+// and at bits (4, 20) and (12, 28) at scale 16 -- n reads as 16n * 2^-24:
+// {n0 n4, 16 n1 16 n5, n2 n6, 16 n3 16 n7} (times 2^-24) for nibbles n0..n7.
+__device__ inline u32x4 sub4(uint32_t x) {
   const uint32_t y = x >> 8;
-  return u32x4{nib_lo(x), nib_hi(x), nib_lo(y), nib_hi(y)};
+  return u32x4{x & 0x000F000Fu, x & 0x00F000F0u, y & 0x000F000Fu, y & 0x00F000F0u};
 }
+constexpr float kSub = 16777216.f;  // 2^24: a nibble's subnormal is n / kSub
+
+// IEEE maximum (a NaN operand gives NaN) without the canonicalizing moves
+// fmaxf brings; the operands are scores, or -inf for tokens a column does
+// not see
+__device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ inline float rows_vmax(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// One (block, head) slab of a pool array as a buffer: its loads take the
+// slab's address from scalar registers and a 32-bit lane offset from a
+// vector register (no vector address arithmetic), and a load past the slab
+// reads zeros.
+typedef __amdgpu_buffer_rsrc_t Slab;
+__device__ inline Slab slab_rsrc(const uint8_t* p, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, int(bytes), kRsrcWord3);
+}
+__device__ inline u32x4 sload4(Slab r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+__device__ inline u32x2 sload2(Slab r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
 
 // Keep v in a register where it is computed: a select of it then stays a
 // select instead of becoming a branch around its computation.
@@ -117,17 +127,18 @@ struct Quant<kFp8, 1> {
   typedef BufF8 Buf;
 };
 
-// NW consecutive dwords at p (NW = 2: 8-byte aligned; 4, 8: 16-byte aligned)
+// NW consecutive dwords at offset off of slab r (NW = 2: 8-byte aligned; 4,
+// 8: 16-byte aligned)
 template <int NW>
-__device__ inline void load_words(const uint8_t* p, uint32_t (&d)[NW]) {
+__device__ inline void load_words(Slab r, uint32_t off, uint32_t (&d)[NW]) {
   if constexpr (NW == 2) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 v = sload2(r, off);
     d[0] = v[0];
     d[1] = v[1];
   } else {
 #pragma unroll
     for (int i = 0; i < NW / 4; ++i) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * i);
+      const u32x4 v = sload4(r, off + 16 * i);
 #pragma unroll
       for (int e = 0; e < 4; ++e) d[4 * i + e] = v[e];
     }
@@ -140,13 +151,33 @@ __device__ inline float half_at(const uint32_t (&m)[NW], int idx) {
   return (idx & 1) ? h_hi(m[idx >> 1]) : h_lo(m[idx >> 1]);
 }
 
-// Scale/zero of token i in group `sel` (a per-lane group index < NG).
+// f16(half HI of w) * a + c as one fp32 fma (one rounding); the compiler
+// makes it one mixed-precision fma that reads the fp16 operand in place.
+// Written as arithmetic, not inline assembly: the compiler then inserts the
+// wait a read of a transcendental result needs (as inline assembly the fma
+// read an exp2 result one instruction after it and took the old value).
+template <bool HI>
+__device__ inline float fma_h(uint32_t w, float a, float c) {
+  const h2 v = __builtin_bit_cast(h2, w);
+  return __builtin_fmaf(float(v[HI ? 1 : 0]), a, c);
+}
+
+// (scale or zero of token i in group `sel`, a per-lane group index < NG) * a
+// + c.  NG = 1: token i is half i & 1 of word i / 2; NG = 2: word i holds
+// groups (0, 1) of token i, rotated so that group sel is its low half.
 template <int NG>
-__device__ inline float half_sel(const uint32_t (&m)[2 * NG], int i, int sel) {
-  float v = half_at(m, i * NG);
-#pragma unroll
-  for (int k = 1; k < NG; ++k) v = sel == k ? half_at(m, i * NG + k) : v;
-  return v;
+__device__ inline float fma_meta(const uint32_t (&m)[2 * NG], int i, int sel, float a, float c) {
+  if constexpr (NG == 1) {
+    return (i & 1) ? fma_h<true>(m[i >> 1], a, c) : fma_h<false>(m[i >> 1], a, c);
+  } else {
+    static_assert(NG == 2, "one or two scale groups");
+    return fma_h<false>(__builtin_amdgcn_alignbit(m[i], m[i], uint32_t(sel) * 16u), a, c);
+  }
+}
+
+// RNE fp16 pair of (a, b) as one word
+__device__ inline uint32_t pk_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, h2{_Float16(a), _Float16(b)});
 }
 
 // NB = register buffers per wave (NB-1 blocks prefetched ahead).  NCT column
@@ -199,6 +230,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   int b = 0, fb = 0;
 
   const float sl2 = a.scale_log2;
+  const float slq = KIND == kInt4 ? sl2 * kSub : sl2;  // the body's score factor
+  // -1 that the compiler does not see as a constant: pv - hi stays one
+  // mixed-precision fma reading hi in place (as a subtraction it would
+  // convert hi on its own first)
+  const float neg1 = pin(-1.f);
   const uint8_t* base = p.base;
   const int32_t* trow = a.tables;
   int hv = 0, h = 0, L = 0;  // segment hv = h * nsl + column slice
@@ -221,8 +257,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   // softmax update of tile t for one block's 4 scores per lane; returns the
   // weights (0 for tokens the column does not see)
   auto softmax = [&](int t, const float (&x)[4], const bool (&vis)[4], float (&pw)[4]) {
-    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = rows_max(bm);
+    float bm = vmax(vmax(x[0], x[1]), vmax(x[2], x[3]));
+    bm = rows_vmax(bm);
     const bool move = bm > m_ref[t] + 2.f;
     if (__any(move)) {
       // a lane whose reference stays keeps its sums (factor 1): a column
@@ -244,37 +280,41 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   };
 
   // ---- body blocks ------------------------------------------------------------
+  // slab addresses in scalar registers; the lane offsets are 32-bit vector
+  // values computed once
+  const uint32_t lo16 = uint32_t(lane) * 16u, lo_meta = uint32_t(8 * NG * g);
   auto fetch = [&](int id, Buf& bf) {
     const size_t sid = size_t(ok(id) ? id : 0) * H + h;  // unconditional load
-    const uint8_t* kc = base + p.off[kArrK] + sid * p.slab[kArrK];
-    const uint8_t* vc = base + p.off[kArrV] + sid * p.slab[kArrV];
-    const uint8_t* ks = base + p.off[kArrKS] + sid * p.slab[kArrKS] + 8 * NG * g;
-    const uint8_t* vs = base + p.off[kArrVS] + sid * p.slab[kArrVS] + 8 * NG * g;
+    auto at = [&](int arr) { return slab_rsrc(base + p.off[arr] + sid * p.slab[arr], p.slab[arr]); };
     if constexpr (KIND == kInt4) {
-      bf.kc = *reinterpret_cast<const u32x4*>(kc + lane * 16);
-      bf.vc = *reinterpret_cast<const u32x4*>(vc + lane * 16);
-      load_words(ks, bf.ks);
-      load_words(base + p.off[kArrKZ] + sid * p.slab[kArrKZ] + 8 * NG * g, bf.kz);
-      load_words(vs, bf.vs);
-      load_words(base + p.off[kArrVZ] + sid * p.slab[kArrVZ] + 8 * NG * g, bf.vz);
+      bf.kc = sload4(at(kArrK), lo16);
+      bf.vc = sload4(at(kArrV), lo16);
+      load_words(at(kArrKS), lo_meta, bf.ks);
+      load_words(at(kArrKZ), lo_meta, bf.kz);
+      load_words(at(kArrVS), lo_meta, bf.vs);
+      load_words(at(kArrVZ), lo_meta, bf.vz);
     } else {
-      bf.kc0 = *reinterpret_cast<const u32x4*>(kc + lane * 16);
-      bf.kc1 = *reinterpret_cast<const u32x4*>(kc + 1024 + lane * 16);
-      bf.vc0 = *reinterpret_cast<const u32x4*>(vc + lane * 16);
-      bf.vc1 = *reinterpret_cast<const u32x4*>(vc + 1024 + lane * 16);
-      load_words(ks, bf.ks);
-      load_words(vs, bf.vs);
+      const Slab kc = at(kArrK), vc = at(kArrV);
+      bf.kc0 = sload4(kc, lo16);
+      bf.kc1 = sload4(kc, 1024 + lo16);
+      bf.vc0 = sload4(vc, lo16);
+      bf.vc1 = sload4(vc, 1024 + lo16);
+      load_words(at(kArrKS), lo_meta, bf.ks);
+      load_words(at(kArrVS), lo_meta, bf.vs);
     }
   };
 
-  // jl: the block's logical index (causal limits)
-  auto consume = [&](int valid, int jl, const Buf& bf) {
+  // jl: the block's logical index (causal limits).  full (a std::bool_constant):
+  // every token of the block is visible -- a whole block of a decode step --
+  // so no token needs a select.
+  auto consume = [&](auto full, int valid, int jl, const Buf& bf) {
+    constexpr bool FULL = decltype(full)::value;
     // K codes as exact fp16 operand fragments, shared by the tiles
     u32x4 kav[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if constexpr (KIND == kInt4) {
-        kav[kk] = nib4(bf.kc[kk]);
+        kav[kk] = sub4(bf.kc[kk]);
       } else {
         const u32x4 u = kk < 2 ? bf.kc0 : bf.kc1;
         const uint32_t x0 = u[(kk & 1) * 2], x1 = u[(kk & 1) * 2 + 1];
@@ -287,9 +327,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     for (int t = 0; t < NCT; ++t) {
       bool vis[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vis[i] = visible(t, valid, jl, i);
+      for (int i = 0; i < 4; ++i) vis[i] = FULL || visible(t, valid, jl, i);
       float x[4];
       if constexpr (KIND == kInt4) {
+        // acc = 2^-24 sum_d q_d c_d per group (the query carries the 1/16 of
+        // the scale-16 codes), qs = 2^-24 sum_d q_d, slq = 2^24 sl2
         f32x4 acc[NG];
 #pragma unroll
         for (int k = 0; k < NG; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -302,7 +344,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
 #pragma unroll
           for (int k = 0; k < NG; ++k)
             sc += half_at(bf.ks, i * NG + k) * (acc[k][i] - half_at(bf.kz, i * NG + k) * qs[t][k]);
-          const float xs = pin(sc * sl2);
+          const float xs = pin(sc * slq);
           x[i] = vis[i] ? xs : -__builtin_inff();
         }
       } else {
@@ -311,7 +353,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
         for (int kk = 0; kk < 4; ++kk) acc = MF::qk(__builtin_bit_cast(h8, kav[kk]), qp[t][kk], acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float xs = pin(half_at(bf.ks, i) * acc[i] * sl2);
+          const float xs = pin(half_at(bf.ks, i) * acc[i] * slq);
           x[i] = vis[i] ? xs : -__builtin_inff();
         }
       }
@@ -322,34 +364,42 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float w_ = pin(half_sel<NG>(bf.vs, i, gsel) * pw[i]);
+        const float w_ = pin(fma_meta<NG>(bf.vs, i, gsel, pw[i], 0.f));
         pv[i] = vis[i] ? w_ : 0.f;
       }
       if constexpr (KIND == kInt4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float z_ = pin(half_sel<NG>(bf.vz, i, gsel) * pv[i]);
-          corr[t] += vis[i] ? z_ : 0.f;
+          if constexpr (FULL) {
+            corr[t] = fma_meta<NG>(bf.vz, i, gsel, pv[i], corr[t]);
+          } else {
+            const float z_ = pin(fma_meta<NG>(bf.vz, i, gsel, pv[i], 0.f));
+            corr[t] += vis[i] ? z_ : 0.f;
+          }
         }
       }
       // B operand in the token order of the code pairs: INT4 (t0, t2),
-      // (t1, t3); FP8 natural
+      // (t1, t3); FP8 natural.  hi = fp16(pv), lo = fp16(pv - hi) (pv - hi
+      // is exact in fp32)
       const int ord[4] = {0, KIND == kInt4 ? 2 : 1, KIND == kInt4 ? 1 : 2, 3};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bhi[t][e] = _Float16(pv[ord[e]]);
-        blo[t][e] = _Float16(pv[ord[e]] - float(bhi[t][e]));
-      }
+      const uint32_t h01 = pk_f16(pv[ord[0]], pv[ord[1]]), h23 = pk_f16(pv[ord[2]], pv[ord[3]]);
+      const uint32_t l01 = pk_f16(fma_h<false>(h01, neg1, pv[ord[0]]), fma_h<true>(h01, neg1, pv[ord[1]]));
+      const uint32_t l23 = pk_f16(fma_h<false>(h23, neg1, pv[ord[2]]), fma_h<true>(h23, neg1, pv[ord[3]]));
+      bhi[t] = __builtin_bit_cast(h4, u32x2{h01, h23});
+      blo[t] = __builtin_bit_cast(h4, u32x2{l01, l23});
     }
     // FP8: zero the bytes of tail tokens (unwritten slots may hold NaN codes)
     const int t0 = 4 * g;
-    const uint32_t vmask = (t0 + 0 < valid ? 0x000000FFu : 0u) | (t0 + 1 < valid ? 0x0000FF00u : 0u) |
-                           (t0 + 2 < valid ? 0x00FF0000u : 0u) | (t0 + 3 < valid ? 0xFF000000u : 0u);
+    const uint32_t vmask = FULL ? ~0u
+                                : (t0 + 0 < valid ? 0x000000FFu : 0u) | (t0 + 1 < valid ? 0x0000FF00u : 0u) |
+                                      (t0 + 2 < valid ? 0x00FF0000u : 0u) | (t0 + 3 < valid ? 0xFF000000u : 0u);
 #pragma unroll
     for (int T_ = 0; T_ < kNT; ++T_) {
       uint32_t lo, hi;
       if constexpr (KIND == kInt4) {
-        const u32x4 nv = nib4(bf.vc[T_ >> 1]);
+        // output tile T holds dim 8r + T: even tiles take the scale-1 codes,
+        // odd tiles the scale-16 ones
+        const u32x4 nv = sub4(bf.vc[T_ >> 1]);
         const int par = T_ & 1;
         lo = nv[par];      // bits 4par: tokens (t0, t2)
         hi = nv[2 + par];  // bits 8 + 4par: tokens (t1, t3)
@@ -364,7 +414,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       for (int t = 0; t < NCT; ++t) o[t][T_] = MF::pv2(at, bhi[t], blo[t], o[t][T_]);
     }
   };
-
   // ---- FP16 blocks of the sink/window arena (raw fp16 in operand order) ----------
   auto fetch16 = [&](int id, Buf16& bf) {
     const size_t sid = size_t(ok16(id) ? id - N : 0) * H + h;  // unconditional load
@@ -441,16 +490,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     // 32kk + 8g + 0..7): loaded here, and permuted into the order in which
     // the code conversion delivers the K elements (and summed per group)
     // once the body's first blocks are in flight
+    auto load_q = [&](h8 (&dst)[NCT][4]) {
+#pragma unroll
+      for (int t = 0; t < NCT; ++t) {
+        const int lc = t * S + lcol;
+        const _Float16* qn = static_cast<const _Float16*>(a.q) + om.row(b, hv, min(lc, ncol - 1)) * kD + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          dst[t][kk] = lc < ncol ? *reinterpret_cast<const h8*>(qn + 32 * kk) : h8{};
+      }
+    };
     h8 qraw[NCT][4];
+    load_q(qraw);
 #pragma unroll
-    for (int t = 0; t < NCT; ++t) {
-      const int lc = t * S + lcol;
-      const _Float16* qn = static_cast<const _Float16*>(a.q) + om.row(b, hv, min(lc, ncol - 1)) * kD + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        qraw[t][kk] = lc < ncol ? *reinterpret_cast<const h8*>(qn + 32 * kk) : h8{};
-      lim[t] = L - nq + om.gcol(hv, min(lc, ncol - 1)) / G;
-    }
+    for (int t = 0; t < NCT; ++t) lim[t] = L - nq + om.gcol(hv, min(t * S + lcol, ncol - 1)) / G;
     auto prep_q = [&]() {
 #pragma unroll
       for (int t = 0; t < NCT; ++t) {
@@ -461,13 +514,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
           const h8 q = qraw[t][kk];
 #pragma unroll
           for (int e = 0; e < 8; ++e) qs[t][kk * NG / 4] += float(q[e]);
+          // INT4: the order of sub4's halves, the scale-16 codes' dims / 16
+          // (exact down to |q| = 2^-10; below, one rounding of a subnormal)
+          const _Float16 r = _Float16(0.0625f);
           if constexpr (KIND == kInt4)
-            qp[t][kk] = h8{q[0], q[4], q[1], q[5], q[2], q[6], q[3], q[7]};
+            qp[t][kk] = h8{q[0], q[4], q[1] * r, q[5] * r, q[2], q[6], q[3] * r, q[7] * r};
           else
             qp[t][kk] = q;
         }
 #pragma unroll
-        for (int k = 0; k < NG; ++k) qs[t][k] = rows_sum(qs[t][k]);
+        for (int k = 0; k < NG; ++k) qs[t][k] = rows_sum(qs[t][k]) * (KIND == kInt4 ? 1.f / kSub : 1.f);
       }
     };
 #pragma unroll
@@ -502,7 +558,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       __builtin_amdgcn_sched_barrier(0);
       prep_q();
       int k = 0;
-      for (; k + NB <= n; k += NB) {
+      // The loop's blocks are whole: a sequence's partial last block is this
+      // wave's last block when the wave holds it, and is left to the blocks
+      // after the loop.  A decode step's loop therefore takes the instance
+      // without per-token selects, and skips an FP16 or out-of-range entry
+      // with a scalar branch (it gets no weight); a verify step or prefill
+      // chunk, whose columns see different lengths, takes the general one.
+      const bool tail = !CAUSAL && (L & 15) != 0 && jw + kWaves * (n - 1) == ((L + 15) >> 4) - 1;
+      const int nl = tail ? n - 1 : n;
+      for (; k + NB <= nl; k += NB) {
         prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
 #pragma unroll
         for (int s = 0; s < NB; ++s) {
@@ -513,31 +577,42 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
           // no instruction of the block's product may move above the next
           // block's loads (it would wait for data still in flight)
           __builtin_amdgcn_sched_barrier(0);
-          consume(valid_of(k + s, ids[s]), jw + kWaves * (k + s), buf[s]);
+          if constexpr (CAUSAL) {
+            consume(std::false_type{}, valid_of(k + s, ids[s]), jw + kWaves * (k + s), buf[s]);
+          } else {
+            if (ok(ids[s])) consume(std::true_type{}, 16, jw + kWaves * (k + s), buf[s]);
+          }
           if (ok16(ids[s])) first16 = min(first16, jw + kWaves * (k + s));
         }
       }
+      // the rest: at most NB blocks, the first NB - 1 of them fetched (the
+      // last one, block k + NB - 1 = nid, only after a partial block kept
+      // out of the loop)
 #pragma unroll
-      for (int s = 0; s < NB - 1; ++s)
+      for (int s = 0; s < NB; ++s)
         if (k + s < n) {
-          consume(valid_of(k + s, ids[s]), jw + kWaves * (k + s), buf[s]);
+          if (s == NB - 1) {
+            ids[s] = nid;
+            fetch(nid, buf[s]);
+          }
+          consume(std::false_type{}, valid_of(k + s, ids[s]), jw + kWaves * (k + s), buf[s]);
           if (ok16(ids[s])) first16 = min(first16, jw + kWaves * (k + s));
         }
     } else {
       prep_q();
     }
-    // the query fragments in natural element order, for the FP16 blocks
-    h8 qf[NCT][4];
+    // INT4: the body read the codes at 2^-24 (even output tiles) and 16 *
+    // 2^-24 (odd ones): the sums back to scale, less the zero-point term
+    // (the FP16 blocks below add to the scaled sums)
+    if constexpr (KIND == kInt4) {
 #pragma unroll
-    for (int t = 0; t < NCT; ++t)
+      for (int t = 0; t < NCT; ++t) {
+        const float cz = rows_sum(corr[t]);
+        corr[t] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const h8 q = qp[t][kk];
-        if constexpr (KIND == kInt4)
-          qf[t][kk] = h8{q[0], q[2], q[4], q[6], q[1], q[3], q[5], q[7]};
-        else
-          qf[t][kk] = q;
+        for (int T_ = 0; T_ < kNT; ++T_) o[t][T_] = o[t][T_] * ((T_ & 1) ? kSub / 16.f : kSub) - cz;
       }
+    }
 
     // the window's FP16 run [jt, jend): count FP16 ids backward from jend - 1
     int jt = jend;
@@ -558,6 +633,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     const int ns = max(0, min(jend, SP) - jbeg);
     const int nf = ns + (jend - jt);
     const int n16 = w < nf ? (nf - w + kWaves - 1) / kWaves : 0;
+    // the query fragments in natural element order, for the FP16 blocks (the
+    // INT4 body permuted and scaled its copy: loaded again)
+    h8 qf[NCT][4];
+    if constexpr (KIND == kInt4) {
+      if (n16 > 0 || first16 < jt) load_q(qf);
+    } else {
+#pragma unroll
+      for (int t = 0; t < NCT; ++t)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qf[t][kk] = qp[t][kk];
+    }
     if (n16 > 0) {
       auto j16 = [&](int k) {
         const int i = w + kWaves * min(k, n16 - 1);
@@ -594,15 +680,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       }
     }
 
-    // ---- finish the piece: zero-point correction, merge ------------------------------
+    // ---- finish the piece: merge -------------------------------------------------------
 #pragma unroll
     for (int t = 0; t < NCT; ++t) {
       l_run[t] = rows_sum(l_run[t]);
-      if constexpr (KIND == kInt4) {
-        corr[t] = rows_sum(corr[t]);
-#pragma unroll
-        for (int T_ = 0; T_ < kNT; ++T_) o[t][T_] -= corr[t];
-      }
       if (keep) stash_piece(sh, w, g, t * S + lcol, o[t], m_ref[t], l_run[t]);
     }
     if (a.defer_merge && jbeg == 0 && threadIdx.x == 0) write_job(a, um, b, hv, hv * um.TB + fb, nb);
