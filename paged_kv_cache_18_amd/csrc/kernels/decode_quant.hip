@@ -558,36 +558,46 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       __builtin_amdgcn_sched_barrier(0);
       prep_q();
       int k = 0;
-      // The loop's blocks are whole: a sequence's partial last block is this
-      // wave's last block when the wave holds it, and is left to the blocks
-      // after the loop.  A decode step's loop therefore takes the instance
-      // without per-token selects, and skips an FP16 or out-of-range entry
-      // with a scalar branch (it gets no weight); a verify step or prefill
-      // chunk, whose columns see different lengths, takes the general one.
-      const bool tail = !CAUSAL && (L & 15) != 0 && jw + kWaves * (n - 1) == ((L + 15) >> 4) - 1;
-      const int nl = tail ? n - 1 : n;
+      // Whole blocks -- every token written and seen by every column -- take
+      // the instance without per-token selects; an FP16 or out-of-range entry
+      // among them is skipped with a scalar branch (it gets no weight).  In
+      // a decode step every block but a sequence's partial last one is whole;
+      // in a verify step of at most 16 queries every block but the one or two
+      // its queries' positions reach into.  Either way a wave holds at most
+      // one other block, its last, which is left to the blocks after the
+      // loops.  A longer prefill chunk takes the general instance throughout.
+      auto step = [&](auto full, int s) {
+        const int nxt = (s + NB - 1) % NB;
+        ids[nxt] = nid;
+        nid = id_of(k + s + NB);
+        fetch(ids[nxt], buf[nxt]);
+        // no instruction of the block's product may move above the next
+        // block's loads (it would wait for data still in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(full)::value) {
+          if (ok(ids[s])) consume(full, 16, jw + kWaves * (k + s), buf[s]);
+        } else {
+          consume(full, valid_of(k + s, ids[s]), jw + kWaves * (k + s), buf[s]);
+        }
+        if (ok16(ids[s])) first16 = min(first16, jw + kWaves * (k + s));
+      };
+      const int seen = CAUSAL ? L - nq + 1 : L;  // positions every column sees
+      const int nl = (!CAUSAL || nq <= 16) ? (16 * (jw + kWaves * (n - 1) + 1) <= seen ? n : n - 1) : 0;
       for (; k + NB <= nl; k += NB) {
         prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
 #pragma unroll
-        for (int s = 0; s < NB; ++s) {
-          const int nxt = (s + NB - 1) % NB;
-          ids[nxt] = nid;
-          nid = id_of(k + s + NB);
-          fetch(ids[nxt], buf[nxt]);
-          // no instruction of the block's product may move above the next
-          // block's loads (it would wait for data still in flight)
-          __builtin_amdgcn_sched_barrier(0);
-          if constexpr (CAUSAL) {
-            consume(std::false_type{}, valid_of(k + s, ids[s]), jw + kWaves * (k + s), buf[s]);
-          } else {
-            if (ok(ids[s])) consume(std::true_type{}, 16, jw + kWaves * (k + s), buf[s]);
-          }
-          if (ok16(ids[s])) first16 = min(first16, jw + kWaves * (k + s));
+        for (int s = 0; s < NB; ++s) step(std::true_type{}, s);
+      }
+      if constexpr (CAUSAL) {
+        for (; k + NB <= n; k += NB) {
+          prio_from_progress(a, pos - pos0 + kWaves * k, prio_span);
+#pragma unroll
+          for (int s = 0; s < NB; ++s) step(std::false_type{}, s);
         }
       }
       // the rest: at most NB blocks, the first NB - 1 of them fetched (the
-      // last one, block k + NB - 1 = nid, only after a partial block kept
-      // out of the loop)
+      // last one, block k + NB - 1 = nid, only after a block kept out of the
+      // whole-block loop)
 #pragma unroll
       for (int s = 0; s < NB; ++s)
         if (k + s < n) {
