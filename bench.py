@@ -2,10 +2,12 @@
 
 One step = one decode step of one attention layer for the whole batch:
   1. append each sequence's newest K/V token into its slot (quantize-on-write
-     for INT4/FP8 pools),
+     for INT4/FP8 pools; with --fused-step, on bf16/fp16 pools, the split
+     kernel writes it itself: pa_decode_step),
   2. split-K decode over all cached tokens (gathered through block tables),
      including the log-sum-exp merge of split segments (fused into the
-     matrix-core kernels; a second launch for the generic kernel).
+     matrix-core kernels; a second launch for the generic kernel and for
+     segments split over many workgroups).
 Inputs are seeded synthetic data already resident in HBM when timing starts.
 
 `value` is KV GB/s: the algorithmic K/V bytes one decode step must read
@@ -193,6 +195,9 @@ def main():
     ap.add_argument("--identity-tables", action="store_true",
                     help="physical blocks in logical order (free order 0..N-1): the contiguous "
                          "comparator for the paging overhead")
+    ap.add_argument("--fused-step", action="store_true",
+                    help="decode steps through pa_decode_step (the 16-bit split kernel writes the "
+                         "new tokens itself)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -248,8 +253,17 @@ def main():
     vargs = (q, kv.pool, tdev, ldev, wl.batch, wl.n_q_heads, nq, wl.q_dtype, tdev.shape[1],
              max_len, wl.scale, out, ws, ws.numel(), sh)
 
+    # --fused-step: the step through pa_decode_step, whose split kernel writes
+    # the new tokens itself on a 16-bit pool with inputs of the pool's dtype
+    # (one launch fewer per step, a longer split launch); the roofline then
+    # times that launch
+    fused = (args.fused_step and nq == 1 and wl.kv_dtype in ("bf16", "f16")
+             and wl.in_dtype == wl.kv_dtype)
+
     def attn_split():   # the dominant launch (verify / prefill: one launch at these shapes)
-        if nq == 1:
+        if fused:
+            B.pa_decode_step_split(q, k_new, v_new, wl.in_dtype, *dargs[1:])
+        elif nq == 1:
             B.pa_decode_split(*dargs)
         elif args.config == "prefill-chunk":
             B.pa_prefill_attention(*vargs)
@@ -261,7 +275,8 @@ def main():
             B.pa_decode_combine(*dargs)
 
     def step():
-        B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, n_new, sh)
+        if not fused:
+            B.pa_append_kv(kv.pool, k_new, v_new, wl.in_dtype, slots_dev, n_new, sh)
         attn_split()
         attn_rest()
 
@@ -331,6 +346,7 @@ def main():
 
     # warm: a spin kernel (no memory traffic) ahead of each step
     warm_step, warm_split = one_by_one(args.steps, lambda: torch.cuda._sleep(300_000))
+    extra["fused_step"] = fused
     extra["warm"] = {"step_us": dist(warm_step), "split_us": dist(warm_split)}
     if args.cold_steps > 0:
         # evict the caches by *reading* 512 MiB (more than the 256 MB

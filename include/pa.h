@@ -374,6 +374,38 @@ pa_status pa_decode_attention_noalloc(const void* q, const pa_pool* pool,
                                       int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
                                       void* out, void* stream);
 
+/* One decode step: write every sequence's newest token, then decode attention
+ * over the cache that includes it ([8GB] section 5 flowchart: the new token's
+ * K/V go through the write path -- FP16 for sink and window blocks, the fused
+ * quantizer for an INT4/FP8 body -- before the attention reads the cache
+ * through the block tables; [PR8] 8.1).  Equivalent to pa_append_kv of token
+ * seq_lens_dev[b] - 1 of each sequence b, at the slot its table row gives
+ * (block_tables_dev[b][(len-1)/block_size] * block_size + (len-1) %
+ * block_size), followed by pa_decode_attention.
+ *  k_new, v_new: device [batch][n_kv_heads][head_dim] of in_dtype
+ *       (F32/F16/BF16), row b the new token of sequence b (length >= 1;
+ *       sequences of length 0 write nothing).  The caller has reserved that
+ *       slot (pa_seq_reserve) and owns its block (pa_cow_clone first when the
+ *       block is shared).
+ *  Other arguments as for pa_decode_attention.
+ * On a bf16/fp16 pool decoded by the matrix-core kernel, with in_dtype equal
+ * to the pool's dtype, the split kernel writes the tokens itself (one launch
+ * fewer); otherwise a launch of its own writes them first.  Errors as for
+ * pa_append_kv and pa_decode_attention. */
+pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, int32_t in_dtype,
+                         pa_pool* pool, const int32_t* block_tables_dev, const int32_t* seq_lens_dev,
+                         int32_t batch, int32_t n_q_heads, int32_t q_dtype, int32_t max_blocks_per_seq,
+                         int32_t max_seq_len, float scale, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+/* The append and split phase of pa_decode_step (pa_decode_combine then
+ * completes it, as after pa_decode_split). */
+pa_status pa_decode_step_split(const void* q, const void* k_new, const void* v_new,
+                               int32_t in_dtype, pa_pool* pool, const int32_t* block_tables_dev,
+                               const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
+                               int32_t q_dtype, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                               float scale, void* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* ---- speculative verify step ----------------------------------------------- */
 
 /* Workspace bytes pa_verify_attention needs for these shapes. */

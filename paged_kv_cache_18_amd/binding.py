@@ -92,6 +92,8 @@ _PROTOS = {
     "pa_prefill_attention": [vp, vp, P32, P32, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz, vp],
     "pa_decode_split": _DECODE_ARGS,
     "pa_decode_combine": _DECODE_ARGS,
+    "pa_decode_step": [vp, vp, vp, i32] + _DECODE_ARGS[1:],
+    "pa_decode_step_split": [vp, vp, vp, i32] + _DECODE_ARGS[1:],
 }
 EXPORTS = sorted(list(_PROTOS) + ["pa_last_error"])
 
@@ -353,6 +355,28 @@ def pa_decode_attention_noalloc(q, pool, tables_dev, lens_dev, batch, n_q_heads,
     _check(lib().pa_decode_attention_noalloc(_ptr(q), pool, _i32ptr(tables_dev), _i32ptr(lens_dev),
                                              batch, n_q_heads, dt, max_blocks, max_seq_len, scale,
                                              _ptr(out), _ptr(stream)))
+
+
+def _step(fn, q, k_new, v_new, in_dtype, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype,
+          max_blocks, max_seq_len, scale, out, workspace, workspace_bytes, stream):
+    dt = DTYPES[q_dtype] if isinstance(q_dtype, str) else int(q_dtype)
+    idt = DTYPES[in_dtype] if isinstance(in_dtype, str) else int(in_dtype)
+    _check(fn(_ptr(q), _ptr(k_new), _ptr(v_new), idt, pool, _i32ptr(tables_dev), _i32ptr(lens_dev),
+              batch, n_q_heads, dt, max_blocks, max_seq_len, scale, _ptr(out), _ptr(workspace),
+              workspace_bytes, _ptr(stream)))
+
+
+def pa_decode_step(q, k_new, v_new, in_dtype, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype,
+                   max_blocks, max_seq_len, scale, out, workspace, workspace_bytes, stream=None):
+    _step(lib().pa_decode_step, q, k_new, v_new, in_dtype, pool, tables_dev, lens_dev, batch,
+          n_q_heads, q_dtype, max_blocks, max_seq_len, scale, out, workspace, workspace_bytes, stream)
+
+
+def pa_decode_step_split(q, k_new, v_new, in_dtype, pool, tables_dev, lens_dev, batch, n_q_heads,
+                         q_dtype, max_blocks, max_seq_len, scale, out, workspace, workspace_bytes,
+                         stream=None):
+    _step(lib().pa_decode_step_split, q, k_new, v_new, in_dtype, pool, tables_dev, lens_dev, batch,
+          n_q_heads, q_dtype, max_blocks, max_seq_len, scale, out, workspace, workspace_bytes, stream)
 
 
 def pa_decode_split(q, pool, tables_dev, lens_dev, batch, n_q_heads, q_dtype, max_blocks,

@@ -416,6 +416,49 @@ __device__ inline bool next_piece(const DecodeArgs& a, const SH& sh, const Units
   return false;
 }
 
+// A decode step that appends its own new token (a.app_k set; 16-bit pools
+// of head_dim 128 with inputs of the pool's dtype).  Token L - 1 of
+// sequence b, KV head h, is written by the wave that will read the segment's
+// last block (tile nb - 1, in the piece holding it): the wave loads the
+// token's K and V words (lane l: dims 2l, 2l + 1) before its pipeline's
+// first loads, and stores them into the slot its table row gives right
+// before it issues the load of that block.  A wave's own memory operations
+// are performed in order, so its load of the block sees the stores; no
+// other wave reads the block.  Column slices of one head: the first slice's wave
+// writes.
+struct NewToken {
+  uint32_t k = 0, v = 0;  // the lane's two K and two V values
+  bool on = false;
+};
+
+__device__ inline NewToken new_token_load(const DecodeArgs& a, int lane, int b, int hv, int nsl,
+                                          int jw, int nst, int jend, int nb, int L) {
+  NewToken nt;
+  nt.on = a.app_k != nullptr && jend == nb && nb > 0 && L >= 1 && hv % nsl == 0 && nb - 1 >= jw &&
+          (nb - 1 - jw) % nst == 0;
+  if (nt.on) {
+    const size_t row = (size_t(b) * a.pool.n_kv_heads + hv / nsl) * kD + 2 * lane;
+    nt.k = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.app_k) + row);
+    nt.v = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.app_v) + row);
+  }
+  return nt;
+}
+
+__device__ inline void new_token_store(const DecodeArgs& a, const NewToken& nt, int lane, int hv,
+                                       int nsl, int L, const int32_t* trow) {
+  if (!nt.on) return;
+  const PoolDev& p = a.pool;
+  const int H = p.n_kv_heads, h = hv / nsl, bs = p.block_size;
+  const int id = table_entry(trow + (L - 1) / bs), t = (L - 1) % bs;
+  if (id < 0 || id >= p.num_blocks) return;
+  const size_t sid = size_t(id) * H + h;
+  uint16_t* ks = reinterpret_cast<uint16_t*>(p.base + p.off[kArrK] + sid * p.slab[kArrK]);
+  uint16_t* vs = reinterpret_cast<uint16_t*>(p.base + p.off[kArrV] + sid * p.slab[kArrV]);
+  *reinterpret_cast<uint32_t*>(ks + raw_k_elem(t, 2 * lane, bs)) = nt.k;
+  vs[raw_v_elem(t, 2 * lane, kD, bs)] = uint16_t(nt.v & 0xFFFFu);
+  vs[raw_v_elem(t, 2 * lane + 1, kD, bs)] = uint16_t(nt.v >> 16);
+}
+
 // Wave issue priority from the share of its chunk a workgroup still has to
 // stream (done of C blocks): bands above 1/2, 1/4 and 1/16 remaining.  With
 // equal chunks, the workgroups a compute unit holds would otherwise progress

@@ -61,8 +61,9 @@ namespace {
 using namespace dec;
 
 // NB register buffers per wave: NB - 1 blocks in flight while one is
-// consumed.  NB = 2 fits three waves per SIMD (12 per compute unit); deeper
-// pipelines trade waves for blocks in flight per wave.
+// consumed.  The kernel runs at two workgroups (two waves per SIMD) per
+// compute unit -- three measured slower -- so it may hold up to 256 registers
+// (NB = 2 needs about 170); deeper pipelines spill.
 //
 // NCT column tiles of 16 and CAUSAL: decode packs the G query heads of a KV
 // head into one tile; the verify step packs n_query x G (query, head) columns
@@ -83,8 +84,8 @@ struct TileId {
 // (the second from L2).  A pair stashes into two slots (wave w into slot
 // w & 1, its tile's columns), which halves the LDS of the merge.
 template <typename T, int NB, int NCT, bool CAUSAL, int BS, bool SPLIT = false>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(
-    NB == 2 && !CAUSAL ? 3 : 2))) void decode_split_mfma16(DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_mfma16(
+    DecodeArgs a) {
   typedef typename Mfma<T>::v8 v8;
   typedef typename Mfma<T>::v4 v4;
   static_assert(!SPLIT || NCT == 2, "tile split needs two tiles");
@@ -277,6 +278,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(
     // re-read it (an L2 hit, never consumed).
     const int jw = jbeg + ws;
     const int n = jw < jend ? (jend - jw + nst - 1) / nst : 0;
+    // a decode step's new token: its words are loaded ahead of the blocks
+    const NewToken ntok = CAUSAL ? NewToken{} : new_token_load(a, lane, b, hv, nsl, jw, nst, jend, nb, L);
     auto id_of = [&](int k) -> Tid {
       const int jt = jw + nst * min(k, n - 1);
       if constexpr (BS == 16) {
@@ -303,6 +306,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(
     if (n > 0) {
       v8 kb[NB][4], vb[NB][4];
       Tid ids[NB];
+      // the new token goes in before the load of its block: ahead of the
+      // first loads when they include it (this wave holds fewer than NB
+      // blocks of the piece), else just before that load -- a wave's loads
+      // and stores complete in order, so its waits for the loads issued
+      // after the stores also wait for the stores: as late as possible, they
+      // hold up nothing but the last block
+      if constexpr (!CAUSAL)
+        if (n < NB) new_token_store(a, ntok, lane, hv, nsl, L, trow);
 #pragma unroll
       for (int s = 0; s < NB - 1; ++s) {
         ids[s] = id_of(s);
@@ -318,6 +329,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(
           const int nxt = (s + NB - 1) % NB;
           ids[nxt] = nid;
           nid = id_of(k + s + NB);
+          if constexpr (!CAUSAL)
+            if (k + s == n - NB) new_token_store(a, ntok, lane, hv, nsl, L, trow);
           fetch(ids[nxt], kb[nxt], vb[nxt]);
           // no instruction of the block's product may move above the next
           // block's loads (it would wait for data still in flight)

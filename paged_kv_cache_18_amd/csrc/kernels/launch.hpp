@@ -32,6 +32,12 @@ hipError_t launch_migrate(const PoolDev& p, const MigrateJob& job, hipStream_t s
 hipError_t launch_append(const PoolDev& p, const void* k, const void* v, int32_t in_dtype,
                          const int32_t* slots, int32_t n_tokens, hipStream_t s);
 
+// Token lens[b] - 1 of every sequence b, from rows b of k / v, into the slot
+// its table row gives (a decode step's append, slots from the tables).
+hipError_t launch_append_last(const PoolDev& p, const void* k, const void* v, int32_t in_dtype,
+                              const int32_t* tables, const int32_t* lens, int32_t batch,
+                              int32_t max_blocks, int32_t max_len, hipStream_t s);
+
 hipError_t launch_block_copy(const PoolDev& p, int32_t src, int32_t dst, hipStream_t s);
 
 enum DecodeKernel : int32_t { kKernGeneric = 0, kKernMfma16 = 1, kKernQuant = 2 };
@@ -67,6 +73,13 @@ struct DecodeArgs {
   int32_t unit_blocks;   // matrix-core kernels: blocks per queued unit (0: none)
   int32_t static_permille;  // share of a region its owner streams, in 1/1000
   int32_t defer_merge;   // matrix-core kernels: 1 = leave split segments to the merge launch
+  // matrix-core decode kernels: a decode step that appends its new token
+  // first -- token lens[b] - 1 of every sequence b, K and V from row b of
+  // [batch][n_kv_heads][head_dim] inputs of dtype app_dt, into the slot its
+  // table gives -- or nullptr
+  const void* app_k;
+  const void* app_v;
+  int32_t app_dt;
 };
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t s);

@@ -299,13 +299,25 @@ void* noalloc_scratch(hipStream_t s);
 
 // noalloc: take the workspace from the library's static scratch array
 // (pa_decode_attention_noalloc) instead of ws / ws_bytes.
+// The step's append (pa_decode_step): K / V rows of the new tokens.
+struct NewTokens {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int32_t dtype = 0;
+};
+
 pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* tables,
                  const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t q_dtype,
                  int32_t max_blocks, int32_t max_seq_len, float scale, void* out, void* ws,
                  size_t ws_bytes, void* stream, int32_t n_query = 1, bool prefill = false,
-                 bool noalloc = false) {
+                 bool noalloc = false, NewTokens nt = {}) {
   return guard([&] {
     need_device(pool);
+    if (nt.k || nt.v) {
+      need(nt.k, "k_new");
+      need(nt.v, "v_new");
+      if (!pa::is_raw(nt.dtype)) fail(pa::kInvalidArg, "in_dtype must be F32, F16 or BF16");
+    }
     check_shapes(pool, batch, n_q_heads, max_seq_len);
     if (n_query < 1 || n_query > kMaxQueries) fail(pa::kInvalidArg, "n_query must be in [1, 4096]");
     const pa::Desc& d = pool->core.desc();
@@ -377,6 +389,19 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     a.split_blocks = pl.split_blocks;
     a.max_splits = pl.max_splits;
     a.kernel = pl.kernel;
+    if (nt.k && (phase & kSplit)) {
+      // the 16-bit matrix-core kernel writes the new tokens itself (inputs of
+      // the pool's dtype); otherwise a launch of their own goes first
+      if (pl.kernel == pa::kKernMfma16 && nt.dtype == d.kv_dtype) {
+        a.app_k = nt.k;
+        a.app_v = nt.v;
+        a.app_dt = nt.dtype;
+      } else {
+        check_hip(pa::launch_append_last(a.pool, nt.k, nt.v, nt.dtype, tables, lens, batch, max_blocks,
+                                         max_seq_len, s),
+                  "append launch");
+      }
+    }
     if (phase & kSplit) check_hip(pa::launch_decode_split(a, s), "decode split launch");
     if (phase & kCombine) check_hip(pa::launch_decode_combine(a, s), "decode combine launch");
   });
@@ -755,6 +780,24 @@ pa_status pa_decode_combine(const void* q, const pa_pool* pool, const int32_t* t
                             void* ws, size_t ws_bytes, void* stream) {
   return decode(kCombine, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks,
                 max_seq_len, scale, out, ws, ws_bytes, stream);
+}
+
+pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, int32_t in_dtype,
+                         pa_pool* pool, const int32_t* tables, const int32_t* lens, int32_t batch,
+                         int32_t n_q_heads, int32_t q_dtype, int32_t max_blocks,
+                         int32_t max_seq_len, float scale, void* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return decode(kBoth, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
+                scale, out, ws, ws_bytes, stream, 1, false, false, NewTokens{k_new, v_new, in_dtype});
+}
+
+pa_status pa_decode_step_split(const void* q, const void* k_new, const void* v_new,
+                               int32_t in_dtype, pa_pool* pool, const int32_t* tables,
+                               const int32_t* lens, int32_t batch, int32_t n_q_heads,
+                               int32_t q_dtype, int32_t max_blocks, int32_t max_seq_len,
+                               float scale, void* out, void* ws, size_t ws_bytes, void* stream) {
+  return decode(kSplit, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
+                scale, out, ws, ws_bytes, stream, 1, false, false, NewTokens{k_new, v_new, in_dtype});
 }
 
 pa_status pa_verify_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,

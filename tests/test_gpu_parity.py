@@ -751,6 +751,64 @@ def test_full_mixed_window():
     log(f"[gpu] mixed window full max err {err:.3g}")
 
 
+# ---- decode step: the step writes its newest token itself -------------------------
+STEP_CASES = {
+    "bf16": lambda: W.from_lengths([1, 15, 16, 17, 300, 1000, 2049], 32, 8, 128, "bf16", seed=211),
+    "f16-block32": lambda: W.from_lengths([1, 31, 32, 33, 500], 32, 8, 128, "f16", seed=212,
+                                          block_size=32),
+    "bf16-block8": lambda: W.from_lengths([1, 7, 8, 9, 400], 32, 8, 128, "bf16", seed=213, block_size=8),
+    "int4-sink": lambda: W.from_lengths([1, 16, 17, 700, 1500], 32, 8, 128, "int4", seed=214,
+                                        group=128, sink=True, outliers=True),
+    "fp8-sink": lambda: W.from_lengths([1, 16, 17, 700], 32, 8, 128, "fp8", seed=215, sink=True),
+    "int4-g64-window": lambda: W.window_batch([1, 100, 145, 1000], steps=2, window=128, group=64,
+                                              kv="int4", seed=216),
+    "f32-generic": lambda: W.from_lengths([1, 40, 333], 8, 4, 64, "f32", seed=217),
+}
+
+
+@pytest.mark.parametrize("name", list(STEP_CASES))
+def test_decode_step_writes_newest_token(name):
+    """pa_decode_step on a cache whose newest token of every sequence was
+    first overwritten with other values: the step writes the token into the
+    slot its table gives (the stored bytes match the oracle's bit for bit) and
+    the attention reads it (outputs match the oracle, and equal pa_append_kv
+    of the token followed by pa_decode_attention bit for bit).  The 16-bit
+    pools take the split kernel's own write, the others a launch of its own."""
+    wl = STEP_CASES[name]()
+    log(f"[gpu] decode step {name} B={wl.batch}")
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    tdev, ldev, t, l = kv.device_tables()
+    dt = TORCH_DT[wl.in_dtype]
+    rows_k, rows_v, slots = [], [], []
+    for b, sid in enumerate(wl.decode_seqs):
+        L = int(l[b])
+        K, V = wl.seq_tokens(sid)
+        rows_k.append(K[L - 1])
+        rows_v.append(V[L - 1])
+        slots.append(int(t[b, (L - 1) // wl.block_size]) * wl.block_size + (L - 1) % wl.block_size)
+    k_new = torch.from_numpy(np.stack(rows_k)).to(dt).to(DEV)
+    v_new = torch.from_numpy(np.stack(rows_v)).to(dt).to(DEV)
+    slots_dev = torch.tensor(slots, dtype=torch.int32, device=DEV)
+    q = torch.from_numpy(wl.q()).to(TORCH_DT[wl.q_dtype]).to(DEV)
+    bq, hq, _ = q.shape
+    max_len = int(max(l.max(), 1))
+    ref = kv.decode(q, tdev, ldev, max_len).clone()  # the cache as appended
+    # other values in the newest tokens' slots, which the step must overwrite
+    B.pa_append_kv(kv.pool, k_new * -3 + 1, v_new * 0.5 - 2, wl.in_dtype, slots_dev, bq, kv.stream())
+    need = B.pa_decode_workspace_bytes(kv.pool, bq, hq, max_len)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV)
+    out = torch.full_like(q, 7.0)
+    B.pa_decode_step(q, k_new, v_new, wl.in_dtype, kv.pool, tdev, ldev, bq, hq, wl.q_dtype,
+                     tdev.shape[1], max_len, wl.scale, out, ws, ws.numel(), kv.stream())
+    torch.cuda.synchronize()
+    check_stored(kv, wl, t, l)
+    assert torch.equal(out.view(torch.int16) if out.element_size() == 2 else out.view(torch.int32),
+                       ref.view(torch.int16) if ref.element_size() == 2 else ref.view(torch.int32)), \
+        f"{name}: step output differs from append + decode"
+    assert_close(out.to(torch.float64).cpu().numpy(), expected(wl), wl.q_dtype, f"decode step {name}")
+
+
 # ---- chunked paged prefill --------------------------------------------------------
 def prefill_chunk_gpu(kv, wl, k, n, seqs, env=None):
     """Attention of prefill chunk k (its n queries) for the sequences `seqs`,
