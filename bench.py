@@ -260,7 +260,7 @@ def main():
     fused = (args.fused_step and nq == 1 and wl.kv_dtype in ("bf16", "f16")
              and wl.in_dtype == wl.kv_dtype)
 
-    def attn_split():   # the dominant launch (verify / prefill: one launch at these shapes)
+    def attn_split():   # the dominant launch (prefill: the only one at these shapes)
         if fused:
             B.pa_decode_step_split(q, k_new, v_new, wl.in_dtype, *dargs[1:])
         elif nq == 1:
@@ -268,11 +268,13 @@ def main():
         elif args.config == "prefill-chunk":
             B.pa_prefill_attention(*vargs)
         else:
-            B.pa_verify_attention(*vargs)
+            B.pa_verify_split(*vargs)
 
-    def attn_rest():
+    def attn_rest():    # the merge launch, where the split leaves one
         if nq == 1:
             B.pa_decode_combine(*dargs)
+        elif args.config != "prefill-chunk":
+            B.pa_verify_combine(*vargs)
 
     def step():
         if not fused:

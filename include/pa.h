@@ -439,6 +439,21 @@ pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t*
                               int32_t n_query, int32_t q_dtype, int32_t max_blocks_per_seq,
                               int32_t max_seq_len, float scale, void* out, void* workspace,
                               size_t workspace_bytes, void* stream);
+/* The two phases of pa_verify_attention, as pa_decode_split and
+ * pa_decode_combine are of pa_decode_attention: the split launch, then the
+ * merge of segments the split left to a second launch (nothing else to do
+ * at most shapes).  Same arguments; call both, in this order, with the same
+ * workspace. */
+pa_status pa_verify_split(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
+                          const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
+                          int32_t n_query, int32_t q_dtype, int32_t max_blocks_per_seq,
+                          int32_t max_seq_len, float scale, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+pa_status pa_verify_combine(const void* q, const pa_pool* pool, const int32_t* block_tables_dev,
+                            const int32_t* seq_lens_dev, int32_t batch, int32_t n_q_heads,
+                            int32_t n_query, int32_t q_dtype, int32_t max_blocks_per_seq,
+                            int32_t max_seq_len, float scale, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* ---- chunked paged prefill ---------------------------------------------------- */
 

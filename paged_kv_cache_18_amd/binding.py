@@ -88,6 +88,8 @@ _PROTOS = {
     "pa_decode_attention_noalloc": [vp, vp, P32, P32, i32, i32, i32, i32, i32, f32, vp, vp],
     "pa_verify_workspace_bytes": [vp, i32, i32, i32, i32, C.POINTER(sz)],
     "pa_verify_attention": [vp, vp, P32, P32, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz, vp],
+    "pa_verify_split": [vp, vp, P32, P32, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz, vp],
+    "pa_verify_combine": [vp, vp, P32, P32, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz, vp],
     "pa_prefill_workspace_bytes": [vp, i32, i32, i32, i32, C.POINTER(sz)],
     "pa_prefill_attention": [vp, vp, P32, P32, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz, vp],
     "pa_decode_split": _DECODE_ARGS,
@@ -406,13 +408,31 @@ def pa_verify_workspace_bytes(pool, batch, n_q_heads, n_query, max_seq_len):
     return out.value
 
 
+def _verify(fn, q, pool, tables_dev, lens_dev, batch, n_q_heads, n_query, q_dtype, max_blocks,
+            max_seq_len, scale, out, workspace, workspace_bytes, stream):
+    dt = DTYPES[q_dtype] if isinstance(q_dtype, str) else int(q_dtype)
+    _check(fn(_ptr(q), pool, _i32ptr(tables_dev), _i32ptr(lens_dev), batch, n_q_heads, n_query, dt,
+              max_blocks, max_seq_len, scale, _ptr(out), _ptr(workspace), workspace_bytes,
+              _ptr(stream)))
+
+
 def pa_verify_attention(q, pool, tables_dev, lens_dev, batch, n_q_heads, n_query, q_dtype,
                         max_blocks, max_seq_len, scale, out, workspace, workspace_bytes,
                         stream=None):
-    dt = DTYPES[q_dtype] if isinstance(q_dtype, str) else int(q_dtype)
-    _check(lib().pa_verify_attention(_ptr(q), pool, _i32ptr(tables_dev), _i32ptr(lens_dev), batch,
-                                     n_q_heads, n_query, dt, max_blocks, max_seq_len, scale,
-                                     _ptr(out), _ptr(workspace), workspace_bytes, _ptr(stream)))
+    _verify(lib().pa_verify_attention, q, pool, tables_dev, lens_dev, batch, n_q_heads, n_query,
+            q_dtype, max_blocks, max_seq_len, scale, out, workspace, workspace_bytes, stream)
+
+
+def pa_verify_split(q, pool, tables_dev, lens_dev, batch, n_q_heads, n_query, q_dtype, max_blocks,
+                    max_seq_len, scale, out, workspace, workspace_bytes, stream=None):
+    _verify(lib().pa_verify_split, q, pool, tables_dev, lens_dev, batch, n_q_heads, n_query,
+            q_dtype, max_blocks, max_seq_len, scale, out, workspace, workspace_bytes, stream)
+
+
+def pa_verify_combine(q, pool, tables_dev, lens_dev, batch, n_q_heads, n_query, q_dtype, max_blocks,
+                      max_seq_len, scale, out, workspace, workspace_bytes, stream=None):
+    _verify(lib().pa_verify_combine, q, pool, tables_dev, lens_dev, batch, n_q_heads, n_query,
+            q_dtype, max_blocks, max_seq_len, scale, out, workspace, workspace_bytes, stream)
 
 
 def pa_prefill_workspace_bytes(pool, batch, n_q_heads, chunk, max_seq_len):

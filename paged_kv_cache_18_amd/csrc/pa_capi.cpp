@@ -821,6 +821,22 @@ pa_status pa_verify_attention(const void* q, const pa_pool* pool, const int32_t*
                 scale, out, ws, ws_bytes, stream, n_query);
 }
 
+pa_status pa_verify_split(const void* q, const pa_pool* pool, const int32_t* tables,
+                          const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t n_query,
+                          int32_t q_dtype, int32_t max_blocks, int32_t max_seq_len, float scale,
+                          void* out, void* ws, size_t ws_bytes, void* stream) {
+  return decode(kSplit, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
+                scale, out, ws, ws_bytes, stream, n_query);
+}
+
+pa_status pa_verify_combine(const void* q, const pa_pool* pool, const int32_t* tables,
+                            const int32_t* lens, int32_t batch, int32_t n_q_heads, int32_t n_query,
+                            int32_t q_dtype, int32_t max_blocks, int32_t max_seq_len, float scale,
+                            void* out, void* ws, size_t ws_bytes, void* stream) {
+  return decode(kCombine, q, pool, tables, lens, batch, n_q_heads, q_dtype, max_blocks, max_seq_len,
+                scale, out, ws, ws_bytes, stream, n_query);
+}
+
 pa_status pa_prefill_workspace_bytes(const pa_pool* pool, int32_t batch, int32_t n_q_heads,
                                      int32_t chunk, int32_t max_seq_len, size_t* bytes) {
   return guard([&] {

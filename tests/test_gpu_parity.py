@@ -751,6 +751,33 @@ def test_full_mixed_window():
     log(f"[gpu] mixed window full max err {err:.3g}")
 
 
+@pytest.mark.parametrize("kvdt,group", [("int4", 128), ("bf16", 0)])
+def test_verify_phases_equal_whole_call(kvdt, group):
+    """pa_verify_split followed by pa_verify_combine gives pa_verify_attention's
+    output bit for bit -- also where the split leaves its segments to the merge
+    launch (one long INT4 sequence: 64 pieces per segment)."""
+    if kvdt == "int4":
+        wl = W.from_lengths([20000, 3], 32, 8, 128, "int4", seed=231, group=group, sink=True)
+    else:
+        wl = W.from_lengths([20000, 700, 3], 32, 8, 128, "bf16", seed=232)
+    nq = 6
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    tdev, ldev, t, l = kv.device_tables()
+    q = torch.from_numpy(wl.q_verify(nq)).to(TORCH_DT[wl.q_dtype]).to(DEV)
+    bq, max_len = q.shape[0], int(max(l.max(), 1))
+    need = B.pa_verify_workspace_bytes(kv.pool, bq, wl.n_q_heads, nq, max_len)
+    args = (kv.pool, tdev, ldev, bq, wl.n_q_heads, nq, wl.q_dtype, tdev.shape[1], max_len, wl.scale)
+    whole = torch.empty((bq, nq, wl.n_q_heads, wl.head_dim), dtype=q.dtype, device=DEV)
+    parts = torch.full_like(whole, 7.0)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV)
+    B.pa_verify_attention(q, *args, whole, ws, ws.numel(), kv.stream())
+    B.pa_verify_split(q, *args, parts, ws, ws.numel(), kv.stream())
+    B.pa_verify_combine(q, *args, parts, ws, ws.numel(), kv.stream())
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int16), parts.view(torch.int16)), f"verify phases {kvdt}"
+
+
 # ---- decode step: the step writes its newest token itself -------------------------
 STEP_CASES = {
     "bf16": lambda: W.from_lengths([1, 15, 16, 17, 300, 1000, 2049], 32, 8, 128, "bf16", seed=211),
