@@ -312,6 +312,20 @@ def test_quantized_split_k_and_kernels_agree(kvdt, group, split):
     assert_close(out_g, ref, "f16", f"{kvdt} generic kernel split {split}")
 
 
+@pytest.mark.parametrize("kvdt,group", [("int4", 128), ("int4", 64), ("fp8", 0)])
+@pytest.mark.parametrize("nb", ["3", "4"])
+def test_quantized_whole_block_loop_edges(kvdt, group, nb):
+    """The quantized kernel's loop of whole blocks leaves a wave's partial
+    last block to the blocks after it, which then number up to the prefetch
+    depth -- the last of them fetched only there.  Regions of 48 blocks
+    (12 per wave) over sequences of 144 and 145 blocks, the last partial,
+    put that case in the last region's wave, next to its neighbours."""
+    wl = W.from_lengths([2293, 2309, 2318], 32, 8, 128, kvdt, seed=241, group=group, sink=True,
+                        outliers=True)
+    _, out, _, _ = run(wl, env={"PA_SPLIT_BLOCKS": "48", "PA_QUANT_NB": nb})
+    assert_close(out, expected(wl), "f16", f"{kvdt} g{group} whole-block loop edges nb{nb}")
+
+
 @pytest.mark.parametrize("kvdt", ["int4", "fp8"])
 def test_full_mixed_precision(kvdt):
     """Full mixed-precision workload (65,536 + 64 appended tokens, FP16 sink,
