@@ -231,6 +231,30 @@ struct Units {
   __device__ int queued(int q) const { return (q % R) * per() + 1 + q / R; }
 };
 
+// The cut of a list of TB blocks per segment (wave-uniform arithmetic).
+__device__ inline Units cut_of(const DecodeArgs& a, int TB) {
+  const int W = TB * seg_heads(a);
+  const int R = a.max_splits;  // the split kernel's grid
+  int C, Cs, U = 1, m = 0, n = 0, q = 0, hs = 0;
+  if (a.split_blocks > 0) {
+    C = Cs = a.split_blocks;
+  } else {
+    C = max(1, (W + R - 1) / R);
+    Cs = C;
+    if (a.unit_blocks > 0 && a.static_permille < 1000) {
+      U = a.unit_blocks;
+      Cs = max(1, int(int64_t(C) * max(a.static_permille, 0) / 1000));
+      m = (C - Cs + U - 1) / U;
+    } else if (R % seg_heads(a) == 0 && TB > 0) {
+      hs = seg_heads(a);
+      n = TB;
+      q = R / hs;
+      C = Cs = (TB + q - 1) / q;
+    }
+  }
+  return Units{W, R, C, Cs, U, m, n, TB, hs, q};
+}
+
 // Wave 0 reads the lengths (one load per sequence, kept in LDS for the
 // first kLenCap) and sizes the cut from them; every thread gets both.
 template <class SH>
@@ -253,41 +277,71 @@ __device__ inline Units setup_units(const DecodeArgs& a, SH& sh, int w, int lane
       }
       W += __shfl(incl, 63, 64);
     }
-    const int TB = W;
-    W *= seg_heads(a);
-    const int R = a.max_splits;  // the split kernel's grid
-    int C, Cs, U = 1, m = 0, n = 0, q = 0, hs = 0;
-    if (a.split_blocks > 0) {
-      C = Cs = a.split_blocks;
-    } else {
-      C = max(1, (W + R - 1) / R);
-      Cs = C;
-      if (a.unit_blocks > 0 && a.static_permille < 1000) {
-        U = a.unit_blocks;
-        Cs = max(1, int(int64_t(C) * max(a.static_permille, 0) / 1000));
-        m = (C - Cs + U - 1) / U;
-      } else if (R % seg_heads(a) == 0 && TB > 0) {
-        hs = seg_heads(a);
-        n = TB;
-        q = R / hs;
-        C = Cs = (TB + q - 1) / q;
-      }
-    }
+    const Units u = cut_of(a, W);
     if (lane == 0) {
-      sh.units[0] = W;
-      sh.units[1] = R;
-      sh.units[2] = C;
-      sh.units[3] = Cs;
-      sh.units[4] = U;
-      sh.units[5] = m;
-      sh.units[6] = n;
-      sh.units[7] = q;
-      sh.units[8] = TB;
-      sh.units[9] = hs;
+      sh.units[0] = u.W;
+      sh.units[1] = u.R;
+      sh.units[2] = u.C;
+      sh.units[3] = u.Cs;
+      sh.units[4] = u.U;
+      sh.units[5] = u.m;
+      sh.units[6] = u.n;
+      sh.units[7] = u.q;
+      sh.units[8] = u.TB;
+      sh.units[9] = u.hs;
     }
   }
   __syncthreads();
   return Units{sh.units[0], sh.units[1], sh.units[2], sh.units[3], sh.units[4], sh.units[5], sh.units[6], sh.units[8], sh.units[9], sh.units[7]};
+}
+
+// ---- The cut with the lengths in registers (batches of at most 64) ----------
+// Every wave reads the lengths itself, lane b holding sequence b, and keeps
+// the running sum of their block counts in a register: the cut, the
+// sequence holding a position and each piece's bounds then come from
+// cross-lane reads of registers, with no LDS traffic and no workgroup barrier
+// ahead of the first block loads.  A launch takes this form when the batch
+// fits one wave and no queue is asked for (every workgroup streams exactly
+// its own region).
+constexpr int kRegLens = 64;
+
+struct RegLens {
+  int len;   // lane b: the length of sequence b (0 past the batch)
+  int incl;  // lane b: blocks of sequences 0..b
+  __device__ int len_of(int b) const { return __builtin_amdgcn_readlane(len, b & 63); }
+  __device__ int blocks_of(int b) const { return (len_of(b) + 15) >> 4; }
+};
+
+// Inclusive running sum over the 64 lanes: shifts inside each row of 16
+// lanes, then each row's total carried into the rows above it.
+__device__ inline int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+__device__ inline RegLens reg_lens(const DecodeArgs& a, int lane) {
+  RegLens r;
+  r.len = lane < a.batch ? seq_len(a, lane) : 0;
+  r.incl = wave_incl_sum((r.len + 15) >> 4);
+  return r;
+}
+
+__device__ inline Units reg_units(const DecodeArgs& a, const RegLens& rl) {
+  return cut_of(a, __builtin_amdgcn_readlane(rl.incl, 63));
+}
+
+// The sequence b holding position p0 and the place fb of its first block in
+// its head's list, from the running sums.
+__device__ inline void reg_locate(const Units& um, const RegLens& rl, int p0, int& b, int& fb) {
+  const int r0 = p0 % um.TB;
+  const unsigned long long hit = __ballot(rl.incl > r0);  // lanes past the batch hold TB
+  b = hit ? __builtin_ctzll(hit) : 64;
+  fb = b > 0 ? __builtin_amdgcn_readlane(rl.incl, (b - 1) & 63) : 0;
 }
 
 // The sequence b holding position p0 and the place fb of its first block in
@@ -378,13 +432,13 @@ __device__ inline int next_unit(const DecodeArgs& a, SH& sh, const Units& um) {
 
 
 // Zero the output rows of empty sequences (no piece covers them); workgroup
-// c takes sequences c, c + grid, ...
-template <typename TO, class SH>
-__device__ inline void zero_empty_rows(const DecodeArgs& a, const SH& sh) {
+// c takes sequences c, c + grid, ...  blocks(b): the block count of sequence b.
+template <typename TO, class BK>
+__device__ inline void zero_empty_rows(const DecodeArgs& a, BK blocks) {
   const int Hq = a.n_q_heads, nq = max(a.n_query, 1);
   TO* out = static_cast<TO*>(a.out);
   for (int b = blockIdx.x; b < a.batch; b += gridDim.x)
-    if (blocks_of(a, sh, b) == 0)
+    if (blocks(b) == 0)
       for (int i = threadIdx.x; i < nq * Hq * kD; i += kWaves * 64)
         out[size_t(b) * nq * Hq * kD + i] = TO(0.f);
 }
@@ -392,8 +446,8 @@ __device__ inline void zero_empty_rows(const DecodeArgs& a, const SH& sh) {
 // The next piece [jbeg, jend) of segment (b, h) starting at position pos;
 // advances (b, fb) past finished or empty sequences, back to the first
 // sequence where pos enters the next head's list.  False when done.
-template <class SH>
-__device__ inline bool next_piece(const DecodeArgs& a, const SH& sh, const Units& um, int pos, int pos1,
+template <class BK>
+__device__ inline bool next_piece(const DecodeArgs& a, BK blocks, const Units& um, int pos, int pos1,
                                   int& b, int& fb, int& h, int& jbeg, int& jend, int& nb) {
   while (pos < pos1) {
     const int hv = pos / um.TB, r = pos - hv * um.TB;
@@ -402,7 +456,7 @@ __device__ inline bool next_piece(const DecodeArgs& a, const SH& sh, const Units
       fb = 0;
     }
     if (b >= a.batch) return false;
-    nb = blocks_of(a, sh, b);
+    nb = blocks(b);
     if (r >= fb + nb) {
       fb += nb;
       ++b;

@@ -83,7 +83,10 @@ struct TileId {
 // one tile's registers and every block is read by two waves of the workgroup
 // (the second from L2).  A pair stashes into two slots (wave w into slot
 // w & 1, its tile's columns), which halves the LDS of the merge.
-template <typename T, int NB, int NCT, bool CAUSAL, int BS, bool SPLIT = false>
+//
+// RL: a batch of at most 64 sequences with no queue, whose lengths every wave
+// keeps in registers (see RegLens).
+template <typename T, int NB, int NCT, bool CAUSAL, int BS, bool SPLIT = false, bool RL = false>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_mfma16(
     DecodeArgs a) {
   typedef typename Mfma<T>::v8 v8;
@@ -102,8 +105,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const int H = p.n_kv_heads, Hq = a.n_q_heads, G = Hq / H;
   const OutMap om = out_map(a);
   const int nq = om.nq, nsl = om.nsl;
-  const Units um = setup_units(a, sh, w, lane);
-  zero_empty_rows<T>(a, sh);
+  const RegLens rl = [&] {
+    if constexpr (RL) return reg_lens(a, lane);
+    else return RegLens{0, 0};
+  }();
+  const Units um = [&] {
+    if constexpr (RL) return reg_units(a, rl);
+    else return setup_units(a, sh, w, lane);
+  }();
+  auto blocks_at = [&](int bb) {
+    if constexpr (RL) return rl.blocks_of(bb);
+    else return blocks_of(a, sh, bb);
+  };
+  zero_empty_rows<T>(a, blocks_at);
   int b = 0, fb = 0;
 
   const T* kbase = reinterpret_cast<const T*>(p.base + p.off[kArrK]);
@@ -239,18 +253,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   };
 
   const int own_unit = um.owned_by_head(int(blockIdx.x));
-  for (int unit = own_unit; unit >= 0; unit = next_unit(a, sh, um)) {
+  for (int unit = own_unit; unit >= 0; unit = RL ? -1 : next_unit(a, sh, um)) {
   const int pos0 = um.start(unit), pos1 = um.end(unit);
   if (pos0 >= pos1) continue;  // a region past the end of the work
-  locate(a, sh, um, w, lane, pos0, b, fb);
+  if constexpr (RL) reg_locate(um, rl, pos0, b, fb);
+  else locate(a, sh, um, w, lane, pos0, b, fb);
   // progress-based priority in the owner's prefix; queued units run at the
   // base priority, behind the workgroups still streaming their own prefix
   const int prio_span = unit == own_unit ? pos1 - pos0 : 0;
   int pos = pos0;
   bool first = true;
   int jbeg = 0, jend = 0, nb = 0;
-  while (next_piece(a, sh, um, pos, pos1, b, fb, hv, jbeg, jend, nb)) {
-    L = len_of(a, sh, b);
+  while (next_piece(a, blocks_at, um, pos, pos1, b, fb, hv, jbeg, jend, nb)) {
+    if constexpr (RL) L = rl.len_of(b);
+    else L = len_of(a, sh, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
     h = hv / nsl;
     const int ncol = om.cols(hv);
@@ -377,24 +393,42 @@ int mfma_nb() {
 template <typename T, int BS>
 hipError_t launch_bs(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.max_splits)), block(kWaves * 64);
+  // the register-lengths form for batches of at most 64 sequences with no
+  // queue, at the default prefetch depth and tile split
+  const bool rl = a.batch <= kRegLens && !(a.unit_blocks > 0 && a.static_permille < 1000);
   if (a.n_query > 1) {  // verify / prefill chunk: one or two column tiles, causal
     const int ncol = a.n_query * (a.n_q_heads / a.pool.n_kv_heads);  // > 32: slices of 32
-    if (ncol <= 16)
-      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, true, BS>), grid, block, 0, s, a);
-    else if (verify_split())
-      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 2, true, BS, true>), grid, block, 0, s, a);
-    else
+    if (ncol <= 16) {
+      if (rl)
+        hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, true, BS, false, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, true, BS>), grid, block, 0, s, a);
+    } else if (verify_split()) {
+      if (rl)
+        hipLaunchKernelGGL((decode_split_mfma16<T, 2, 2, true, BS, true, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((decode_split_mfma16<T, 2, 2, true, BS, true>), grid, block, 0, s, a);
+    } else {
       hipLaunchKernelGGL((decode_split_mfma16<T, 2, 2, true, BS>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
   }
   if constexpr (BS == 16) {
     switch (mfma_nb()) {
       case 3: hipLaunchKernelGGL((decode_split_mfma16<T, 3, 1, false, 16>), grid, block, 0, s, a); break;
       case 4: hipLaunchKernelGGL((decode_split_mfma16<T, 4, 1, false, 16>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, false, 16>), grid, block, 0, s, a); break;
+      default:
+        if (rl)
+          hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, false, 16, false, true>), grid, block, 0, s, a);
+        else
+          hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, false, 16>), grid, block, 0, s, a);
+        break;
     }
   } else {
-    hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, false, BS>), grid, block, 0, s, a);
+    if (rl)
+      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, false, BS, false, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_split_mfma16<T, 2, 1, false, BS>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

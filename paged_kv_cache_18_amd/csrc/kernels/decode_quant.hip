@@ -207,7 +207,10 @@ __device__ inline uint32_t pk_f16(float a, float b) {
 // ids the body loop met before that run (a table between a multi-block
 // reserve and its settle: FP16 runs between body runs) are streamed after
 // it, one block at a time, by the wave that met them.
-template <int KIND, int NB, int NG, int NCT, bool CAUSAL>
+//
+// RL: a batch of at most 64 sequences with no queue, whose lengths every wave
+// keeps in registers (see RegLens).
+template <int KIND, int NB, int NG, int NCT, bool CAUSAL, bool RL = false>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 && NCT == 1 ? 3 : 2))) void decode_split_quant(DecodeArgs a) {
   typedef typename Quant<KIND, NG>::Buf Buf;
   typedef Mfma<_Float16> MF;
@@ -225,8 +228,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   const bool keep = gsel == g * NG / 4;         // this lane's output rows lie in that group
   const OutMap om = out_map(a);
   const int nq = om.nq, nsl = om.nsl;
-  const Units um = setup_units(a, sh, w, lane);
-  zero_empty_rows<_Float16>(a, sh);
+  const RegLens rl = [&] {
+    if constexpr (RL) return reg_lens(a, lane);
+    else return RegLens{0, 0};
+  }();
+  const Units um = [&] {
+    if constexpr (RL) return reg_units(a, rl);
+    else return setup_units(a, sh, w, lane);
+  }();
+  auto blocks_at = [&](int bb) {
+    if constexpr (RL) return rl.blocks_of(bb);
+    else return blocks_of(a, sh, bb);
+  };
+  zero_empty_rows<_Float16>(a, blocks_at);
   int b = 0, fb = 0;
 
   const float sl2 = a.scale_log2;
@@ -468,18 +482,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
   };
 
   const int own_unit = um.owned(int(blockIdx.x));
-  for (int unit = own_unit; unit >= 0; unit = next_unit(a, sh, um)) {
+  for (int unit = own_unit; unit >= 0; unit = RL ? -1 : next_unit(a, sh, um)) {
   const int pos0 = um.start(unit), pos1 = um.end(unit);
   if (pos0 >= pos1) continue;  // a region past the end of the work
-  locate(a, sh, um, w, lane, pos0, b, fb);
+  if constexpr (RL) reg_locate(um, rl, pos0, b, fb);
+  else locate(a, sh, um, w, lane, pos0, b, fb);
   // progress-based priority in the owner's prefix; queued units run at the
   // base priority, behind the workgroups still streaming their own prefix
   const int prio_span = unit == own_unit ? pos1 - pos0 : 0;
   int pos = pos0;
   bool first = true;
   int jbeg = 0, jend = 0, nb = 0;
-  while (next_piece(a, sh, um, pos, pos1, b, fb, hv, jbeg, jend, nb)) {
-    L = len_of(a, sh, b);
+  while (next_piece(a, blocks_at, um, pos, pos1, b, fb, hv, jbeg, jend, nb)) {
+    if constexpr (RL) L = rl.len_of(b);
+    else L = len_of(a, sh, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
     h = hv / nsl;
     const int ncol = om.cols(hv);
@@ -744,19 +760,38 @@ int occ_kind(int nct) {
   }
 }
 
+// The register-lengths form (RL) for batches of at most 64 sequences with no
+// queue, at the default prefetch depths; the general form otherwise.
+inline bool reg_lens_ok(const DecodeArgs& a) {
+  return a.batch <= kRegLens && !(a.unit_blocks > 0 && a.static_permille < 1000);
+}
+
 template <int KIND, int NG>
 void launch_kind(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.max_splits)), block(kWaves * 64);
+  const bool rl = reg_lens_ok(a);
   if (a.n_query > 1) {  // verify step / prefill chunk: logical columns of a segment
     const int cols = a.col_slices > 1 ? a.slice_cols : a.n_query * (a.n_q_heads / a.pool.n_kv_heads);
-    if (cols * NG <= 16)
-      hipLaunchKernelGGL((decode_split_quant<KIND, kVerifyNB<1>, NG, 1, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((decode_split_quant<KIND, kVerifyNB<2>, NG, 2, true>), grid, block, 0, s, a);
+    if (cols * NG <= 16) {
+      if (rl)
+        hipLaunchKernelGGL((decode_split_quant<KIND, kVerifyNB<1>, NG, 1, true, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((decode_split_quant<KIND, kVerifyNB<1>, NG, 1, true>), grid, block, 0, s, a);
+    } else {
+      if (rl)
+        hipLaunchKernelGGL((decode_split_quant<KIND, kVerifyNB<2>, NG, 2, true, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((decode_split_quant<KIND, kVerifyNB<2>, NG, 2, true>), grid, block, 0, s, a);
+    }
     return;
   }
   switch (quant_nb<NG>()) {
-    case 3: hipLaunchKernelGGL((decode_split_quant<KIND, 3, NG, 1, false>), grid, block, 0, s, a); break;
+    case 3:
+      if (rl)
+        hipLaunchKernelGGL((decode_split_quant<KIND, 3, NG, 1, false, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((decode_split_quant<KIND, 3, NG, 1, false>), grid, block, 0, s, a);
+      break;
     case 4: hipLaunchKernelGGL((decode_split_quant<KIND, 4, NG, 1, false>), grid, block, 0, s, a); break;
     case 6: hipLaunchKernelGGL((decode_split_quant<KIND, 6, NG, 1, false>), grid, block, 0, s, a); break;
     default: hipLaunchKernelGGL((decode_split_quant<KIND, 2, NG, 1, false>), grid, block, 0, s, a); break;
