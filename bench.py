@@ -2,8 +2,8 @@
 
 One step = one decode step of one attention layer for the whole batch:
   1. append each sequence's newest K/V token into its slot (quantize-on-write
-     for INT4/FP8 pools; with --fused-step, on bf16/fp16 pools, the split
-     kernel writes it itself: pa_decode_step),
+     for INT4/FP8 pools; with --fused-step the split kernel writes it
+     itself: pa_decode_step),
   2. split-K decode over all cached tokens (gathered through block tables),
      including the log-sum-exp merge of split segments (fused into the
      matrix-core kernels; a second launch for the generic kernel and for
@@ -196,8 +196,8 @@ def main():
                     help="physical blocks in logical order (free order 0..N-1): the contiguous "
                          "comparator for the paging overhead")
     ap.add_argument("--fused-step", action="store_true",
-                    help="decode steps through pa_decode_step (the 16-bit split kernel writes the "
-                         "new tokens itself)")
+                    help="decode steps through pa_decode_step (the split kernel writes the new "
+                         "tokens itself)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -254,11 +254,11 @@ def main():
              max_len, wl.scale, out, ws, ws.numel(), sh)
 
     # --fused-step: the step through pa_decode_step, whose split kernel writes
-    # the new tokens itself on a 16-bit pool with inputs of the pool's dtype
-    # (one launch fewer per step, a longer split launch); the roofline then
-    # times that launch
-    fused = (args.fused_step and nq == 1 and wl.kv_dtype in ("bf16", "f16")
-             and wl.in_dtype == wl.kv_dtype)
+    # the new tokens itself (16-bit pools with inputs of the pool's dtype;
+    # INT4/FP8 pools quantize them), one launch fewer per step and a longer
+    # split launch; the roofline then times that launch
+    fused = (args.fused_step and nq == 1
+             and (wl.kv_dtype in ("int4", "fp8") or wl.in_dtype == wl.kv_dtype))
 
     def attn_split():   # the dominant launch (prefill: the only one at these shapes)
         if fused:

@@ -388,10 +388,12 @@ pa_status pa_decode_attention_noalloc(const void* q, const pa_pool* pool,
  *       slot (pa_seq_reserve) and owns its block (pa_cow_clone first when the
  *       block is shared).
  *  Other arguments as for pa_decode_attention.
- * On a bf16/fp16 pool decoded by the matrix-core kernel, with in_dtype equal
- * to the pool's dtype, the split kernel writes the tokens itself (one launch
- * fewer); otherwise a launch of its own writes them first.  Errors as for
- * pa_append_kv and pa_decode_attention. */
+ * The matrix-core split kernels write the tokens themselves (one launch
+ * fewer): on a bf16/fp16 pool with in_dtype equal to the pool's dtype, and
+ * on an INT4/FP8 pool (quantized, or FP16 into sink and window blocks, by
+ * the workgroup that holds the sequence's last block, before it loads any
+ * block) at the default prefetch depth; otherwise a launch of its own writes
+ * them first.  Errors as for pa_append_kv and pa_decode_attention. */
 pa_status pa_decode_step(const void* q, const void* k_new, const void* v_new, int32_t in_dtype,
                          pa_pool* pool, const int32_t* block_tables_dev, const int32_t* seq_lens_dev,
                          int32_t batch, int32_t n_q_heads, int32_t q_dtype, int32_t max_blocks_per_seq,

@@ -32,6 +32,7 @@
 #include <cstdlib>
 #include <type_traits>
 
+#include "append_common.hpp"
 #include "decode_common.hpp"
 
 namespace pa {
@@ -209,8 +210,9 @@ __device__ inline uint32_t pk_f16(float a, float b) {
 // it, one block at a time, by the wave that met them.
 //
 // RL: a batch of at most 64 sequences with no queue, whose lengths every wave
-// keeps in registers (see RegLens).
-template <int KIND, int NB, int NG, int NCT, bool CAUSAL, bool RL = false>
+// keeps in registers (see RegLens).  AP: a decode step that appends its new
+// token (a.app_k set; decode only).
+template <int KIND, int NB, int NG, int NCT, bool CAUSAL, bool RL = false, bool AP = false>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB == 2 && NCT == 1 ? 3 : 2))) void decode_split_quant(DecodeArgs a) {
   typedef typename Quant<KIND, NG>::Buf Buf;
   typedef Mfma<_Float16> MF;
@@ -498,6 +500,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
     else L = len_of(a, sh, b);
     trow = a.tables + size_t(b) * a.max_blocks_per_seq;
     h = hv / nsl;
+    // a decode step that appends its new token (a.app_k set): the workgroup
+    // whose piece ends the segment writes token L - 1 of head h -- wave 0 its
+    // K, wave 1 its V, quantized where the block is a body block -- before any
+    // of its waves loads a block; the barrier orders those stores before the
+    // other waves' loads (no other workgroup reads the segment's last block)
+    if constexpr (AP && !CAUSAL) {
+      if (jend == nb && nb > 0 && L >= 1) {
+        if (w < 2)
+          app::append_one<1>(p, a.app_k, a.app_v, a.app_dt, size_t(b), h, w, table_entry(trow + (L - 1) / 16),
+                             (L - 1) % 16, lane);
+        __syncthreads();
+      }
+    }
     const int ncol = om.cols(hv);
     const int lo = max(jbeg, SP);  // first non-sink block of the piece
     // the table's last 64 entries of the piece, for the window scan below
@@ -784,6 +799,18 @@ void launch_kind(const DecodeArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((decode_split_quant<KIND, kVerifyNB<2>, NG, 2, true>), grid, block, 0, s, a);
     }
     return;
+  }
+  if (a.app_k != nullptr) {  // a decode step: the default depth writes the new tokens itself
+    if (quant_nb<NG>() == 3) {
+      if (rl)
+        hipLaunchKernelGGL((decode_split_quant<KIND, 3, NG, 1, false, true, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((decode_split_quant<KIND, 3, NG, 1, false, false, true>), grid, block, 0, s, a);
+      return;
+    }
+    if (launch_append_last(a.pool, a.app_k, a.app_v, a.app_dt, a.tables, a.lens, a.batch,
+                           a.max_blocks_per_seq, a.max_seq_len, s) != hipSuccess)
+      return;  // the caller's hipGetLastError reports it
   }
   switch (quant_nb<NG>()) {
     case 3:

@@ -390,9 +390,10 @@ pa_status decode(int phase, const void* q, const pa_pool* pool, const int32_t* t
     a.max_splits = pl.max_splits;
     a.kernel = pl.kernel;
     if (nt.k && (phase & kSplit)) {
-      // the 16-bit matrix-core kernel writes the new tokens itself (inputs of
-      // the pool's dtype); otherwise a launch of their own goes first
-      if (pl.kernel == pa::kKernMfma16 && nt.dtype == d.kv_dtype) {
+      // the matrix-core kernels write the new tokens themselves (16-bit pools:
+      // inputs of the pool's dtype; INT4/FP8 pools quantize them); otherwise a
+      // launch of their own goes first
+      if ((pl.kernel == pa::kKernMfma16 && nt.dtype == d.kv_dtype) || pl.kernel == pa::kKernQuant) {
         a.app_k = nt.k;
         a.app_v = nt.v;
         a.app_dt = nt.dtype;
