@@ -393,6 +393,33 @@ def test_more_sequences_than_the_lds_length_cache(kvdt, env):
     assert_close(out, expected(wl), "bf16" if kvdt == "bf16" else "f16", f"700 seqs {kvdt} {env}")
 
 
+# Batches on both sides of 64 sequences: up to 64 the split kernels keep the
+# lengths in one register per wave (every wave reads them itself), beyond that
+# in LDS; empty sequences take the zero-row path of either form.
+REG_LEN_BATCHES = [63, 64, 65, 100]
+
+
+@pytest.mark.parametrize("kvdt", ["bf16", "int4", "fp8"])
+@pytest.mark.parametrize("batch", REG_LEN_BATCHES)
+def test_register_and_lds_length_forms(kvdt, batch):
+    r = np.random.default_rng(300 + batch)
+    lens = [int(x) for x in r.integers(1, 200, size=batch)]
+    for i in range(3, batch, 17):
+        lens[i] = 0
+    lens[-1] = 0  # the last lane of a 64-sequence batch
+    wl = W.from_lengths(lens, 32, 8, 128, kvdt, seed=300 + batch, group=128 if kvdt == "int4" else 0,
+                        sink=kvdt != "bf16")
+    _, out, _, _ = run(wl)
+    assert np.all(out[[i for i, x in enumerate(lens) if x == 0]] == 0.0)
+    assert_close(out, expected(wl), "bf16" if kvdt == "bf16" else "f16", f"{batch} seqs {kvdt}")
+    nq = 5
+    _, vout = run_verify(wl, nq)
+    rows = [i for i in range(batch) if lens[i] > 0][-12:]  # the last rows, near the 64 boundary
+    from _ref import expected_verify
+    assert_close(vout[rows], expected_verify(wl, nq, rows=rows)[rows], "bf16" if kvdt == "bf16" else "f16",
+                 f"verify {batch} seqs {kvdt}")
+
+
 STALE_CASES = [("bf16", [300, 16]), ("fp8", [300, 16]), ("int4", [3000, 17, 700]),
                ("bf16", [900, 33, 2000, 1, 517, 0, 3000])]
 
