@@ -831,7 +831,18 @@ STEP_CASES = {
     "int4-g64-window": lambda: W.window_batch([1, 100, 145, 1000], steps=2, window=128, group=64,
                                               kv="int4", seed=216),
     "f32-generic": lambda: W.from_lengths([1, 40, 333], 8, 4, 64, "f32", seed=217),
+    # more than 64 sequences: the quantized kernel's LDS form of the cut
+    "int4-80-seqs": lambda: W.from_lengths([1 + (i * 37) % 190 for i in range(80)], 32, 8, 128, "int4",
+                                           seed=218, group=128, sink=True),
+    "fp8-70-seqs": lambda: W.from_lengths([1 + (i * 53) % 230 for i in range(70)], 32, 8, 128, "fp8",
+                                          seed=219, sink=True),
+    # a queue (LDS form) and a non-default prefetch depth (the append launch)
+    "int4-queue": lambda: W.from_lengths([1, 16, 17, 700, 1500], 32, 8, 128, "int4", seed=220,
+                                         group=128, sink=True),
+    "fp8-depth4": lambda: W.from_lengths([1, 16, 17, 700], 32, 8, 128, "fp8", seed=221, sink=True),
 }
+STEP_ENVS = {"int4-queue": {"PA_WG_PER_CU": "1", "PA_UNIT_BLOCKS": "3", "PA_STATIC_PERMILLE": "600"},
+             "fp8-depth4": {"PA_QUANT_NB": "4"}}
 
 
 @pytest.mark.parametrize("name", list(STEP_CASES))
@@ -840,10 +851,25 @@ def test_decode_step_writes_newest_token(name):
     first overwritten with other values: the step writes the token into the
     slot its table gives (the stored bytes match the oracle's bit for bit) and
     the attention reads it (outputs match the oracle, and equal pa_append_kv
-    of the token followed by pa_decode_attention bit for bit).  The 16-bit
-    pools take the split kernel's own write, the others a launch of its own."""
+    of the token followed by pa_decode_attention bit for bit).  The matrix-core
+    split kernels write the token themselves (the quantized one at its default
+    prefetch depth), the others take a launch of its own."""
     wl = STEP_CASES[name]()
-    log(f"[gpu] decode step {name} B={wl.batch}")
+    env = STEP_ENVS.get(name, {})
+    log(f"[gpu] decode step {name} B={wl.batch} env={env}")
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        _decode_step_case(name, wl)
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def _decode_step_case(name, wl):
     kv = PagedKV(wl, DEV)
     kv.replay()
     tdev, ldev, t, l = kv.device_tables()
