@@ -420,6 +420,24 @@ def test_register_and_lds_length_forms(kvdt, batch):
                  f"verify {batch} seqs {kvdt}")
 
 
+@pytest.mark.parametrize("kvdt", ["bf16", "int4"])
+@pytest.mark.parametrize("batch", [1, 40, 70])
+def test_all_sequences_empty(kvdt, batch):
+    """Every length 0 (register form up to 64 sequences, LDS form beyond):
+    the decode writes zero rows and nothing else, with no block to read."""
+    wl = W.from_lengths([5] * batch, 32, 8, 128, kvdt, seed=310 + batch, group=128 if kvdt == "int4" else 0,
+                        sink=kvdt != "bf16")
+    kv = PagedKV(wl, DEV)
+    kv.replay()
+    tdev, _, _, _ = kv.device_tables()
+    ldev = torch.zeros(batch, dtype=torch.int32, device=DEV)
+    q = torch.from_numpy(wl.q()).to(TORCH_DT[wl.q_dtype]).to(DEV)
+    out = torch.full((batch + 1,) + tuple(q.shape[1:]), 7.0, dtype=q.dtype, device=DEV)
+    kv.decode(q, tdev, ldev, 1, out=out[:batch])
+    torch.cuda.synchronize()
+    assert torch.all(out[:batch] == 0.0) and torch.all(out[batch] == 7.0)
+
+
 STALE_CASES = [("bf16", [300, 16]), ("fp8", [300, 16]), ("int4", [3000, 17, 700]),
                ("bf16", [900, 33, 2000, 1, 517, 0, 3000])]
 
