@@ -718,16 +718,26 @@ __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& o
   TO* out = static_cast<TO*>(a.out);
   for (int idx = threadIdx.x; idx < NC * kD; idx += kWaves * 64) {
     const int hc = idx / kD, d = idx % kD;
+    // every slot's reads issued before any is used (one LDS round trip)
+    float mv[SH::kSlots], lv[SH::kSlots], ov[SH::kSlots];
+#pragma unroll
+    for (int v = 0; v < SH::kSlots; ++v) {
+      mv[v] = sh.m[v][hc];
+      lv[v] = sh.l[v][hc];
+      ov[v] = sh.o[v][hc][d];
+    }
     float M = -__builtin_inff();
 #pragma unroll
-    for (int v = 0; v < SH::kSlots; ++v) M = fmaxf(M, sh.m[v][hc]);
+    for (int v = 0; v < SH::kSlots; ++v) M = fmaxf(M, mv[v]);
     float lsum = 0.f, osum = 0.f;
 #pragma unroll
     for (int v = 0; v < SH::kSlots; ++v) {
-      if (sh.m[v][hc] == -__builtin_inff()) continue;  // wave saw no block (or no visible token)
-      const float wt = exp2f(sh.m[v][hc] - M);
-      lsum += sh.l[v][hc] * wt;
-      osum += sh.o[v][hc][d] * wt;
+      // a slot whose wave saw no block (or no visible token) adds nothing
+      // (selected, not branched around: its terms are computed and dropped)
+      const bool none = mv[v] == -__builtin_inff();
+      const float wt = exp2f(mv[v] - M);
+      lsum += none ? 0.f : lv[v] * wt;
+      osum += none ? 0.f : ov[v] * wt;
     }
     if (complete) {
       if (hc < om.cols(h)) out[om.row(b, h, hc) * kD + d] = TO(lsum > 0.f ? osum / lsum : 0.f);
