@@ -596,12 +596,38 @@ struct Lse {
     l = l * sa + li * sb;
     m = mn;
   }
+  // N pieces at once: their common maximum first, then every piece's weight
+  // on its own (no chain of rescales); a piece of max -inf (no token) adds
+  // nothing.
+  template <int N>
+  __device__ void add_all(const float (&mi)[N], const float (&li)[N], const f32x4 (&oi)[N]) {
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < N; ++u) mn = fmaxf(mn, mi[u]);
+    if (mn == -__builtin_inff()) return;  // nothing seen yet
+    const float sa = m == -__builtin_inff() ? 0.f : exp2f(m - mn);
+    float ln = l * sa;
+    f32x4 on = o * sa;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const bool none = mi[u] == -__builtin_inff();
+      const float w = exp2f(mi[u] - mn);
+      ln += none ? 0.f : li[u] * w;
+      on += none ? f32x4{0.f, 0.f, 0.f, 0.f} : oi[u] * w;
+    }
+    m = mn;
+    l = ln;
+    o = on;
+  }
 };
 
 // c0: the segment's first unit; split_first: its first piece sits in that
 // unit's second slot; rows: the partial rows the workspace holds (bounds of
 // the buffer loads).
-template <typename TO, class SH>
+// ALL: each batch's pieces at once with a common maximum (Lse::add_all; the
+// merge launch), else one at a time (Lse::add; the split kernels, whose
+// registers the batched form crowds).
+template <typename TO, class SH, bool ALL = false>
 __device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& om, int b, int h,
                                      int c0, bool split_first, int np, unsigned rows, int col0,
                                      int ncol) {
@@ -645,13 +671,27 @@ __device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& 
       if (tid < span * nh) mls[tid] = float2{__uint_as_float(pair[0]), __uint_as_float(pair[1])};
       __syncthreads();
       if (pg < P) {
+        if constexpr (ALL) {
+          float mb[kMergeBatch], lb[kMergeBatch];
+          f32x4 ob[kMergeBatch];
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
-          const int i = q0 + u * P + pg;
-          if (i < np) {
-            const float2 ml = mls[(u * P + pg) * nh + hc - h0];
-            r.add(ml.x, ml.y, f32x4{__uint_as_float(ov[u][0]), __uint_as_float(ov[u][1]),
-                                    __uint_as_float(ov[u][2]), __uint_as_float(ov[u][3])});
+          for (int u = 0; u < kMergeBatch; ++u) {
+            const float2 ml = mls[min((u * P + pg) * nh + hc - h0, span * nh - 1)];
+            mb[u] = q0 + u * P + pg < np ? ml.x : -__builtin_inff();  // past the end: no piece
+            lb[u] = ml.y;
+            ob[u] = f32x4{__uint_as_float(ov[u][0]), __uint_as_float(ov[u][1]), __uint_as_float(ov[u][2]),
+                          __uint_as_float(ov[u][3])};
+          }
+          r.add_all(mb, lb, ob);
+        } else {
+#pragma unroll
+          for (int u = 0; u < kMergeBatch; ++u) {
+            const int i = q0 + u * P + pg;
+            if (i < np) {
+              const float2 ml = mls[(u * P + pg) * nh + hc - h0];
+              r.add(ml.x, ml.y, f32x4{__uint_as_float(ov[u][0]), __uint_as_float(ov[u][1]),
+                                      __uint_as_float(ov[u][2]), __uint_as_float(ov[u][3])});
+            }
           }
         }
       }
@@ -668,9 +708,24 @@ __device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& 
       __syncthreads();
       if (tid < Ft) {
         r = Lse{-__builtin_inff(), 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
-        for (int g2 = 0; g2 < P; ++g2) {
-          const float* q = red + (g2 * Ft + tid) * 6;
-          r.add(q[0], q[1], f32x4{q[2], q[3], q[4], q[5]});
+        if constexpr (ALL) {
+          for (int g0 = 0; g0 < P; g0 += 4) {  // the P piece groups, four at a time
+            float mg[4], lg[4];
+            f32x4 og[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float* q = red + (min(g0 + k, P - 1) * Ft + tid) * 6;
+              mg[k] = g0 + k < P ? q[0] : -__builtin_inff();
+              lg[k] = q[1];
+              og[k] = f32x4{q[2], q[3], q[4], q[5]};
+            }
+            r.add_all(mg, lg, og);
+          }
+        } else {
+          for (int g2 = 0; g2 < P; ++g2) {
+            const float* q = red + (g2 * Ft + tid) * 6;
+            r.add(q[0], q[1], f32x4{q[2], q[3], q[4], q[5]});
+          }
         }
       }
       __syncthreads();  // red is rewritten by the next trip

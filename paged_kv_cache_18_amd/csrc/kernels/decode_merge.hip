@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_merge_kernel(DecodeArgs a)
   const int j0 = job[0], np = job[1];
   if (seq_len(a, b) == 0 || np <= 1) return;  // workgroup-uniform
   const unsigned rows = unsigned((a.ws_ml - a.ws_o) / kD);  // partial rows of the workspace
-  merge_segment<TO>(a, sh, om, b, h, j0 & 0x7FFFFFFF, j0 < 0, np, rows, hc, 1);
+  merge_segment<TO, Shared, true>(a, sh, om, b, h, j0 & 0x7FFFFFFF, j0 < 0, np, rows, hc, 1);
 }
 
 }  // namespace
