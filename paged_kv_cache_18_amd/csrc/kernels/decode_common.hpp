@@ -518,9 +518,26 @@ __device__ inline void new_token_store(const DecodeArgs& a, const NewToken& nt, 
 // equal chunks, the workgroups a compute unit holds would otherwise progress
 // in dispatch order (older waves win issue arbitration) and the youngest
 // would finish last; this lets the ones behind catch up.
+//
+// ELDER (the 16-bit kernel): the grid's first half, dispatched first, runs
+// one band lower at equal progress, so that the second half's workgroup on
+// the same compute unit keeps pace from the start (the quantized kernel
+// measured slower with it).
+template <bool ELDER = false>
 __device__ inline void prio_from_progress(const DecodeArgs& a, int done, int C) {
   if (!a.prio) return;
   const int r = max(C - done, 0);
+  if constexpr (ELDER) {
+    if (int(blockIdx.x) < int(gridDim.x) / 2) {
+      if (2 * r > C)
+        __builtin_amdgcn_s_setprio(2);
+      else if (4 * r > C)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
+      return;
+    }
+  }
   if (2 * r > C)
     __builtin_amdgcn_s_setprio(3);
   else if (4 * r > C)

@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       Tid nid = id_of(NB - 1);
       int k = 0;
       for (; k + NB <= n; k += NB) {
-        prio_from_progress(a, pos - pos0 + nst * k, prio_span);
+        prio_from_progress<true>(a, pos - pos0 + nst * k, prio_span);
 #pragma unroll
         for (int s = 0; s < NB; ++s) {
           const int nxt = (s + NB - 1) % NB;
