@@ -644,7 +644,9 @@ struct Lse {
 // ALL: each batch's pieces at once with a common maximum (Lse::add_all; the
 // merge launch), else one at a time (Lse::add; the split kernels, whose
 // registers the batched form crowds).
-template <typename TO, class SH, bool ALL = false>
+// WIDE: slices of 9-24 columns with up to 4 pieces take one memory round
+// trip (the two-tile kernels).
+template <typename TO, class SH, bool ALL = false, bool WIDE = false>
 __device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& om, int b, int h,
                                      int c0, bool split_first, int np, unsigned rows, int col0,
                                      int ncol) {
@@ -662,6 +664,50 @@ __device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& 
   static_assert(256 * 6 + 2 * 256 <= sizeof(sh.o) / sizeof(float), "LDS reuse");
   TO* out = static_cast<TO*>(a.out);
   const int tid = threadIdx.x;
+  const int F = ncol * kCols;  // float4 columns of the slice
+  if (WIDE && !ALL && F > 256 && F <= 3 * 256 && np <= 4) {
+    // Wide slice, few pieces (a verify step's 17-24 columns): each thread
+    // takes up to three float4 columns, one per trip of 256, and all their
+    // pieces' loads are in flight at once (one memory round trip instead of
+    // one per trip); pieces are added in order, as in the trips below.
+    const int pt = min(tid, np * ncol - 1);
+    const u32x2 pair = __builtin_amdgcn_raw_buffer_load_b64(
+        rml, (row_of(pt / ncol) + col0 + pt % ncol) * 8u, 0, kSc1);
+    u32x4 ov[12];
+#pragma unroll
+    for (int u = 0; u < 12; ++u) {
+      const int i = min(u % 4, np - 1);                            // past the end: a re-read
+      const int cc = col0 * kCols + min(tid + 256 * (u / 4), F - 1);  // never used
+      ov[u] = __builtin_amdgcn_raw_buffer_load_b128(
+          ro, row_of(i) * kD * 4u + unsigned(cc / kCols) * kD * 4u + unsigned(cc % kCols) * 16u, 0, kSc1);
+    }
+    if (tid < np * ncol) mls[tid] = float2{__uint_as_float(pair[0]), __uint_as_float(pair[1])};
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int c = tid + 256 * k;
+      if (c >= F) break;
+      const int hc = col0 + c / kCols;
+      Lse r{-__builtin_inff(), 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < np) {
+          const float2 ml = mls[i * ncol + hc - col0];
+          const u32x4 v = ov[4 * k + i];
+          r.add(ml.x, ml.y, f32x4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                                  __uint_as_float(v[3])});
+        }
+      }
+      if (hc < om.cols(h)) {  // the last column slice may be short
+        const float inv = r.l > 0.f ? 1.f / r.l : 0.f;
+        TO* o = out + om.row(b, h, hc) * kD + (c % kCols) * 4;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) o[e2] = TO(r.o[e2] * inv);
+      }
+    }
+    __syncthreads();  // mls is LDS the caller reuses
+    return;
+  }
   // float4 columns [col0, col0 + 32*ncol) in trips of at most 256
   for (int base = col0 * kCols; base < (col0 + ncol) * kCols; base += 256) {
     const int Ft = min(256, (col0 + ncol) * kCols - base);
@@ -781,7 +827,7 @@ __device__ inline void stash_piece(SH& sh, int w, int g, int col, const f32x4 (&
 // issued for its next piece keep flying through the merge; the one exchange
 // through memory (a partial read by the completing arrival) waits for this
 // workgroup's stores explicitly before the arrival counts.
-template <typename TO, class SH>
+template <typename TO, bool WIDE = false, class SH>
 __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& om, bool complete,
                                     int slot, int unit, int b, int h, int S, int nb,
                                     const Units& um) {
@@ -830,7 +876,7 @@ __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& o
     if (threadIdx.x == 0) sh.last = arrive(a, c0, np) ? 1 : 0;
     lds_barrier();
     if (sh.last)
-      merge_segment<TO>(a, sh, om, b, h, c0, S != um.start(c0), np,
+      merge_segment<TO, SH, false, WIDE>(a, sh, om, b, h, c0, S != um.start(c0), np,
                         unsigned(um.total()) * 2u * unsigned(NC), 0, NC);
   }
   lds_barrier();
