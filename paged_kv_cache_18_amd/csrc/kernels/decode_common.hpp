@@ -834,6 +834,53 @@ __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& o
   const int NC = om.ncol();
   lds_barrier();
   TO* out = static_cast<TO*>(a.out);
+  if constexpr (WIDE) {
+    // Many columns: four consecutive dimensions per thread, so one weight
+    // computation and one 16-byte partial store serve four outputs (the
+    // arithmetic per output is the loop's below).
+    const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_o, (short)0, int(unsigned(um.total()) * 2u * unsigned(NC) * kD * 4u), kRsrcWord3);
+    for (int i4 = threadIdx.x; i4 < NC * (kD / 4); i4 += kWaves * 64) {
+      const int hc = i4 / (kD / 4), d0 = (i4 % (kD / 4)) * 4;
+      float mv[SH::kSlots], lv[SH::kSlots], ov[SH::kSlots][4];
+#pragma unroll
+      for (int v = 0; v < SH::kSlots; ++v) {
+        mv[v] = sh.m[v][hc];
+        lv[v] = sh.l[v][hc];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[v][e] = sh.o[v][hc][d0 + e];
+      }
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int v = 0; v < SH::kSlots; ++v) M = fmaxf(M, mv[v]);
+      float lsum = 0.f, osum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < SH::kSlots; ++v) {
+        const bool none = mv[v] == -__builtin_inff();
+        const float wt = exp2f(mv[v] - M);
+        lsum += none ? 0.f : lv[v] * wt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) osum[e] += none ? 0.f : ov[v][e] * wt;
+      }
+      if (complete) {
+        if (hc < om.cols(h)) {
+          TO* o = out + om.row(b, h, hc) * kD + d0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = TO(lsum > 0.f ? osum[e] / lsum : 0.f);
+        }
+      } else {
+        const unsigned row = (unsigned(unit) * 2u + unsigned(slot)) * unsigned(NC) + unsigned(hc);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(osum[0]), __float_as_uint(osum[1]), __float_as_uint(osum[2]),
+                  __float_as_uint(osum[3])},
+            rws, (row * kD + unsigned(d0)) * 4u, 0, kSc1);
+        if (d0 == 0) {
+          st_agent(&a.ws_ml[size_t(row) * 2], M);
+          st_agent(&a.ws_ml[size_t(row) * 2 + 1], lsum);
+        }
+      }
+    }
+  } else
   for (int idx = threadIdx.x; idx < NC * kD; idx += kWaves * 64) {
     const int hc = idx / kD, d = idx % kD;
     // every slot's reads issued before any is used (one LDS round trip)
