@@ -234,13 +234,6 @@ Plan make_plan(const pa_pool* p, int32_t batch, int32_t n_q_heads, int32_t max_s
                                             n_query == 1 ? 0 : seg_cols * ngroups <= 16 ? 1 : 2,
                                             d.group_size);
         per_cu = std::min(per_cu, kDecodePerCu);
-        // A 16-bit verify step of one column slice on two tiles runs one
-        // workgroup per compute unit: half the regions, so half the piece
-        // ends, whose merges of 17-32 columns cost more than the second
-        // workgroup's latency hiding gains (the Llama-3-8B-shaped batch
-        // with 6 queries: 136.2 against 137.4 us)
-        if (pl.kernel == pa::kKernMfma16 && n_query > 1 && nsl == 1 && seg_cols * ngroups > 16)
-          per_cu = 1;
       }
       pl.max_splits = int32_t(std::max<int64_t>(
           1, std::min<int64_t>({w, int64_t(cu_count()) * per_cu, int64_t(kCtrCap / 2)})));
