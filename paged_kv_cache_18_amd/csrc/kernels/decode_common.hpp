@@ -644,8 +644,8 @@ struct Lse {
 // ALL: each batch's pieces at once with a common maximum (Lse::add_all; the
 // merge launch), else one at a time (Lse::add; the split kernels, whose
 // registers the batched form crowds).
-// WIDE: slices of 9-24 columns with up to 4 pieces take one memory round
-// trip (the two-tile kernels).
+// WIDE (the 16-bit kernel and the quantized causal ones): slices of 9-24
+// columns with up to 4 pieces take one memory round trip.
 template <typename TO, class SH, bool ALL = false, bool WIDE = false>
 __device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& om, int b, int h,
                                      int c0, bool split_first, int np, unsigned rows, int col0,
@@ -835,9 +835,9 @@ __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& o
   lds_barrier();
   TO* out = static_cast<TO*>(a.out);
   if constexpr (WIDE) {
-    // Many columns: four consecutive dimensions per thread, so one weight
-    // computation and one 16-byte partial store serve four outputs (the
-    // arithmetic per output is the loop's below).
+    // Four consecutive dimensions per thread, so one weight computation and
+    // one 16-byte partial store serve four outputs (the arithmetic per output
+    // is the loop's below, which the quantized decode instances keep).
     const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
         a.ws_o, (short)0, int(unsigned(um.total()) * 2u * unsigned(NC) * kD * 4u), kRsrcWord3);
     for (int i4 = threadIdx.x; i4 < NC * (kD / 4); i4 += kWaves * 64) {
