@@ -826,7 +826,8 @@ __device__ inline void stash_piece(SH& sh, int w, int g, int col, const f32x4 (&
 // reused by the next piece).  Its barriers wait on LDS only, so loads a wave
 // issued for its next piece keep flying through the merge; the one exchange
 // through memory (a partial read by the completing arrival) waits for this
-// workgroup's stores explicitly before the arrival counts.
+// workgroup's stores explicitly before the arrival counts.  WIDE: four
+// consecutive dimensions per thread, and the one-trip segment merge.
 template <typename TO, bool WIDE = false, class SH>
 __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& om, bool complete,
                                     int slot, int unit, int b, int h, int S, int nb,
