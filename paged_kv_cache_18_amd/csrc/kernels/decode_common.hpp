@@ -644,8 +644,8 @@ struct Lse {
 // ALL: each batch's pieces at once with a common maximum (Lse::add_all; the
 // merge launch), else one at a time (Lse::add; the split kernels, whose
 // registers the batched form crowds).
-// WIDE (the 16-bit kernel and the quantized causal ones): slices of 9-24
-// columns with up to 4 pieces take one memory round trip.
+// WIDE (the split kernels): slices of 9-24 columns with up to 4 pieces take
+// one memory round trip.
 template <typename TO, class SH, bool ALL = false, bool WIDE = false>
 __device__ inline void merge_segment(const DecodeArgs& a, SH& sh, const OutMap& om, int b, int h,
                                      int c0, bool split_first, int np, unsigned rows, int col0,
@@ -826,76 +826,32 @@ __device__ inline void stash_piece(SH& sh, int w, int g, int col, const f32x4 (&
 // reused by the next piece).  Its barriers wait on LDS only, so loads a wave
 // issued for its next piece keep flying through the merge; the one exchange
 // through memory (a partial read by the completing arrival) waits for this
-// workgroup's stores explicitly before the arrival counts.  WIDE: four
-// consecutive dimensions per thread, and the one-trip segment merge.
-template <typename TO, bool WIDE = false, class SH>
+// workgroup's stores explicitly before the arrival counts.
+template <typename TO, class SH>
 __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& om, bool complete,
                                     int slot, int unit, int b, int h, int S, int nb,
                                     const Units& um) {
   const int NC = om.ncol();
   lds_barrier();
   TO* out = static_cast<TO*>(a.out);
-  if constexpr (WIDE) {
-    // Four consecutive dimensions per thread, so one weight computation and
-    // one 16-byte partial store serve four outputs (the arithmetic per output
-    // is the loop's below, which the quantized decode instances keep).
-    const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
-        a.ws_o, (short)0, int(unsigned(um.total()) * 2u * unsigned(NC) * kD * 4u), kRsrcWord3);
-    for (int i4 = threadIdx.x; i4 < NC * (kD / 4); i4 += kWaves * 64) {
-      const int hc = i4 / (kD / 4), d0 = (i4 % (kD / 4)) * 4;
-      float mv[SH::kSlots], lv[SH::kSlots], ov[SH::kSlots][4];
-#pragma unroll
-      for (int v = 0; v < SH::kSlots; ++v) {
-        mv[v] = sh.m[v][hc];
-        lv[v] = sh.l[v][hc];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[v][e] = sh.o[v][hc][d0 + e];
-      }
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int v = 0; v < SH::kSlots; ++v) M = fmaxf(M, mv[v]);
-      float lsum = 0.f, osum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int v = 0; v < SH::kSlots; ++v) {
-        const bool none = mv[v] == -__builtin_inff();
-        const float wt = exp2f(mv[v] - M);
-        lsum += none ? 0.f : lv[v] * wt;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) osum[e] += none ? 0.f : ov[v][e] * wt;
-      }
-      if (complete) {
-        if (hc < om.cols(h)) {
-          TO* o = out + om.row(b, h, hc) * kD + d0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = TO(lsum > 0.f ? osum[e] / lsum : 0.f);
-        }
-      } else {
-        const unsigned row = (unsigned(unit) * 2u + unsigned(slot)) * unsigned(NC) + unsigned(hc);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4{__float_as_uint(osum[0]), __float_as_uint(osum[1]), __float_as_uint(osum[2]),
-                  __float_as_uint(osum[3])},
-            rws, (row * kD + unsigned(d0)) * 4u, 0, kSc1);
-        if (d0 == 0) {
-          st_agent(&a.ws_ml[size_t(row) * 2], M);
-          st_agent(&a.ws_ml[size_t(row) * 2 + 1], lsum);
-        }
-      }
-    }
-  } else
-  for (int idx = threadIdx.x; idx < NC * kD; idx += kWaves * 64) {
-    const int hc = idx / kD, d = idx % kD;
-    // every slot's reads issued before any is used (one LDS round trip)
-    float mv[SH::kSlots], lv[SH::kSlots], ov[SH::kSlots];
+  // Four consecutive dimensions per thread: one weight computation and one
+  // 16-byte partial store serve four outputs.
+  const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
+      a.ws_o, (short)0, int(unsigned(um.total()) * 2u * unsigned(NC) * kD * 4u), kRsrcWord3);
+  for (int i4 = threadIdx.x; i4 < NC * (kD / 4); i4 += kWaves * 64) {
+    const int hc = i4 / (kD / 4), d0 = (i4 % (kD / 4)) * 4;
+    float mv[SH::kSlots], lv[SH::kSlots], ov[SH::kSlots][4];
 #pragma unroll
     for (int v = 0; v < SH::kSlots; ++v) {
       mv[v] = sh.m[v][hc];
       lv[v] = sh.l[v][hc];
-      ov[v] = sh.o[v][hc][d];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[v][e] = sh.o[v][hc][d0 + e];
     }
     float M = -__builtin_inff();
 #pragma unroll
     for (int v = 0; v < SH::kSlots; ++v) M = fmaxf(M, mv[v]);
-    float lsum = 0.f, osum = 0.f;
+    float lsum = 0.f, osum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < SH::kSlots; ++v) {
       // a slot whose wave saw no block (or no visible token) adds nothing
@@ -903,16 +859,24 @@ __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& o
       const bool none = mv[v] == -__builtin_inff();
       const float wt = exp2f(mv[v] - M);
       lsum += none ? 0.f : lv[v] * wt;
-      osum += none ? 0.f : ov[v] * wt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) osum[e] += none ? 0.f : ov[v][e] * wt;
     }
     if (complete) {
-      if (hc < om.cols(h)) out[om.row(b, h, hc) * kD + d] = TO(lsum > 0.f ? osum / lsum : 0.f);
+      if (hc < om.cols(h)) {
+        TO* o = out + om.row(b, h, hc) * kD + d0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = TO(lsum > 0.f ? osum[e] / lsum : 0.f);
+      }
     } else {
-      const size_t row = (size_t(unit) * 2 + slot) * NC + hc;
-      st_agent(&a.ws_o[row * kD + d], osum);
-      if (d == 0) {
-        st_agent(&a.ws_ml[row * 2], M);
-        st_agent(&a.ws_ml[row * 2 + 1], lsum);
+      const unsigned row = (unsigned(unit) * 2u + unsigned(slot)) * unsigned(NC) + unsigned(hc);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{__float_as_uint(osum[0]), __float_as_uint(osum[1]), __float_as_uint(osum[2]),
+                __float_as_uint(osum[3])},
+          rws, (row * kD + unsigned(d0)) * 4u, 0, kSc1);
+      if (d0 == 0) {
+        st_agent(&a.ws_ml[size_t(row) * 2], M);
+        st_agent(&a.ws_ml[size_t(row) * 2 + 1], lsum);
       }
     }
   }
@@ -924,7 +888,7 @@ __device__ inline void finish_piece(const DecodeArgs& a, SH& sh, const OutMap& o
     if (threadIdx.x == 0) sh.last = arrive(a, c0, np) ? 1 : 0;
     lds_barrier();
     if (sh.last)
-      merge_segment<TO, SH, false, WIDE>(a, sh, om, b, h, c0, S != um.start(c0), np,
+      merge_segment<TO, SH, false, true>(a, sh, om, b, h, c0, S != um.start(c0), np,
                         unsigned(um.total()) * 2u * unsigned(NC), 0, NC);
   }
   lds_barrier();

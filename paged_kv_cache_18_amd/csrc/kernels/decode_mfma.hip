@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       stash_piece(sh, ws, g, 16 * (t0 + t) + c, o[t], m_ref[t], l_run[t]);
     }
     if (a.defer_merge && jbeg == 0 && threadIdx.x == 0) write_job(a, um, b, hv, hv * um.TB + fb, nb);
-    finish_piece<T, true>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, hv, hv * um.TB + fb,
+    finish_piece<T>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, hv, hv * um.TB + fb,
                     nb, um);
     pos += jend - jbeg;
     first = false;

@@ -728,7 +728,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(NB 
       if (keep) stash_piece(sh, w, g, t * S + lcol, o[t], m_ref[t], l_run[t]);
     }
     if (a.defer_merge && jbeg == 0 && threadIdx.x == 0) write_job(a, um, b, hv, hv * um.TB + fb, nb);
-    finish_piece<_Float16, CAUSAL>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, hv,
+    finish_piece<_Float16>(a, sh, om, jbeg == 0 && jend == nb, first ? 0 : 1, unit, b, hv,
                            hv * um.TB + fb, nb, um);
     pos += jend - jbeg;
     first = false;
